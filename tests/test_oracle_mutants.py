@@ -1,0 +1,145 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them: a dropped scale, a wrong GQA index, an off-by-one
+causal window, K and V swapped, a log2 logsumexp, a missing normalisation,
+an unshifted exponential, a merge that forgets to rescale, and an energy that
+drops its zeta term.  None of these variants is used anywhere else."""
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+
+def _row(q, k, v, scale, mistake):
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    n = k.shape[0]
+    if n == 0:
+        return np.zeros(v.shape[1]), -math.inf
+    if mistake == "kv_swapped":
+        k, v = v, k
+    s = (1.0 if mistake == "no_scale" else scale) * (k @ q)
+    if mistake == "sign":
+        s = -s
+    if mistake == "no_max_shift":
+        with np.errstate(over="ignore", invalid="ignore"):
+            e = np.exp(s)
+            return (e @ v) / e.sum(), math.log(e.sum()) if np.isfinite(e.sum()) else math.nan
+    M = s.max()
+    e = np.exp(s - M)
+    lse = M + math.log(e.sum())
+    if mistake == "lse_log2":
+        lse = lse / math.log(2.0)
+    if mistake == "lse_drops_max":
+        lse = math.log(e.sum())
+    if mistake == "unnormalised":
+        return e @ v, lse
+    return (e / e.sum()) @ v, lse
+
+
+def _attend_factory(mistake):
+    def attend(q, k, v, kv_lens, scale, causal=False, rows=None, slab=0):
+        B, q_len, Hq, D = q.shape
+        Hkv = k.shape[1]
+        G = Hq // Hkv
+        O = np.zeros((B, q_len, Hq, v.shape[-1])) if v is not None else None
+        lse = np.zeros((B, q_len, Hq))
+        for b in range(B):
+            for i in range(q_len):
+                Lb = int(kv_lens[b])
+                if causal and mistake != "causal_ignored":
+                    n = Lb - q_len + i + (0 if mistake == "causal_off_by_one" else 1)
+                else:
+                    n = Lb
+                n = max(0, min(Lb, n))
+                for h in range(Hq):
+                    kvh = h % Hkv if mistake == "gqa_modulo" else h // G
+                    vv = v[b, kvh, :n] if v is not None else k[b, kvh, :n]
+                    o, l = _row(q[b, i, h], k[b, kvh, :n], vv, scale, mistake)
+                    if O is not None:
+                        O[b, i, h] = o
+                    lse[b, i, h] = l
+        return O, lse
+    return attend
+
+
+def _merge_factory(mistake):
+    def merge(a, b):
+        ma, la, oa = a
+        mb, lb, ob = b
+        m = max(ma, mb)
+        if m == -math.inf:
+            return (-math.inf, 0.0, np.zeros_like(oa))
+        wa = math.exp(ma - m) if ma != -math.inf else 0.0
+        wb = math.exp(mb - m) if mb != -math.inf else 0.0
+        if mistake == "merge_no_rescale_o":
+            return (m, la * wa + lb * wb, oa + ob)
+        if mistake == "merge_inverted_weight":
+            wa = math.exp(m - ma) if ma != -math.inf else 0.0
+            wb = math.exp(m - mb) if mb != -math.inf else 0.0
+        return (m, la * wa + lb * wb, oa * wa + ob * wb)
+    return merge
+
+
+def _energy_factory(mistake):
+    def energy(q, k, v, scale, zeta=None):
+        if mistake == "energy_no_zeta":
+            zeta = None
+        if mistake == "energy_scaled_zeta" and zeta is not None:
+            zeta = scale * np.asarray(zeta)
+        return oracle.energy(q, k, v, scale, zeta)
+    return energy
+
+
+def _bif_factory(attend):
+    def attend_bifurcated(q, kp, vp, ks, vs, scale, samples=None):
+        S, Hq, D = q.shape
+        O = np.zeros((S, Hq, D)); lse = np.zeros((S, Hq))
+        for s in range(S):
+            kc = np.concatenate([kp, ks[s]], axis=1)[None]
+            vc = np.concatenate([vp, vs[s]], axis=1)[None]
+            o, l = attend(q[s][None, None], kc, vc, [kc.shape[2]], scale)
+            O[s], lse[s] = o[0, 0], l[0, 0]
+        return O, lse
+    return attend_bifurcated
+
+
+ATTEND_MISTAKES = ["no_scale", "sign", "kv_swapped", "gqa_modulo", "causal_off_by_one",
+                   "causal_ignored", "lse_log2", "lse_drops_max", "unnormalised", "no_max_shift"]
+MERGE_MISTAKES = ["merge_no_rescale_o", "merge_inverted_weight"]
+ENERGY_MISTAKES = ["energy_no_zeta", "energy_scaled_zeta"]
+
+
+def _impl(mistake):
+    att = _attend_factory(mistake if mistake in ATTEND_MISTAKES else None)
+    return types.SimpleNamespace(
+        attend=att,
+        attend_bifurcated=_bif_factory(att),
+        energy=_energy_factory(mistake),
+        chunk_partial=oracle.chunk_partial,
+        merge=_merge_factory(mistake),
+        finalize=oracle.finalize,
+    )
+
+
+def test_faithful_variant_passes_all_pins():
+    """The loop-based variant with no mistake passes every pin (so the mutants
+    below fail because of their mistake, not because of the harness)."""
+    impl = _impl(None)
+    for pin in pins.ALL_PINS:
+        pin(impl)
+
+
+@pytest.mark.parametrize("mistake", ATTEND_MISTAKES + MERGE_MISTAKES + ENERGY_MISTAKES)
+def test_pins_catch_planted_mistake(mistake):
+    impl = _impl(mistake)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(impl)
+        except (AssertionError, ValueError, FloatingPointError, OverflowError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {mistake!r}"
