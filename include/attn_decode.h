@@ -1,0 +1,192 @@
+/*
+ * attn_decode.h -- exact split-KV softmax attention decoding on AMD Instinct
+ * MI355X (gfx950).  C ABI: plain pointers, sizes and status codes.
+ *
+ * What is computed.  For every query row (sequence b, query token i, query
+ * head h) the library returns the attention output
+ *     O = sum_t softmax_t(scale * q . k_t) v_t
+ * and its logsumexp ("energy")
+ *     lse = ln sum_t exp(scale * q . k_t)
+ * over the visible keys t of KV head h / (Hq / Hkv).  This is the plain
+ * definition S = Q K^T / sqrt(d_k), P = softmax(S), O = P V of the "attention
+ * acceleration" concept page (technical principles, section 1).  The cache is
+ * cut into chunks; each chunk yields the statistics m = max, l = sum e^(s-m)
+ * and the unnormalised partial output o (same page, section 2.1, online
+ * softmax), and the partials are combined by the associative merge
+ *     m = max(m_a, m_b), l = l_a e^(m_a-m) + l_b e^(m_b-m), o likewise,
+ * which is exact in any order because max and logsumexp are associative
+ * (Tree Attention article, "an energy view of attention").  Star Attention's
+ * phase 2 (query encoding and token generation) aggregates the same softmax
+ * statistics across hosts; here the chunks of one GPU play the hosts.
+ *
+ * Layouts (row-major, last axis contiguous, 16-byte aligned base pointers):
+ *     Q    [B][q_len][Hq][D]      element type attn_dtype_t
+ *     K, V [B][Hkv][L_max][D]     element type attn_dtype_t
+ *     O    [B][q_len][Hq][D]      float32
+ *     lse  [B][q_len][Hq]         float32 (natural log)
+ * Query head h reads KV head h / G with G = Hq / Hkv (contiguous groups).
+ * kv_lens[b] is the number of cached tokens of sequence b (tokens at or past
+ * kv_lens[b] are never read, so they may hold anything, NaN included).  With
+ * causal = 1 the q_len new tokens are the last q_len cached positions and
+ * query token i sees keys t <= kv_lens[b] - q_len + i.  A row that sees no
+ * key gets O = 0 and lse = -inf.
+ *
+ * Ownership and streams.  The caller allocates every buffer (device memory
+ * for tensors, kv_lens and the workspace) and keeps it alive until the work
+ * on the stream completes.  The library allocates nothing, keeps no device
+ * state, never synchronises, and caches only the CU count per device.  All
+ * work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *
+ * Null tensors are accepted where they would hold no element (K and V when
+ * max_kv_len == 0, every tensor when B == 0).
+ *
+ * Errors.  Arguments are validated on the host before anything is launched;
+ * on error nothing is enqueued or written and a status other than ATTN_OK is
+ * returned.  ATTN_ERR_HIP reports a failed launch.  No C++ exception crosses
+ * the ABI.  Non-finite inputs propagate into the outputs unchecked.  The
+ * values of kv_lens live on the device and cannot be checked on the host:
+ * they are clamped to [0, max_kv_len] inside the kernels.
+ * Thread safety: every function is reentrant.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  ATTN_ERR_SHAPE = 2,       /* a size is out of range or Hq % Hkv != 0            */
+  ATTN_ERR_DTYPE = 3,       /* unknown element type                               */
+  ATTN_ERR_ALIGN = 4,       /* a tensor base is not 16-byte (4-byte for fp32 out) aligned */
+  ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returned     */
+  ATTN_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed          */
+  ATTN_ERR_UNSUPPORTED = 7, /* head_dim other than 64 or 128, or a shape the kernels do not cover */
+  ATTN_ERR_VALUE = 8        /* non-finite scale, or chunk_len not a positive multiple of 64 */
+} attn_status_t;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype_t;
+
+/* One decode call.  B = batch >= 0, q_len >= 1, Hq % Hkv == 0, D in {64, 128},
+ * 0 <= max_kv_len < 2^31.  kv_lens: device int32[B], or NULL for "every
+ * sequence holds max_kv_len tokens".  scale: logit multiplier, normally
+ * 1/sqrt(D).  chunk_len: 0 lets the partitioner choose the chunk length; a
+ * positive multiple of 64 forces it. */
+typedef struct {
+  int32_t batch;
+  int32_t q_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t causal;
+  int64_t max_kv_len;
+  const int32_t *kv_lens;
+  float scale;
+  int32_t chunk_len;
+  attn_dtype_t dtype;
+} attn_desc_t;
+
+/* The partitioner's decision for a descriptor (introspection and tests). */
+typedef struct {
+  int32_t kernel;            /* 0: VALU split-KV kernel, 1: MFMA query-block kernel   */
+  int32_t rows;              /* R = (Hq / Hkv) * q_len query rows per (b, KV head)     */
+  int32_t rows_per_block;    /* query rows one work item carries                       */
+  int32_t row_blocks;        /* ceil(R / rows_per_block)                               */
+  int32_t chunk_len;         /* C: tokens per chunk                                    */
+  int32_t chunks_per_seq;    /* ceil(max_kv_len / C)                                   */
+  int64_t work_items;        /* B * Hkv * row_blocks * chunks_per_seq workgroups       */
+  int32_t threads_per_item;  /* threads per workgroup                                  */
+  int32_t cu_count;          /* compute units the plan was sized for                   */
+  size_t workspace_bytes;    /* partial (m, l, o) records: one per (item, row)         */
+} attn_plan_t;
+
+/* Partition a decode call for `cu_count` compute units (<= 0: those of the
+ * current device).  Splits each sequence's KV into chunks of C tokens so that
+ * the work items fill the GPU (Tree Attention's per-device local energies and
+ * Star Attention's per-host context blocks, placed on CUs).  Pure host code
+ * when cu_count > 0. */
+attn_status_t attn_decode_plan(const attn_desc_t *desc, int32_t cu_count, attn_plan_t *plan);
+
+/* Bytes of device workspace attn_decode / attn_decode_energy need for `desc`
+ * on the current device (0 is possible for an empty call). */
+attn_status_t attn_workspace_bytes(const attn_desc_t *desc, size_t *bytes);
+
+/* lse only: the energy F at zeta = 0, i.e. the logsumexp of every row, read
+ * from K alone (Tree Attention article, "an energy view of attention": the
+ * local energies are computed in parallel and combined by an associative
+ * reduction).  lse: float32 [B][q_len][Hq]. */
+attn_status_t attn_decode_energy(const attn_desc_t *desc, const void *q, const void *k,
+                                 float *lse, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* O and lse (definition above).  v has the layout of k. */
+attn_status_t attn_decode(const attn_desc_t *desc, const void *q, const void *k, const void *v,
+                          float *o, float *lse, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* The two phases of attn_decode / attn_decode_energy, for callers that time
+ * them separately or move the records between devices before merging (Tree
+ * Attention computes local energies per device and then reduces them; Star
+ * Attention's query host aggregates the hosts' softmax statistics).
+ *
+ * attn_decode_partials: one (m, l, o) record per (b, KV head, chunk, row)
+ * into `workspace` (sized by attn_workspace_bytes).  With v == NULL only
+ * (m, l) are produced (energy only).  Record layout, for the plan P returned
+ * by attn_decode_plan (groups = B * Hkv, Rp = P.row_blocks * P.rows_per_block,
+ * C = P.chunk_len, n = P.chunks_per_seq, X = roundup(4*groups*n*Rp, 256) bytes):
+ *   float m[groups][n][Rp] at byte 0       -- chunk max, in log2 units
+ *   float l[groups][n][Rp] at byte X       -- sum of 2^(s*log2e - m)
+ *   float o[groups][n][Rp][D] at byte 2X   -- unnormalised output
+ * Row r of group (b, kvh) is query token r / G, head kvh*G + r % G; chunk c
+ * covers tokens [c*C, (c+1)*C) and exists for c < ceil(kv_lens[b] / C).
+ *
+ * attn_decode_merge: merges each row's records (exact in any order), then
+ * O = o / l and lse = (m + log2 l) * ln 2.  o == NULL gives lse only; o !=
+ * NULL requires records produced with v != NULL.  Same desc and workspace as
+ * the attn_decode_partials call that filled it; errors as above. */
+attn_status_t attn_decode_partials(const attn_desc_t *desc, const void *q, const void *k,
+                                   const void *v, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+attn_status_t attn_decode_merge(const attn_desc_t *desc, float *o, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Shared-prefix batch sampling (Bifurcated Attention, TL;DR): S samples of
+ * one query token each attend over one shared prefix KV followed by their
+ * own decoded KV.  The prefix part runs as one multi-row contraction per KV
+ * head, so the prefix is read once for all samples; prefix and suffix
+ * partials are then merged exactly.  bf16 only; D in {64, 128}.
+ *     Q  [S][Hq][D]; Kp, Vp [Hkv][Lp][D]; Ks, Vs [S][Hkv][Ls][D]  (bf16)
+ *     O  [S][Hq][D] float32;  lse [S][Hq] float32
+ * Lp >= 0 and Ls >= 0; when both are 0 every row is empty. */
+typedef struct {
+  int32_t num_samples;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int64_t prefix_len;
+  int64_t suffix_len;
+  float scale;
+  attn_dtype_t dtype;
+} attn_bifurcated_desc_t;
+
+attn_status_t attn_bifurcated_workspace_bytes(const attn_bifurcated_desc_t *desc, size_t *bytes);
+
+attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const void *q,
+                                     const void *k_prefix, const void *v_prefix,
+                                     const void *k_suffix, const void *v_suffix, float *o,
+                                     float *lse, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* Static text for a status code. */
+const char *attn_status_string(attn_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DECODE_H */

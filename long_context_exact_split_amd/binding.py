@@ -1,0 +1,311 @@
+"""ctypes binding of ``libattn_decode.so`` (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels.  This module
+checks tensor shapes/dtypes, allocates outputs and the workspace with torch
+(device memory is the only thing torch provides), passes raw pointers and the
+current HIP stream, and turns status codes into ``AttnError``.  If the library
+is not built the functions raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libattn_decode.so"
+
+ATTN_BF16, ATTN_F32 = 0, 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
+          4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP",
+          7: "ATTN_ERR_UNSUPPORTED", 8: "ATTN_ERR_VALUE"}
+EXPORTS = ("attn_decode_plan", "attn_workspace_bytes", "attn_decode_energy", "attn_decode",
+           "attn_decode_partials", "attn_decode_merge", "attn_bifurcated_workspace_bytes",
+           "attn_decode_bifurcated", "attn_status_string")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = STATUS.get(status, str(status))
+        if _lib is not None:
+            msg += ": " + _lib.attn_status_string(status).decode()
+        super().__init__(f"{where}: {msg}")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("max_kv_len", ctypes.c_int64), ("kv_lens", ctypes.c_void_p),
+                ("scale", ctypes.c_float), ("chunk_len", ctypes.c_int32),
+                ("dtype", ctypes.c_int)]
+
+
+class AttnPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("rows_per_block", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int32), ("chunks_per_seq", ctypes.c_int32),
+                ("work_items", ctypes.c_int64), ("threads_per_item", ctypes.c_int32),
+                ("cu_count", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class AttnBifDesc(ctypes.Structure):
+    _fields_ = [("num_samples", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("prefix_len", ctypes.c_int64), ("suffix_len", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return os.path.join(PKG, LIB_NAME)
+
+
+def load_library():
+    """Load the HIP library (raises AttnError-free RuntimeError if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
+                               "(or python -m long_context_exact_split_amd.build)")
+        lib = ctypes.CDLL(path)
+        P, c = ctypes.POINTER, ctypes
+        lib.attn_decode_plan.argtypes = [P(AttnDesc), c.c_int32, P(AttnPlan)]
+        lib.attn_workspace_bytes.argtypes = [P(AttnDesc), P(c.c_size_t)]
+        lib.attn_decode_energy.argtypes = [P(AttnDesc), c.c_void_p, c.c_void_p, c.c_void_p,
+                                           c.c_void_p, c.c_size_t, c.c_void_p]
+        lib.attn_decode.argtypes = [P(AttnDesc), c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                    c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
+        lib.attn_decode_partials.argtypes = [P(AttnDesc), c.c_void_p, c.c_void_p, c.c_void_p,
+                                             c.c_void_p, c.c_size_t, c.c_void_p]
+        lib.attn_decode_merge.argtypes = [P(AttnDesc), c.c_void_p, c.c_void_p, c.c_void_p,
+                                          c.c_size_t, c.c_void_p]
+        lib.attn_bifurcated_workspace_bytes.argtypes = [P(AttnBifDesc), P(c.c_size_t)]
+        lib.attn_decode_bifurcated.argtypes = [P(AttnBifDesc)] + [c.c_void_p] * 8 + [
+            c.c_size_t, c.c_void_p]
+        for name in EXPORTS[:-1]:
+            getattr(lib, name).restype = c.c_int
+        lib.attn_status_string.argtypes = [c.c_int]
+        lib.attn_status_string.restype = c.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise AttnError(status, where)
+
+
+def make_desc(*, batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, kv_lens_ptr=0,
+              scale=None, causal=False, chunk_len=0, dtype=ATTN_BF16) -> AttnDesc:
+    d = AttnDesc()
+    d.batch, d.q_len, d.num_q_heads, d.num_kv_heads = batch, q_len, num_q_heads, num_kv_heads
+    d.head_dim, d.causal, d.max_kv_len = head_dim, int(bool(causal)), max_kv_len
+    d.kv_lens = kv_lens_ptr or None
+    d.scale = (1.0 / math.sqrt(head_dim) if head_dim > 0 else 1.0) if scale is None else scale
+    d.chunk_len, d.dtype = chunk_len, dtype
+    return d
+
+
+def plan(desc: AttnDesc, cu_count: int = 0) -> dict:
+    """The partitioner's decision (pure host code when cu_count > 0)."""
+    lib = load_library()
+    p = AttnPlan()
+    _check(lib.attn_decode_plan(ctypes.byref(desc), cu_count, ctypes.byref(p)), "attn_decode_plan")
+    return p.as_dict()
+
+
+def workspace_bytes(desc: AttnDesc) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "attn_workspace_bytes")
+    return n.value
+
+
+# ----------------------------------------------------------------------------
+# torch-facing wrappers
+# ----------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream_ptr(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _decode_desc(q, k, kv_lens, scale, causal, chunk_len) -> AttnDesc:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, q_len, Hq, D] and k/v [B, Hkv, L, D]")
+    B, q_len, Hq, D = q.shape
+    Bk, Hkv, L, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
+    if kv_lens is not None:
+        torch = _torch()
+        if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
+            raise ValueError("kv_lens must be int32[B] on the device of q")
+        if not kv_lens.is_contiguous():
+            raise ValueError("kv_lens must be contiguous")
+    return make_desc(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                     max_kv_len=L, kv_lens_ptr=_ptr(kv_lens), scale=scale, causal=causal,
+                     chunk_len=chunk_len, dtype=_dtype_code(q))
+
+
+def _check_tensors(*ts):
+    ref = ts[0]
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k and v must share dtype and device")
+
+
+def decode(q, k, v, kv_lens=None, *, scale: Optional[float] = None, causal: bool = False,
+           chunk_len: int = 0, out=None, lse=None, workspace=None) -> Tuple[object, object]:
+    """Exact attention decode: returns (O float32 [B,q_len,Hq,D], lse float32 [B,q_len,Hq])."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensors(q, k, v)
+    if v.shape != k.shape:
+        raise ValueError("v must have the shape of k")
+    desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
+    B, q_len, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty((B, q_len, Hq, D), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        ws = _workspace(workspace_bytes(desc), q.device, workspace)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib.attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                               _ptr(lse), _ptr(ws), nbytes, _stream_ptr(q.device)), "attn_decode")
+    return out, lse
+
+
+class Phases:
+    """The two phases of one decode call on fixed buffers: ``partials()``
+    launches the split-KV kernel (records into the workspace), ``merge()``
+    the merge + normalisation.  Used to time the kernels separately."""
+
+    def __init__(self, q, k, v, kv_lens=None, *, scale=None, causal=False, chunk_len=0):
+        torch = _torch()
+        self.lib = load_library()
+        _check_tensors(q, k, v)
+        self.desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
+        B, q_len, Hq, D = q.shape
+        self.q, self.k, self.v, self.kv_lens = q, k, v, kv_lens
+        self.out = torch.empty((B, q_len, Hq, D), dtype=torch.float32, device=q.device)
+        self.lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        self.ws = _workspace(workspace_bytes(self.desc), q.device, None)
+        self.nbytes = 0 if self.ws is None else self.ws.numel()
+        self.plan = plan(self.desc)
+        self.stream = _stream_ptr(q.device)
+
+    def partials(self):
+        _check(self.lib.attn_decode_partials(ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k),
+                                             _ptr(self.v), _ptr(self.ws), self.nbytes,
+                                             self.stream), "attn_decode_partials")
+
+    def merge(self):
+        _check(self.lib.attn_decode_merge(ctypes.byref(self.desc), _ptr(self.out), _ptr(self.lse),
+                                          _ptr(self.ws), self.nbytes, self.stream),
+               "attn_decode_merge")
+
+
+def decode_energy(q, k, kv_lens=None, *, scale: Optional[float] = None, causal: bool = False,
+                  chunk_len: int = 0, lse=None, workspace=None):
+    """Energy only (reads K, not V): returns lse float32 [B, q_len, Hq]."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensors(q, k)
+    desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
+    B, q_len, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        if lse is None:
+            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        ws = _workspace(workspace_bytes(desc), q.device, workspace)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib.attn_decode_energy(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(ws),
+                                      nbytes, _stream_ptr(q.device)), "attn_decode_energy")
+    return lse
+
+
+def bifurcated_desc(q, kp, ks, scale=None) -> AttnBifDesc:
+    S, Hq, D = q.shape
+    Hkv, Lp, Dp = kp.shape
+    if ks.dim() != 4 or ks.shape[0] != S or ks.shape[1] != Hkv or ks.shape[3] != D or Dp != D:
+        raise ValueError("q [S,Hq,D], k_prefix [Hkv,Lp,D], k_suffix [S,Hkv,Ls,D]")
+    d = AttnBifDesc()
+    d.num_samples, d.num_q_heads, d.num_kv_heads, d.head_dim = S, Hq, Hkv, D
+    d.prefix_len, d.suffix_len = Lp, ks.shape[2]
+    d.scale = (1.0 / math.sqrt(D)) if scale is None else scale
+    d.dtype = _dtype_code(q)
+    return d
+
+
+def decode_bifurcated(q, k_prefix, v_prefix, k_suffix, v_suffix, *, scale: Optional[float] = None,
+                      out=None, lse=None, workspace=None):
+    """Shared-prefix batch sampling: returns (O float32 [S,Hq,D], lse float32 [S,Hq])."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensors(q, k_prefix, v_prefix, k_suffix, v_suffix)
+    if v_prefix.shape != k_prefix.shape or v_suffix.shape != k_suffix.shape:
+        raise ValueError("v tensors must match k tensors")
+    desc = bifurcated_desc(q, k_prefix, k_suffix, scale)
+    S, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+        n = ctypes.c_size_t(0)
+        _check(lib.attn_bifurcated_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+               "attn_bifurcated_workspace_bytes")
+        ws = _workspace(n.value, q.device, workspace)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib.attn_decode_bifurcated(ctypes.byref(desc), _ptr(q), _ptr(k_prefix),
+                                          _ptr(v_prefix), _ptr(k_suffix), _ptr(v_suffix),
+                                          _ptr(out), _ptr(lse), _ptr(ws), nbytes,
+                                          _stream_ptr(q.device)), "attn_decode_bifurcated")
+    return out, lse

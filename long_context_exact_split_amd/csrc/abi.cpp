@@ -1,0 +1,374 @@
+// C-ABI entry points: validate on the host, partition, enqueue the split
+// kernel(s) and the merge on the caller's stream.  Nothing here allocates,
+// synchronises or keeps device state (the CU count per device is cached).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "attn_decode.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+using namespace attn;
+
+#ifndef ATTN_HAVE_MFMA
+#define ATTN_HAVE_MFMA 0
+#endif
+constexpr bool kMfma = ATTN_HAVE_MFMA != 0;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_cache[kMaxDevices];
+
+attn_status_t device_cu_count(int *cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cu = c;
+      return ATTN_OK;
+    }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+    return ATTN_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_cache[dev].store(c, std::memory_order_relaxed);
+  *cu = c;
+  return ATTN_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Lay the (m, l, o) records of a plan out in a workspace slice.
+PartialLayout carve(char *base, const attn_plan_t &p, int64_t groups, int head_dim) {
+  PartialLayout pl{};
+  pl.chunks = p.chunks_per_seq;
+  pl.rows = p.row_blocks * p.rows_per_block;
+  const int64_t records = groups * (int64_t)pl.chunks * pl.rows;
+  if (records <= 0 || !base) return pl;
+  const int64_t ml = round_up(records * (int64_t)sizeof(float), 256);
+  pl.m = reinterpret_cast<float *>(base);
+  pl.l = reinterpret_cast<float *>(base + ml);
+  pl.o = reinterpret_cast<float *>(base + 2 * ml);
+  return pl;
+}
+
+SplitArgs split_args(const attn_desc_t *d, const attn_plan_t &p, const void *q, const void *k,
+                     const void *v, const PartialLayout &part) {
+  SplitArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_lens = d->kv_lens;
+  a.part = part;
+  a.L_max = d->max_kv_len;
+  a.B = d->batch;
+  a.q_len = d->q_len;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.G = d->num_q_heads / d->num_kv_heads;
+  a.R = p.rows;
+  a.row_blocks = p.row_blocks;
+  a.chunk_len = p.chunk_len;
+  a.n_chunks = p.chunks_per_seq;
+  a.causal = d->causal;
+  a.scale_log2 = d->scale * kLog2eHost;
+  return a;
+}
+
+hipError_t launch_split(const attn_desc_t *d, const attn_plan_t &p, const SplitArgs &a,
+                        bool energy, hipStream_t s) {
+  if (p.work_items <= 0) return hipSuccess;
+  if (p.kernel == 1) return launch_split_mfma(p, a, d->head_dim, energy, s);
+  return launch_split_valu(p, a, d->dtype, d->head_dim, energy, s);
+}
+
+// Shared preamble of the decode entry points: validate, plan, check the
+// workspace.  Returns ATTN_OK with *empty set when there is nothing to do.
+attn_status_t prepare(const attn_desc_t *d, void *ws, size_t ws_bytes, attn_plan_t *p,
+                      PartialLayout *part, bool *empty) {
+  *empty = false;
+  attn_status_t st = validate_desc(d);
+  if (st != ATTN_OK) return st;
+  if (d->batch == 0) {
+    *empty = true;
+    return ATTN_OK;
+  }
+  int cu = 0;
+  if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
+  if ((st = make_plan(d, cu, kMfma, p)) != ATTN_OK) return st;
+  if (p->workspace_bytes > 0 && !ws) return ATTN_ERR_NULL;
+  if (ws_bytes < p->workspace_bytes) return ATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return ATTN_ERR_ALIGN;
+  *part = carve(static_cast<char *>(ws), *p, (int64_t)d->batch * d->num_kv_heads, d->head_dim);
+  return ATTN_OK;
+}
+
+attn_status_t check_inputs(const attn_desc_t *d, const void *q, const void *k, const void *v,
+                           bool need_v) {
+  attn_status_t st = validate_desc(d);
+  if (st != ATTN_OK) return st;
+  // An empty call may pass null tensors (torch gives empty tensors a null base).
+  const bool any_q = d->batch > 0, any_kv = any_q && d->max_kv_len > 0;
+  if ((any_q && !q) || (any_kv && (!k || (need_v && !v)))) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || (v && !aligned(v, 16))) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+attn_status_t check_outputs(const attn_desc_t *d, const float *o, const float *lse, bool need_o) {
+  attn_status_t st = validate_desc(d);
+  if (st != ATTN_OK) return st;
+  if (!lse || (need_o && !o)) return ATTN_ERR_NULL;
+  if (!aligned(lse, 4) || (o && !aligned(o, 4))) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+attn_status_t partials_impl(const attn_desc_t *d, const void *q, const void *k, const void *v,
+                            void *ws, size_t ws_bytes, void *stream) {
+  attn_plan_t p;
+  PartialLayout part;
+  bool empty;
+  attn_status_t st = prepare(d, ws, ws_bytes, &p, &part, &empty);
+  if (st != ATTN_OK || empty) return st;
+  (void)hipGetLastError();
+  if (launch_split(d, p, split_args(d, p, q, k, v, part), v == nullptr,
+                   static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status_t merge_impl(const attn_desc_t *d, float *o, float *lse, void *ws, size_t ws_bytes,
+                         void *stream) {
+  attn_plan_t p;
+  PartialLayout part;
+  bool empty;
+  attn_status_t st = prepare(d, ws, ws_bytes, &p, &part, &empty);
+  if (st != ATTN_OK || empty) return st;
+  MergeArgs m{};
+  m.part = part;
+  m.kv_lens = d->kv_lens;
+  m.L_max = d->max_kv_len;
+  m.B = d->batch;
+  m.q_len = d->q_len;
+  m.Hq = d->num_q_heads;
+  m.Hkv = d->num_kv_heads;
+  m.G = d->num_q_heads / d->num_kv_heads;
+  m.R = p.rows;
+  m.chunk_len = p.chunk_len;
+  m.o = o;
+  m.lse = lse;
+  (void)hipGetLastError();
+  if (launch_merge(m, d->head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status_t decode_impl(const attn_desc_t *d, const void *q, const void *k, const void *v,
+                          float *o, float *lse, void *ws, size_t ws_bytes, void *stream,
+                          bool energy) {
+  attn_status_t st = check_inputs(d, q, k, v, !energy);
+  if (st != ATTN_OK) return st;
+  if ((st = check_outputs(d, o, lse, !energy)) != ATTN_OK) return st;
+  if ((st = partials_impl(d, q, k, energy ? nullptr : v, ws, ws_bytes, stream)) != ATTN_OK)
+    return st;
+  return merge_impl(d, energy ? nullptr : o, lse, ws, ws_bytes, stream);
+}
+
+struct BifPlans {
+  attn_desc_t pre, suf;
+  attn_plan_t pp, sp;
+  size_t pre_bytes, total;
+};
+
+attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans *b) {
+  bifurcated_descs(d, &b->pre, &b->suf);
+  attn_status_t st;
+  if ((st = make_plan(&b->pre, cu, kMfma, &b->pp)) != ATTN_OK) return st;
+  if ((st = make_plan(&b->suf, cu, kMfma, &b->sp)) != ATTN_OK) return st;
+  b->pre_bytes = (size_t)round_up((int64_t)b->pp.workspace_bytes, 256);
+  b->total = b->pre_bytes + b->sp.workspace_bytes;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+#if !ATTN_HAVE_MFMA
+hipError_t attn::launch_split_mfma(const attn_plan_t &, const SplitArgs &, int, bool, hipStream_t) {
+  return hipErrorInvalidValue;
+}
+#endif
+
+extern "C" {
+
+attn_status_t attn_decode_plan(const attn_desc_t *desc, int32_t cu_count, attn_plan_t *plan) {
+  try {
+    attn_status_t st = validate_desc(desc);
+    if (st != ATTN_OK) return st;
+    if (!plan) return ATTN_ERR_NULL;
+    int cu = cu_count;
+    if (cu <= 0 && (st = device_cu_count(&cu)) != ATTN_OK) return st;
+    return make_plan(desc, cu, kMfma, plan);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_workspace_bytes(const attn_desc_t *desc, size_t *bytes) {
+  try {
+    attn_status_t st = validate_desc(desc);
+    if (st != ATTN_OK) return st;
+    if (!bytes) return ATTN_ERR_NULL;
+    *bytes = 0;
+    if (desc->batch == 0) return ATTN_OK;
+    int cu = 0;
+    if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
+    attn_plan_t p;
+    if ((st = make_plan(desc, cu, kMfma, &p)) != ATTN_OK) return st;
+    *bytes = p.workspace_bytes;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode_energy(const attn_desc_t *desc, const void *q, const void *k,
+                                 float *lse, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+  try {
+    return decode_impl(desc, q, k, nullptr, nullptr, lse, workspace, workspace_bytes, stream,
+                       true);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode(const attn_desc_t *desc, const void *q, const void *k, const void *v,
+                          float *o, float *lse, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  try {
+    return decode_impl(desc, q, k, v, o, lse, workspace, workspace_bytes, stream, false);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode_partials(const attn_desc_t *desc, const void *q, const void *k,
+                                   const void *v, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  try {
+    attn_status_t st = check_inputs(desc, q, k, v, false);
+    if (st != ATTN_OK) return st;
+    return partials_impl(desc, q, k, v, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode_merge(const attn_desc_t *desc, float *o, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  try {
+    attn_status_t st = check_outputs(desc, o, lse, false);
+    if (st != ATTN_OK) return st;
+    return merge_impl(desc, o, lse, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_bifurcated_workspace_bytes(const attn_bifurcated_desc_t *desc, size_t *bytes) {
+  try {
+    attn_status_t st = validate_bifurcated(desc);
+    if (st != ATTN_OK) return st;
+    if (!bytes) return ATTN_ERR_NULL;
+    *bytes = 0;
+    if (desc->num_samples == 0) return ATTN_OK;
+    int cu = 0;
+    if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
+    BifPlans b;
+    if ((st = bifurcated_plans(desc, cu, &b)) != ATTN_OK) return st;
+    *bytes = b.total;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const void *q,
+                                     const void *k_prefix, const void *v_prefix,
+                                     const void *k_suffix, const void *v_suffix, float *o,
+                                     float *lse, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+  try {
+    attn_status_t st = validate_bifurcated(desc);
+    if (st != ATTN_OK) return st;
+    if (!q || !o || !lse || (desc->prefix_len > 0 && (!k_prefix || !v_prefix)) ||
+        (desc->suffix_len > 0 && (!k_suffix || !v_suffix)))
+      return ATTN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_prefix, 16) || !aligned(v_prefix, 16) ||
+        !aligned(k_suffix, 16) || !aligned(v_suffix, 16) || !aligned(o, 4) || !aligned(lse, 4))
+      return ATTN_ERR_ALIGN;
+    if (desc->num_samples == 0) return ATTN_OK;
+    int cu = 0;
+    if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
+    BifPlans b;
+    if ((st = bifurcated_plans(desc, cu, &b)) != ATTN_OK) return st;
+    if (b.total > 0 && !workspace) return ATTN_ERR_NULL;
+    if (workspace_bytes < b.total) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+    char *ws = static_cast<char *>(workspace);
+    const PartialLayout pre = carve(ws, b.pp, (int64_t)desc->num_kv_heads, desc->head_dim);
+    const PartialLayout suf = carve(ws + b.pre_bytes, b.sp,
+                                    (int64_t)desc->num_samples * desc->num_kv_heads,
+                                    desc->head_dim);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (launch_split(&b.pre, b.pp, split_args(&b.pre, b.pp, q, k_prefix, v_prefix, pre), false,
+                     s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if (launch_split(&b.suf, b.sp, split_args(&b.suf, b.sp, q, k_suffix, v_suffix, suf), false,
+                     s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    MergeArgs m{};
+    m.part = suf;
+    if (b.pp.work_items > 0) m.shared = pre;
+    m.kv_lens = nullptr;
+    m.L_max = desc->suffix_len;
+    m.B = desc->num_samples;
+    m.q_len = 1;
+    m.Hq = desc->num_q_heads;
+    m.Hkv = desc->num_kv_heads;
+    m.G = desc->num_q_heads / desc->num_kv_heads;
+    m.R = m.G;
+    m.chunk_len = b.sp.chunk_len;
+    m.o = o;
+    m.lse = lse;
+    if (launch_merge(m, desc->head_dim, s) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+const char *attn_status_string(attn_status_t status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is null";
+    case ATTN_ERR_SHAPE: return "a size is out of range, or num_q_heads % num_kv_heads != 0";
+    case ATTN_ERR_DTYPE: return "unknown element type";
+    case ATTN_ERR_ALIGN: return "a tensor base pointer is misaligned";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than the size query returned";
+    case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case ATTN_ERR_UNSUPPORTED: return "shape not covered by the kernels (head_dim must be 64 or 128)";
+    case ATTN_ERR_VALUE: return "invalid scalar: non-finite scale, causal not 0/1, or chunk_len "
+                                "not a non-negative multiple of 64";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

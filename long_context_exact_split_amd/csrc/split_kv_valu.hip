@@ -1,0 +1,389 @@
+// Split-KV decode on the vector ALUs (gfx950, wave64).
+//
+// One workgroup = one work item (sequence b, KV head, row block, chunk of C
+// tokens).  It streams the chunk's K and V rows from HBM exactly once and
+// serves every query row of the GQA group from them, producing the chunk's
+// softmax statistics m = max s, l = sum e^(s-m) and the unnormalised output
+// o = sum e^(s-m) v ("attention acceleration" concept page, section 2.1,
+// online softmax; the chunks stand in for the per-device local energies of
+// the Tree Attention article and the per-host blocks of Star Attention's
+// phase 2).  A second kernel (merge_partials below) combines the records.
+//
+// Lane layout: a key row of D elements is read by LPK lanes with one 16-byte
+// load each, so a wave load covers KPW = 64 / LPK consecutive keys (1 KiB of
+// contiguous memory for bf16, D = 128).  Each lane keeps its slice of every
+// query row of the block in registers; the slice dot products are combined
+// across the LPK lanes with DPP row operations.  Every group of LPK lanes runs
+// its own online softmax over the keys it reads (tile-level rescaling, taken
+// only when the running max grows by more than 2^8), and the key slots and
+// waves are merged once at the end of the chunk.
+//
+// Logits are kept in log2 units (scale * log2 e folded into one fp32
+// multiply after the fp32 dot product), so exponentials are v_exp_f32.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr float kLazyRescale = 8.0f;  // log2 units: rescale only past a 256x growth
+
+template <typename T, int D>
+struct Geometry {
+  static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane per 16-byte load
+  static constexpr int LPK = D / EPL;              // lanes per key row
+  static constexpr int KPW = kWave / LPK;          // keys per wave load
+};
+
+template <typename T>
+__device__ __forceinline__ void widen(const uint4 &w, float (&f)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+    f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+    f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+  } else {
+    f[0] = __builtin_bit_cast(float, w.x); f[1] = __builtin_bit_cast(float, w.y);
+    f[2] = __builtin_bit_cast(float, w.z); f[3] = __builtin_bit_cast(float, w.w);
+  }
+}
+
+// Slice dot product: bf16 pairs on v_dot2_f32_bf16 (exact products, fp32
+// accumulation), fp32 on FMAs.
+template <typename T>
+__device__ __forceinline__ float slice_dot(const uint4 &q, const uint4 &k) {
+  if constexpr (sizeof(T) == 2) {
+    float acc = dot2_bf16(q.x, k.x, 0.0f);
+    acc = dot2_bf16(q.y, k.y, acc);
+    acc = dot2_bf16(q.z, k.z, acc);
+    return dot2_bf16(q.w, k.w, acc);
+  } else {
+    float acc = __builtin_bit_cast(float, q.x) * __builtin_bit_cast(float, k.x);
+    acc = fmaf(__builtin_bit_cast(float, q.y), __builtin_bit_cast(float, k.y), acc);
+    acc = fmaf(__builtin_bit_cast(float, q.z), __builtin_bit_cast(float, k.z), acc);
+    return fmaf(__builtin_bit_cast(float, q.w), __builtin_bit_cast(float, k.w), acc);
+  }
+}
+
+template <typename T, int D, int RB, int KT, bool ENERGY>
+__global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
+  using Geo = Geometry<T, D>;
+  constexpr int EPL = Geo::EPL, LPK = Geo::LPK, KPW = Geo::KPW;
+  constexpr int TK = KPW * KT;  // keys per wave tile
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int kr = lane / LPK;  // key slot in a wave load
+  const int kl = lane % LPK;  // slice of the key row
+
+  int item = blockIdx.x;
+  const int chunk = item % a.n_chunks;
+  item /= a.n_chunks;
+  const int rb = item % a.row_blocks;
+  const int group = item / a.row_blocks;
+  const int b = group / a.Hkv;
+  const int kvh = group - b * a.Hkv;
+
+  int Lb = a.kv_lens ? a.kv_lens[b] : (int)a.L_max;
+  Lb = Lb < 0 ? 0 : (Lb > (int)a.L_max ? (int)a.L_max : Lb);
+  const int c0 = chunk * a.chunk_len;
+  if (c0 >= Lb) return;  // past the sequence: the merge reads ceil(L_b / C) records only
+  const int c1 = min(c0 + a.chunk_len, Lb);
+
+  // Visibility limit per row (keys t < lim[r]) and the query slices.
+  int lim[RB];
+  int hi = c0;
+  uint4 q[RB];
+  const T *Q = static_cast<const T *>(a.q);
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int rg = rb * RB + r;
+    int n = c0;
+    q[r] = make_uint4(0, 0, 0, 0);
+    if (rg < a.R) {
+      const int i = rg / a.G;
+      const int h = kvh * a.G + (rg - i * a.G);
+      n = a.causal ? Lb - a.q_len + i + 1 : Lb;
+      n = n < c0 ? c0 : (n > c1 ? c1 : n);
+      const T *qrow = Q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + kl * EPL;
+      q[r] = *reinterpret_cast<const uint4 *>(qrow);
+    }
+    lim[r] = n;
+    hi = max(hi, n);
+  }
+
+  float m[RB], l[RB], o[RB][ENERGY ? 1 : EPL];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.0f;
+    if constexpr (!ENERGY) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[r][e] = 0.0f;
+    }
+  }
+
+  const int64_t row_base = (int64_t)group * a.L_max * D + kl * EPL;
+  const T *kbase = static_cast<const T *>(a.k) + row_base;
+  const T *vbase = ENERGY ? nullptr : static_cast<const T *>(a.v) + row_base;
+  const int n_tiles = (hi - c0 + TK - 1) / TK;
+
+  uint4 kc[KT], vc[ENERGY ? 1 : KT];
+  auto load_tile = [&](int tile, uint4 (&kd)[KT], uint4 (&vd)[ENERGY ? 1 : KT]) {
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      int t = c0 + tile * TK + j * KPW + kr;
+      t = t < hi ? t : hi - 1;  // clamp: masked keys read a valid row
+      kd[j] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)t * D);
+      if constexpr (!ENERGY) vd[j] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)t * D);
+    }
+  };
+
+  int tile = wave;
+  if (tile < n_tiles) load_tile(tile, kc, vc);
+  for (; tile < n_tiles; tile += kWaves) {
+    // Prefetch the wave's next tile (or re-read this one, an L2 hit, on the last).
+    uint4 kn[KT], vn[ENERGY ? 1 : KT];
+    load_tile(tile + kWaves < n_tiles ? tile + kWaves : tile, kn, vn);
+
+    float s[KT][RB];
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+#pragma unroll
+      for (int r = 0; r < RB; ++r) s[j][r] = group_sum<LPK>(slice_dot<T>(q[r], kc[j]));
+
+    float tmax[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) tmax[r] = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int t = c0 + tile * TK + j * KPW + kr;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        s[j][r] = t < lim[r] ? s[j][r] * a.scale_log2 : -INFINITY;
+        tmax[r] = fmaxf(tmax[r], s[j][r]);
+      }
+    }
+    bool need = false;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) need |= tmax[r] > m[r] + kLazyRescale;
+    if (__any(need)) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const float mn = fmaxf(m[r], tmax[r]);
+        const float alpha = rescale_factor(m[r], mn);
+        l[r] *= alpha;
+        if constexpr (!ENERGY) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+        }
+        m[r] = mn;
+      }
+    }
+    float mref[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) mref[r] = m[r] == -INFINITY ? 0.0f : m[r];
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      float vf[EPL];
+      if constexpr (!ENERGY) widen<T>(vc[j], vf);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const float p = fast_exp2(s[j][r] - mref[r]);
+        l[r] += p;
+        if constexpr (!ENERGY) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      kc[j] = kn[j];
+      if constexpr (!ENERGY) vc[j] = vn[j];
+    }
+  }
+
+  // Merge the KPW key slots of the wave (lanes with equal kl).
+#pragma unroll
+  for (int off = LPK; off < kWave; off *= 2) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const float mo = __shfl_xor(m[r], off);
+      const float lo = __shfl_xor(l[r], off);
+      const float M = fmaxf(m[r], mo);
+      const float fa = rescale_factor(m[r], M), fb = rescale_factor(mo, M);
+      l[r] = l[r] * fa + lo * fb;
+      if constexpr (!ENERGY) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float oo = __shfl_xor(o[r][e], off);
+          o[r][e] = o[r][e] * fa + oo * fb;
+        }
+      }
+      m[r] = M;
+    }
+  }
+
+  // Merge the waves through LDS and write the chunk's record.
+  __shared__ float sm[kWaves][RB], sl[kWaves][RB];
+  __shared__ float so[ENERGY ? 1 : kWaves][ENERGY ? 1 : RB][ENERGY ? 1 : D];
+  if (kr == 0) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      if constexpr (!ENERGY) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) so[wave][r][kl * EPL + e] = o[r][e];
+      }
+      if (kl == 0) {
+        sm[wave][r] = m[r];
+        sl[wave][r] = l[r];
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t rec0 = ((int64_t)group * a.part.chunks + chunk) * a.part.rows + rb * RB;
+  constexpr int kOut = ENERGY ? RB : RB * D;
+  for (int idx = threadIdx.x; idx < kOut; idx += kThreads) {
+    const int r = ENERGY ? idx : idx / D;
+    const int d = ENERGY ? 0 : idx - r * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w][r]);
+    float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = rescale_factor(sm[w][r], M);
+      if constexpr (!ENERGY) acc += so[w][r][d] * f;
+      lsum += sl[w][r] * f;
+    }
+    if constexpr (!ENERGY) a.part.o[(rec0 + r) * D + d] = acc;
+    if (d == 0) {
+      a.part.m[rec0 + r] = M;
+      a.part.l[rec0 + r] = lsum;
+    }
+  }
+}
+
+// One wave per output row: merge the row's records (log-depth max over the
+// records with DPP, then one rescale of each record), normalise, write O, lse.
+template <int D, bool ENERGY>
+__global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
+  constexpr int EPM = D / kWave;  // output elements per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (row >= (int64_t)a.B * a.Hkv * a.R) return;
+  const int r = (int)(row % a.R);
+  const int group = (int)(row / a.R);
+  const int b = group / a.Hkv;
+  const int kvh = group - b * a.Hkv;
+
+  int64_t Lb = a.kv_lens ? (int64_t)a.kv_lens[b] : a.L_max;
+  Lb = Lb < 0 ? 0 : (Lb > a.L_max ? a.L_max : Lb);
+  int P = (int)((Lb + a.chunk_len - 1) / a.chunk_len);
+  P = min(P, a.part.chunks);
+  const int S = a.shared.m ? a.shared.chunks : 0;
+
+  const int64_t pstride = a.part.rows;
+  const int64_t prow = (int64_t)group * a.part.chunks * pstride + r;
+  const int64_t sstride = a.shared.rows;
+  const int64_t srow = a.shared.m ? (int64_t)kvh * a.shared.chunks * sstride + (int64_t)b * a.R + r : 0;
+
+  float M = -INFINITY;
+  for (int c = lane; c < P + S; c += kWave)
+    M = fmaxf(M, c < P ? a.part.m[prow + c * pstride] : a.shared.m[srow + (c - P) * sstride]);
+  M = wave_max(M);
+
+  float lsum = 0.0f, acc[EPM];
+#pragma unroll
+  for (int e = 0; e < EPM; ++e) acc[e] = 0.0f;
+#pragma unroll 4
+  for (int c = 0; c < P; ++c) {
+    const int64_t rec = prow + c * pstride;
+    const float f = rescale_factor(a.part.m[rec], M);
+    lsum += f * a.part.l[rec];
+    if constexpr (!ENERGY) {
+#pragma unroll
+      for (int e = 0; e < EPM; ++e) acc[e] += f * a.part.o[rec * D + lane * EPM + e];
+    }
+  }
+#pragma unroll 4
+  for (int c = 0; c < S; ++c) {
+    const int64_t rec = srow + c * sstride;
+    const float f = rescale_factor(a.shared.m[rec], M);
+    lsum += f * a.shared.l[rec];
+    if constexpr (!ENERGY) {
+#pragma unroll
+      for (int e = 0; e < EPM; ++e) acc[e] += f * a.shared.o[rec * D + lane * EPM + e];
+    }
+  }
+
+  const int i = r / a.G;
+  const int h = kvh * a.G + (r - i * a.G);
+  const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
+  const bool empty = M == -INFINITY || !(lsum > 0.0f);
+  if (lane == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(lsum)) * kLn2;
+  if constexpr (!ENERGY) {
+    const float inv = empty ? 0.0f : 1.0f / lsum;
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) a.o[orow * D + lane * EPM + e] = acc[e] * inv;
+  }
+}
+
+template <typename T, int D, int RB, bool ENERGY>
+hipError_t launch_t(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+  constexpr int KT = RB <= 4 ? 8 : 4;
+  if (plan.work_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL((split_kv_valu<T, D, RB, KT, ENERGY>), dim3((unsigned)plan.work_items),
+                     dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool ENERGY>
+hipError_t launch_rb(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+  switch (plan.rows_per_block) {
+    case 1: return launch_t<T, D, 1, ENERGY>(plan, a, stream);
+    case 2: return launch_t<T, D, 2, ENERGY>(plan, a, stream);
+    case 4: return launch_t<T, D, 4, ENERGY>(plan, a, stream);
+    case 8: return launch_t<T, D, 8, ENERGY>(plan, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, bool ENERGY>
+hipError_t launch_d(const attn_plan_t &plan, const SplitArgs &a, int D, hipStream_t stream) {
+  return D == 64 ? launch_rb<T, 64, ENERGY>(plan, a, stream)
+                 : launch_rb<T, 128, ENERGY>(plan, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_split_valu(const attn_plan_t &plan, const SplitArgs &a, attn_dtype_t dtype,
+                             int head_dim, bool energy_only, hipStream_t stream) {
+  if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
+  if (dtype == ATTN_BF16)
+    return energy_only ? launch_d<uint16_t, true>(plan, a, head_dim, stream)
+                       : launch_d<uint16_t, false>(plan, a, head_dim, stream);
+  return energy_only ? launch_d<float, true>(plan, a, head_dim, stream)
+                     : launch_d<float, false>(plan, a, head_dim, stream);
+}
+
+hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.R;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  const bool energy = a.o == nullptr;
+  if (head_dim == 64) {
+    if (energy) hipLaunchKernelGGL((merge_partials<64, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((merge_partials<64, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (energy) hipLaunchKernelGGL((merge_partials<128, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((merge_partials<128, false>), grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,157 @@
+"""C-ABI boundary on the CPU: symbols, struct layout, validation errors.
+
+Every call here fails validation (or is a pure-host plan query), so no HIP
+runtime call is made and no GPU is needed."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from long_context_exact_split_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.skip("library not built")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("attn_decode_energy", "attn_decode", "attn_decode_bifurcated"):
+        assert n in names
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_[a-z_]+)\b", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_struct_layouts_match_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "attn_decode.h"
+#define F(T, m) printf(#T "." #m " %zu\\n", offsetof(T, m));
+int main(void) {
+  printf("attn_desc_t %zu\\n", sizeof(attn_desc_t));
+  F(attn_desc_t, max_kv_len) F(attn_desc_t, kv_lens) F(attn_desc_t, scale)
+  F(attn_desc_t, chunk_len) F(attn_desc_t, dtype)
+  printf("attn_plan_t %zu\\n", sizeof(attn_plan_t));
+  F(attn_plan_t, work_items) F(attn_plan_t, threads_per_item) F(attn_plan_t, workspace_bytes)
+  printf("attn_bifurcated_desc_t %zu\\n", sizeof(attn_bifurcated_desc_t));
+  F(attn_bifurcated_desc_t, prefix_len) F(attn_bifurcated_desc_t, scale) F(attn_bifurcated_desc_t, dtype)
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True,
+                                                               text=True, check=True).stdout.split("\n") if line)
+    structs = {"attn_desc_t": binding.AttnDesc, "attn_plan_t": binding.AttnPlan,
+               "attn_bifurcated_desc_t": binding.AttnBifDesc}
+    for key, val in got.items():
+        if "." in key:
+            s, f = key.split(".")
+            assert getattr(structs[s], f).offset == int(val), key
+        else:
+            assert ctypes.sizeof(structs[key]) == int(val), key
+
+
+def _desc(**kw):
+    base = dict(batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128, max_kv_len=1000)
+    base.update(kw)
+    return binding.make_desc(**base)
+
+
+BAD = [
+    (dict(num_q_heads=6, num_kv_heads=4), "ATTN_ERR_SHAPE"),
+    (dict(q_len=0), "ATTN_ERR_SHAPE"),
+    (dict(batch=-1), "ATTN_ERR_SHAPE"),
+    (dict(max_kv_len=-5), "ATTN_ERR_SHAPE"),
+    (dict(max_kv_len=2 ** 31), "ATTN_ERR_SHAPE"),
+    (dict(num_kv_heads=0), "ATTN_ERR_SHAPE"),
+    (dict(head_dim=96), "ATTN_ERR_UNSUPPORTED"),
+    (dict(head_dim=0), "ATTN_ERR_SHAPE"),
+    (dict(dtype=7), "ATTN_ERR_DTYPE"),
+    (dict(scale=float("nan")), "ATTN_ERR_VALUE"),
+    (dict(scale=float("inf")), "ATTN_ERR_VALUE"),
+    (dict(chunk_len=100), "ATTN_ERR_VALUE"),
+    (dict(chunk_len=-64), "ATTN_ERR_VALUE"),
+    (dict(causal=True), None),  # valid
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_validation_errors_before_any_hip_call(lib, kw, status):
+    d = _desc(**kw)
+    code = lib.attn_decode(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 1 << 30, None)
+    e = lib.attn_decode_energy(ctypes.byref(d), 16, 16, 16, 16, 1 << 30, None)
+    if status is None:
+        assert code not in (1, 2, 3, 4, 7, 8)  # may be ATTN_ERR_HIP without a GPU
+        return
+    assert binding.STATUS[code] == status and binding.STATUS[e] == status
+
+
+def test_null_and_alignment_errors(lib):
+    d = _desc()
+    assert binding.STATUS[lib.attn_decode(None, 16, 16, 16, 16, 16, 16, 1, None)] == "ATTN_ERR_NULL"
+    assert binding.STATUS[lib.attn_decode(ctypes.byref(d), 0, 16, 16, 16, 16, 16, 1, None)] == "ATTN_ERR_NULL"
+    assert binding.STATUS[lib.attn_decode(ctypes.byref(d), 16, 16, 0, 16, 16, 16, 1, None)] == "ATTN_ERR_NULL"
+    assert binding.STATUS[lib.attn_decode(ctypes.byref(d), 16, 16, 16, 0, 16, 16, 1, None)] == "ATTN_ERR_NULL"
+    # energy needs neither v nor o
+    assert binding.STATUS[lib.attn_decode_energy(ctypes.byref(d), 16, 16, 0, 16, 1, None)] == "ATTN_ERR_NULL"
+    assert binding.STATUS[lib.attn_decode(ctypes.byref(d), 8, 16, 16, 16, 16, 16, 1, None)] == "ATTN_ERR_ALIGN"
+    assert binding.STATUS[lib.attn_decode(ctypes.byref(d), 16, 16, 16, 18, 16, 16, 1, None)] == "ATTN_ERR_ALIGN"
+    # an empty batch is a valid no-op (no device needed)
+    e = _desc(batch=0)
+    assert lib.attn_decode(ctypes.byref(e), 16, 16, 16, 16, 16, 0, 0, None) == 0
+
+
+def test_bifurcated_validation(lib):
+    d = binding.AttnBifDesc()
+    d.num_samples, d.num_q_heads, d.num_kv_heads, d.head_dim = 4, 8, 2, 128
+    d.prefix_len, d.suffix_len, d.scale, d.dtype = 100, 10, 0.1, binding.ATTN_BF16
+    args = [16] * 7 + [16, 1 << 30, None]
+    d.num_q_heads = 7
+    assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *args)] == "ATTN_ERR_SHAPE"
+    d.num_q_heads = 8
+    d.dtype = binding.ATTN_F32
+    assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *args)] == "ATTN_ERR_UNSUPPORTED"
+    d.dtype = binding.ATTN_BF16
+    d.head_dim = 80
+    assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *args)] == "ATTN_ERR_UNSUPPORTED"
+    d.head_dim = 128
+    d.suffix_len = -1
+    assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *args)] == "ATTN_ERR_SHAPE"
+    d.suffix_len = 10
+    assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *([16] * 6 + [0, 16, 1, None]))] == "ATTN_ERR_NULL"
+    d.num_samples = 0
+    assert lib.attn_decode_bifurcated(ctypes.byref(d), *args) == 0
+
+
+def test_status_strings(lib):
+    for code, name in binding.STATUS.items():
+        s = lib.attn_status_string(code).decode()
+        assert s and s != "unknown status", name
+    assert lib.attn_status_string(99).decode() == "unknown status"

@@ -1,0 +1,274 @@
+"""HIP path (through the C ABI) against the fp64 oracle, element by element.
+
+Small shapes are compared on every output; the full-size workloads are
+compared on every row the oracle can afford (all rows for the 8B-shaped GQA
+decode and the bifurcated batch; sampled KV-head groups for the 5.12M-token
+cache and the 70B-shaped ragged batch)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import check_rows, dev, say, workload_tensors
+from long_context_exact_split_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(w, chunk_len=None):
+    q, k, v, lens = workload_tensors(w)
+    O, lse = binding.decode(q, k, v, lens, scale=w.scale, causal=w.causal,
+                            chunk_len=w.chunk_len if chunk_len is None else chunk_len)
+    torch.cuda.synchronize()
+    return O.cpu().numpy(), lse.cpu().numpy()
+
+
+def oracle_decode(w, rows=None):
+    return oracle.attend(w.q, w.k, w.v, w.kv_lens, w.scale, w.causal, rows=rows)
+
+
+# ----------------------------------------------------------------------------
+# The five workload shapes
+# ----------------------------------------------------------------------------
+def test_single_query_fp32_eight_chunks():
+    w = inputs.single_query_fp32(seed=1)
+    desc = binding.make_desc(batch=1, q_len=1, num_q_heads=1, num_kv_heads=1, head_dim=64,
+                             max_kv_len=4096, chunk_len=512, dtype=binding.ATTN_F32)
+    p = binding.plan(desc)
+    assert p["chunks_per_seq"] == 8
+    say(f"single_query_fp32 plan: {p}")
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what="single_query_fp32")
+
+
+def test_llama3_8b_gqa_full():
+    w = inputs.llama3_8b_gqa(seed=2)
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what="llama3_8b_gqa (B=8, L=32768)")
+
+
+# ----------------------------------------------------------------------------
+# Small shapes spanning several tiles and a ragged tail
+# ----------------------------------------------------------------------------
+SMALL = [
+    # B, q_len, Hq, Hkv, D, L, dtype, causal, lens
+    (1, 1, 1, 1, 64, 4096, "f32", False, None),
+    (1, 1, 8, 8, 128, 1000, "f32", False, None),
+    (2, 1, 4, 2, 128, 777, "f32", False, [777, 300]),
+    (3, 1, 32, 8, 128, 2049, "bf16", False, None),
+    (2, 1, 8, 8, 64, 5000, "bf16", False, [5000, 4097]),
+    (2, 1, 16, 2, 128, 3000, "bf16", False, [1, 2999]),
+    (2, 1, 6, 2, 64, 1500, "bf16", False, [1500, 17]),
+    (4, 1, 10, 2, 128, 1234, "bf16", False, "uniform:1:1234"),
+    (2, 4, 8, 2, 128, 2000, "bf16", True, [2000, 1003]),
+    (2, 2, 4, 4, 64, 333, "bf16", True, [333, 2]),
+    (3, 3, 2, 1, 128, 700, "f32", True, [700, 3, 1]),
+    (2, 4, 64, 8, 128, 4500, "bf16", True, [4500, 4096]),
+    (1, 4, 32, 8, 64, 999, "bf16", True, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}_ql{c[1]}_Hq{c[2]}_Hkv{c[3]}_D{c[4]}_L{c[5]}_{c[6]}{'_causal' if c[7] else ''}" for c in SMALL])
+def test_small_shapes(case):
+    B, q_len, Hq, Hkv, D, L, dt, causal, lens = case
+    w = inputs.make_decode("small", 100 + L, B=B, q_len=q_len, Hq=Hq, Hkv=Hkv, D=D, L_max=L,
+                           kv_lens=lens, dtype=dt, causal=causal, nan_pad=True)
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what=f"small {case}")
+
+
+@pytest.mark.parametrize("chunk_len", [64, 128, 512, 4096])
+def test_forced_chunk_lengths(chunk_len):
+    w = inputs.make_decode("chunks", 7, B=2, q_len=1, Hq=8, Hkv=2, D=128, L_max=3000,
+                           kv_lens=[3000, 1700], nan_pad=True)
+    O, lse = run_decode(w, chunk_len=chunk_len)
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what=f"chunk_len={chunk_len}")
+
+
+# ----------------------------------------------------------------------------
+# Degenerate cases
+# ----------------------------------------------------------------------------
+def test_empty_cache_and_empty_rows():
+    w = inputs.make_decode("empty", 3, B=3, q_len=2, Hq=4, Hkv=2, D=64, L_max=300,
+                           kv_lens=[0, 1, 300], causal=True, nan_pad=True)
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    assert np.isneginf(lr[0]).all() and np.isneginf(lr[1, 0]).all()  # rows that see nothing
+    check_rows(O, lse, Or, lr, what="empty rows")
+
+
+def test_zero_length_cache():
+    q = torch.randn(2, 1, 4, 128, device="cuda").to(torch.bfloat16)
+    k = torch.empty(2, 2, 0, 128, device="cuda", dtype=torch.bfloat16)
+    O, lse = binding.decode(q, k, k)
+    torch.cuda.synchronize()
+    assert torch.isneginf(lse).all() and (O == 0).all()
+    lse_e = binding.decode_energy(q, k)
+    torch.cuda.synchronize()
+    assert torch.isneginf(lse_e).all()
+
+
+def test_single_key_returns_its_value_row():
+    w = inputs.make_decode("one", 5, B=1, q_len=1, Hq=4, Hkv=1, D=128, L_max=1)
+    O, lse = run_decode(w)
+    v = w.values("v")[0, 0, 0]
+    assert np.abs(O[0, 0] - v[None, :]).max() <= 1e-6
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what="single key")
+
+
+def test_identical_keys_give_mean_of_v():
+    w = inputs.make_decode("same", 6, B=1, q_len=1, Hq=2, Hkv=1, D=64, L_max=1000)
+    w.k[0, 0, :] = w.k[0, 0, 0]
+    O, lse = run_decode(w)
+    mean_v = w.values("v")[0, 0].astype(np.float64).mean(axis=0)
+    assert np.abs(O[0, 0] - mean_v[None]).max() <= 2e-3
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what="identical keys")
+
+
+def test_huge_logits_are_stable():
+    w = inputs.make_decode("huge", 8, B=1, q_len=1, Hq=4, Hkv=1, D=128, L_max=4000, dtype="f32")
+    w.q *= np.float32(40.0)  # logits of several hundred
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    assert np.abs(lr).max() > 200
+    check_rows(O, lse, Or, lr, what="huge logits")
+
+
+# ----------------------------------------------------------------------------
+# Properties of the path
+# ----------------------------------------------------------------------------
+def test_energy_lse_matches_decode_lse():
+    w = inputs.make_decode("energy", 9, B=2, q_len=2, Hq=16, Hkv=4, D=128, L_max=5000,
+                           kv_lens=[5000, 2222], causal=True, nan_pad=True)
+    q, k, v, lens = workload_tensors(w)
+    O, lse = binding.decode(q, k, v, lens, causal=True)
+    lse_e = binding.decode_energy(q, k, lens, causal=True)
+    torch.cuda.synchronize()
+    _, lr = oracle.attend(w.q, w.k, None, w.kv_lens, w.scale, True)
+    check_rows(None, lse_e.cpu().numpy(), None, lr, what="energy-only lse")
+    assert torch.equal(lse_e, lse), "energy-only lse differs from attn_decode's lse"
+
+
+def test_two_runs_bitwise_identical():
+    w = inputs.make_decode("det", 10, B=2, q_len=1, Hq=32, Hkv=8, D=128, L_max=20000)
+    q, k, v, lens = workload_tensors(w)
+    O1, l1 = binding.decode(q, k, v, lens)
+    O2, l2 = binding.decode(q, k, v, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
+
+
+def test_chunking_does_not_change_the_result_beyond_rounding():
+    w = inputs.make_decode("assoc", 11, B=1, q_len=1, Hq=8, Hkv=2, D=128, L_max=8192)
+    a = run_decode(w, chunk_len=64)
+    b = run_decode(w, chunk_len=8192)
+    assert np.abs(a[0] - b[0]).max() < 1e-4 and np.abs(a[1] - b[1]).max() < 1e-5
+
+
+# ----------------------------------------------------------------------------
+# Full-size long-context and ragged workloads (sampled rows)
+# ----------------------------------------------------------------------------
+def _needle_rows(w, extra_heads=(5, 18, 27)):
+    rows = [(0, 0, w.G * kvh) for (_, kvh, _) in w.notes["needles"]]
+    return rows + [(0, 0, h) for h in extra_heads]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_long_context_1m_needle():
+    w = inputs.long_context_gqa(L=1 << 20, seed=31)
+    say("generated 1M-token cache")
+    O, lse = run_decode(w)
+    rows = _needle_rows(w)
+    Or, lr = oracle_decode(w, rows=rows)
+    check_rows(O, lse, Or, lr, rows=rows, what="long_context_gqa L=1,048,576")
+    for (_, kvh, n) in w.notes["needles"]:
+        assert 29.0 < lse[0, 0, w.G * kvh] < 31.0
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_long_context_5m_needle():
+    w = inputs.long_context_gqa(L=5_120_000, seed=3)
+    say("generated 5.12M-token cache")
+    q, k, v, lens = workload_tensors(w)
+    O, lse = binding.decode(q, k, v, lens)
+    torch.cuda.synchronize()
+    O, lse = O.cpu().numpy(), lse.cpu().numpy()
+    del q, k, v
+    torch.cuda.empty_cache()
+    # three KV-head groups (the oracle streams 5.12M tokens per group)
+    rows = [r for r in _needle_rows(w, extra_heads=(1, 29)) if r[2] // w.G in (0, 3, 7)]
+    Or, lr = oracle_decode(w, rows=rows)
+    check_rows(O, lse, Or, lr, rows=rows, what="long_context_gqa L=5,120,000")
+    # the needle dominates: O is its V row up to the weight left to the others
+    for (_, kvh, n) in w.notes["needles"]:
+        h = w.G * kvh
+        assert 29.0 < lse[0, 0, h] < 31.0
+        vn = w.values("v")[0, kvh, n]
+        assert np.abs(O[0, 0, h] - vn).max() < 0.05
+    lit = inputs.long_context_gqa(L=200_000, seed=3, literal_c=6.0)
+    O2, l2 = run_decode(lit)
+    rows2 = _needle_rows(lit)
+    Or2, lr2 = oracle_decode(lit, rows=rows2)
+    check_rows(O2, l2, Or2, lr2, rows=rows2, what="needle with the literal constant 6")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_llama31_70b_ragged_full_size():
+    w = inputs.llama31_70b_ragged(seed=5)
+    say(f"lengths {w.kv_lens.tolist()}")
+    O, lse = run_decode(w)
+    rng = np.random.default_rng(0)
+    rows = []
+    for b in rng.choice(w.B, size=6, replace=False):
+        kvh = int(rng.integers(0, w.Hkv))
+        rows += [(int(b), i, h) for i in range(w.q_len) for h in range(kvh * w.G, (kvh + 1) * w.G)]
+    Or, lr = oracle_decode(w, rows=rows)
+    check_rows(O, lse, Or, lr, rows=rows, what="llama31_70b_ragged (sampled groups)")
+
+
+def test_llama31_70b_ragged_small():
+    w = inputs.llama31_70b_ragged(seed=5, L_max=6000, L_lo=100, B=5)
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what="ragged 70B-shaped, small lengths")
+
+
+# ----------------------------------------------------------------------------
+# Bifurcated shared-prefix batch
+# ----------------------------------------------------------------------------
+def run_bifurcated(w):
+    O, lse = binding.decode_bifurcated(dev(w.q), dev(w.kp), dev(w.vp), dev(w.ks), dev(w.vs),
+                                       scale=w.scale)
+    torch.cuda.synchronize()
+    return O.cpu().numpy(), lse.cpu().numpy()
+
+
+def test_bifurcated_small():
+    w = inputs.bifurcated_prefix(seed=41, S=5, Lp=1000, Ls=77)
+    O, lse = run_bifurcated(w)
+    Or, lr = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale)
+    check_rows(O[:, None], lse[:, None], Or[:, None], lr[:, None], what="bifurcated small")
+
+
+def test_bifurcated_degenerate_parts():
+    for Lp, Ls in ((0, 50), (300, 0), (0, 0), (1, 1)):
+        w = inputs.bifurcated_prefix(seed=42, S=3, Hq=8, Hkv=2, D=64, Lp=Lp, Ls=Ls)
+        O, lse = run_bifurcated(w)
+        Or, lr = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale)
+        check_rows(O[:, None], lse[:, None], Or[:, None], lr[:, None], what=f"bifurcated Lp={Lp} Ls={Ls}")
+
+
+def test_bifurcated_full_size():
+    w = inputs.bifurcated_prefix(seed=4)
+    O, lse = run_bifurcated(w)
+    Or, lr = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale)
+    check_rows(O[:, None], lse[:, None], Or[:, None], lr[:, None], what="bifurcated_prefix full")
