@@ -34,7 +34,7 @@ def workload_tensors(w):
 
 def check_rows(O, lse, O_ref, lse_ref, rows=None, what=""):
     """Compare GPU outputs to the oracle on all rows (or the listed (b,i,h) rows)."""
-    O = np.asarray(O, dtype=np.float64)
+    O = None if O is None else np.asarray(O, dtype=np.float64)
     lse = np.asarray(lse, dtype=np.float64)
     if rows is None:
         sel = np.ones(lse.shape, dtype=bool)

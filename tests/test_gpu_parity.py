@@ -136,7 +136,7 @@ def test_huge_logits_are_stable():
     w.q *= np.float32(40.0)  # logits of several hundred
     O, lse = run_decode(w)
     Or, lr = oracle_decode(w)
-    assert np.abs(lr).max() > 200
+    assert np.abs(lr).max() > 100  # logits ~ N(0, 40^2): the max over 4000 keys is ~140
     check_rows(O, lse, Or, lr, what="huge logits")
 
 
