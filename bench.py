@@ -33,13 +33,75 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--min-warmup-s", type=float, default=0.5,
+                    help="keep warming up until this much wall time has passed (clock ramp)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="long_context_1m")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="KV heads of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the HBM read-stream reference measurement")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("long_context_exact_split_amd/csrc/split_kv_valu.hip",
+                  "long_context_exact_split_amd/csrc/device_common.h",
+                  "long_context_exact_split_amd/csrc/kernels.h")
+COUNTERS = "profiles/split_kv_valu_long_context_1m.counters.txt"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by its copy-kernel
+    calibration factor), or None when the kernel sources changed since."""
+    path = os.path.join(ROOT, COUNTERS)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def read_ceiling(torch):
+    """Best HBM read bandwidth of the reference stream kernel (non-temporal
+    16-byte loads, one 256-thread block per CU) over a 4 GiB buffer."""
+    import ctypes
+    from long_context_exact_split_amd import hbm_probe
+    lib = hbm_probe.load()
+    n = 4 << 30
+    src = torch.empty(n // 4, dtype=torch.int32, device="cuda").random_()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(cus, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    best = 0.0
+    for rep in range(13):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        lib.hbm_read_probe(ctypes.c_void_p(src.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                           cus, 1, ctypes.c_void_p(s.cuda_stream))
+        b.record(s)
+        torch.cuda.synchronize()
+        if rep >= 3:
+            best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src
+    return best
 
 
 def cpu_baseline(w, heads, O_gpu, lse_gpu):
@@ -93,9 +155,16 @@ def main():
     q, k, v = dev(w.q), dev(w.k), dev(w.v)
     ph = binding.Phases(q, k, v, scale=w.scale)
     print(f"# plan {ph.plan}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    # Untimed warm-up: at least --warmup steps and --min-warmup-s seconds.  From
+    # idle the GPU needs ~30-40 back-to-back steps (~25 ms) to reach its
+    # steady clocks; the timed region measures the steady state.
+    warm, t_w = 0, time.perf_counter()
+    while warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         ph.partials()
         ph.merge()
+        warm += 1
+        if warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -129,6 +198,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": warm,
         "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -143,12 +213,17 @@ def main():
         "hbm_gbps": path_gbps,
         "hbm_frac_of_peak": path_gbps / PEAK_GBPS,
         "split_kernel_ms": split_avg,
+        "split_kernel_ms_median": statistics.median(split_ms),
         "merge_kernel_ms": statistics.mean(merge_ms),
         "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": split_gbps / PEAK_GBPS, "traffic": None,
-                     "kernel": "split_kv_valu<bf16,128,4>",
+                     "frac": split_gbps / PEAK_GBPS, "traffic": counter_traffic(),
+                     "kernel": "split_kv_valu<bf16,128,rows=4>",
                      "algorithmic_bytes_per_launch": kv_bytes + q_bytes},
     }
+    if not args.no_ceiling:
+        ceil = read_ceiling(torch)
+        result["hbm_read_ceiling_gbps"] = ceil
+        result["roofline"]["frac_of_read_ceiling"] = split_gbps / ceil
     if not args.no_cpu_baseline:
         O = ph.out.cpu().numpy()
         lse = ph.lse.cpu().numpy()

@@ -17,6 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libattn_decode.so"
+PROBE_NAME = "libhbm_probe.so"  # HBM read-stream / copy reference kernels
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -24,6 +25,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
 # Packed fp32 VALU ops are kept out of the generated code.
 HIP_ONLY = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 DEFINES = ["-DATTN_HAVE_MFMA=" + os.environ.get("ATTN_HAVE_MFMA", "0")]
+# Optional kernel tuning parameters (e.g. "-DATTN_SPLIT_KT_SMALL=16"); the
+# defaults in the sources are the measured choices.
+DEFINES += os.environ.get("ATTN_BUILD_DEFINES", "").split()
 
 
 def hipcc() -> str:
@@ -50,13 +54,8 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    out = os.path.join(PKG, LIB_NAME)
+def _link(objs, name, verbose, out_dir=PKG):
+    out = os.path.join(out_dir, name)
     tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     if verbose:
@@ -66,6 +65,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
     return out
+
+
+def build(verbose: bool = False, out_dir: str = PKG, build_dir: str = BUILD) -> str:
+    """Compile every source and link the library; returns its path."""
+    global BUILD
+    BUILD = build_dir
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    probe = os.path.join(CSRC, "probe", "hbm_probe.hip")
+    with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + [probe]))
+    _link(objs[-1:], PROBE_NAME, verbose, out_dir)
+    return _link(objs[:-1], LIB_NAME, verbose, out_dir)
 
 
 if __name__ == "__main__":

@@ -29,9 +29,10 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
-int items_per_cu() {
-  static const int v = env_int("ATTN_DECODE_ITEMS_PER_CU", kDefaultItemsPerCu, 1, 1024);
-  return v;
+int items_per_cu(bool ragged) {
+  static const int forced = env_int("ATTN_DECODE_ITEMS_PER_CU", 0, 1, 1024);
+  if (forced > 0) return forced;
+  return ragged ? kRaggedItemsPerCu : kDenseItemsPerCu;
 }
 
 attn_status_t validate_desc(const attn_desc_t *d) {
@@ -77,7 +78,7 @@ attn_status_t make_plan(const attn_desc_t *d, int cu_count, bool mfma_available,
     C = d->chunk_len;
   } else {
     const int64_t work = groups * p->row_blocks * L;
-    const int64_t target = (int64_t)cu_count * items_per_cu();
+    const int64_t target = (int64_t)cu_count * items_per_cu(d->kv_lens != nullptr);
     C = round_up((work + target - 1) / (target > 0 ? target : 1), kChunkGrain);
     if (C < kChunkGrain) C = kChunkGrain;
     const int64_t whole = round_up(L > 0 ? L : 1, kChunkGrain);

@@ -27,9 +27,30 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef ATTN_SPLIT_WAVES
+#define ATTN_SPLIT_WAVES 4   // waves per workgroup
+#endif
+#ifndef ATTN_SPLIT_KT_SMALL
+#define ATTN_SPLIT_KT_SMALL 4  // keys per lane group per tile, blocks of <= 4 rows
+#endif
+#ifndef ATTN_SPLIT_KT_LARGE
+#define ATTN_SPLIT_KT_LARGE 4  // keys per lane group per tile, blocks of 8 rows
+#endif
+#ifndef ATTN_SPLIT_NT
+#define ATTN_SPLIT_NT 1      // K/V loads marked non-temporal: read once, kept out of the caches
+#endif
+
+constexpr int kWaves = ATTN_SPLIT_WAVES;
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLazyRescale = 8.0f;  // log2 units: rescale only past a 256x growth
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load16(const void *p) {
+  const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+  const u32x4 v = ATTN_SPLIT_NT ? __builtin_nontemporal_load(q) : *q;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <typename T, int D>
 struct Geometry {
@@ -137,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
     for (int j = 0; j < KT; ++j) {
       int t = c0 + tile * TK + j * KPW + kr;
       t = t < hi ? t : hi - 1;  // clamp: masked keys read a valid row
-      kd[j] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)t * D);
-      if constexpr (!ENERGY) vd[j] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)t * D);
+      kd[j] = load16(kbase + (int64_t)t * D);
+      if constexpr (!ENERGY) vd[j] = load16(vbase + (int64_t)t * D);
     }
   };
 
@@ -268,14 +289,22 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   }
 }
 
-// One wave per output row: merge the row's records (log-depth max over the
-// records with DPP, then one rescale of each record), normalise, write O, lse.
+// One workgroup per output row.  The row's records are read in parallel:
+// 16 bytes of o per lane, kMergeThreads / (D/4) records per pass, so a row of
+// ~100 records takes a handful of passes instead of a serial walk.  The max
+// over the records is a block-wide reduction (DPP within waves, LDS across
+// them); each record is then rescaled once and the partial sums of the
+// record groups are added through LDS in a fixed order (deterministic).
+constexpr int kMergeThreads = 256;
+
 template <int D, bool ENERGY>
-__global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
-  constexpr int EPM = D / kWave;  // output elements per lane
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  if (row >= (int64_t)a.B * a.Hkv * a.R) return;
+__global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
+  constexpr int LPR = D / 4;                 // lanes per record (float4 each)
+  constexpr int NG = kMergeThreads / LPR;    // records in flight per pass
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t row = blockIdx.x;
   const int r = (int)(row % a.R);
   const int group = (int)(row / a.R);
   const int b = group / a.Hkv;
@@ -286,56 +315,70 @@ __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
   int P = (int)((Lb + a.chunk_len - 1) / a.chunk_len);
   P = min(P, a.part.chunks);
   const int S = a.shared.m ? a.shared.chunks : 0;
-
   const int64_t pstride = a.part.rows;
   const int64_t prow = (int64_t)group * a.part.chunks * pstride + r;
   const int64_t sstride = a.shared.rows;
   const int64_t srow = a.shared.m ? (int64_t)kvh * a.shared.chunks * sstride + (int64_t)b * a.R + r : 0;
+  auto rec_of = [&](int c) { return c < P ? prow + c * pstride : srow + (c - P) * sstride; };
+  auto m_of = [&](int c) { return c < P ? a.part.m[prow + c * pstride] : a.shared.m[srow + (c - P) * sstride]; };
 
+  __shared__ float red[kMergeThreads / kWave];
   float M = -INFINITY;
-  for (int c = lane; c < P + S; c += kWave)
-    M = fmaxf(M, c < P ? a.part.m[prow + c * pstride] : a.shared.m[srow + (c - P) * sstride]);
+  for (int c = tid; c < P + S; c += kMergeThreads) M = fmaxf(M, m_of(c));
   M = wave_max(M);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / kWave; ++w) M = fmaxf(M, red[w]);
 
-  float lsum = 0.0f, acc[EPM];
-#pragma unroll
-  for (int e = 0; e < EPM; ++e) acc[e] = 0.0f;
-#pragma unroll 4
-  for (int c = 0; c < P; ++c) {
-    const int64_t rec = prow + c * pstride;
-    const float f = rescale_factor(a.part.m[rec], M);
-    lsum += f * a.part.l[rec];
+  const int cg = tid / LPR;   // record group
+  const int dl = tid % LPR;   // float4 slot within the record
+  float lsum = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = cg; c < P + S; c += NG) {
+    const bool shared = c >= P;
+    const int64_t rec = rec_of(c);
+    const float f = rescale_factor(shared ? a.shared.m[rec] : a.part.m[rec], M);
+    lsum += f * (shared ? a.shared.l[rec] : a.part.l[rec]);
     if constexpr (!ENERGY) {
-#pragma unroll
-      for (int e = 0; e < EPM; ++e) acc[e] += f * a.part.o[rec * D + lane * EPM + e];
+      const float *op = (shared ? a.shared.o : a.part.o) + rec * D + dl * 4;
+      const float4 v = *reinterpret_cast<const float4 *>(op);
+      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
     }
   }
-#pragma unroll 4
-  for (int c = 0; c < S; ++c) {
-    const int64_t rec = srow + c * sstride;
-    const float f = rescale_factor(a.shared.m[rec], M);
-    lsum += f * a.shared.l[rec];
-    if constexpr (!ENERGY) {
-#pragma unroll
-      for (int e = 0; e < EPM; ++e) acc[e] += f * a.shared.o[rec * D + lane * EPM + e];
-    }
-  }
+  __shared__ float sl[NG];
+  __shared__ float4 so[ENERGY ? 1 : NG][ENERGY ? 1 : LPR];
+  if (dl == 0) sl[cg] = lsum;
+  if constexpr (!ENERGY) so[cg][dl] = acc;
+  __syncthreads();
 
   const int i = r / a.G;
   const int h = kvh * a.G + (r - i * a.G);
   const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
-  const bool empty = M == -INFINITY || !(lsum > 0.0f);
-  if (lane == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(lsum)) * kLn2;
-  if constexpr (!ENERGY) {
-    const float inv = empty ? 0.0f : 1.0f / lsum;
+  float ltot = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPM; ++e) a.o[orow * D + lane * EPM + e] = acc[e] * inv;
+  for (int g = 0; g < NG; ++g) ltot += sl[g];
+  const bool empty = M == -INFINITY || !(ltot > 0.0f);
+  if (tid == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(ltot)) * kLn2;
+  if constexpr (!ENERGY) {
+    if (tid < LPR) {
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float4 v = so[g][tid];
+        t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+      }
+      const float inv = empty ? 0.0f : 1.0f / ltot;
+      float *dst = a.o + orow * D + tid * 4;  // O is only 4-byte aligned
+      dst[0] = t.x * inv; dst[1] = t.y * inv; dst[2] = t.z * inv; dst[3] = t.w * inv;
+    }
   }
 }
 
 template <typename T, int D, int RB, bool ENERGY>
 hipError_t launch_t(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
-  constexpr int KT = RB <= 4 ? 8 : 4;
+  constexpr int KT = RB <= 4 ? ATTN_SPLIT_KT_SMALL : ATTN_SPLIT_KT_LARGE;
   if (plan.work_items <= 0) return hipSuccess;
   hipLaunchKernelGGL((split_kv_valu<T, D, RB, KT, ENERGY>), dim3((unsigned)plan.work_items),
                      dim3(kThreads), 0, stream, a);
@@ -374,14 +417,14 @@ hipError_t launch_split_valu(const attn_plan_t &plan, const SplitArgs &a, attn_d
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hkv * a.R;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const dim3 grid((unsigned)rows), block(kMergeThreads);
   const bool energy = a.o == nullptr;
   if (head_dim == 64) {
-    if (energy) hipLaunchKernelGGL((merge_partials<64, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((merge_partials<64, false>), grid, dim3(256), 0, stream, a);
+    if (energy) hipLaunchKernelGGL((merge_partials<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((merge_partials<64, false>), grid, block, 0, stream, a);
   } else {
-    if (energy) hipLaunchKernelGGL((merge_partials<128, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((merge_partials<128, false>), grid, dim3(256), 0, stream, a);
+    if (energy) hipLaunchKernelGGL((merge_partials<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((merge_partials<128, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

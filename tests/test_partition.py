@@ -20,13 +20,21 @@ def test_forced_chunk_len_single_query_fp32():
     assert p["kernel"] == 0 and p["rows"] == 1 and p["rows_per_block"] == 1
 
 
-def test_gqa_decode_fills_the_gpu():
+def test_dense_decode_gives_one_item_per_cu():
+    # every sequence full: one contiguous chunk per CU
     p = plan(batch=8, max_kv_len=32768)
     assert p["rows"] == 4 and p["rows_per_block"] == 4 and p["row_blocks"] == 1
-    assert p["work_items"] >= 256 * 2
-    assert p["chunk_len"] % 256 == 0
+    assert p["work_items"] == 256 and p["chunk_len"] == 8192
     p = plan(max_kv_len=1 << 20)
-    assert p["work_items"] >= 512 and p["chunks_per_seq"] * p["chunk_len"] >= 1 << 20
+    assert p["work_items"] == 256 and p["chunk_len"] == 32768
+    p = plan(max_kv_len=5_120_000)
+    assert 256 >= p["work_items"] > 240 and p["chunks_per_seq"] * p["chunk_len"] >= 5_120_000
+
+
+def test_ragged_lengths_get_finer_chunks():
+    # lengths on the device: the host plans on max_kv_len with ~4 items per CU
+    p = plan(batch=16, num_q_heads=32, num_kv_heads=8, max_kv_len=131072, kv_lens_ptr=0x1000)
+    assert p["work_items"] >= 4 * 256 * 0.9
 
 
 def test_empty_and_tiny():
