@@ -1,15 +1,16 @@
 #!/usr/bin/env python3
-"""Benchmark: exact split-KV decode of a 1M-token GQA cache on one MI355X.
+"""Benchmark: exact split-KV attention decode on one MI355X.
 
-Workload (one step = one full decode call: split-KV kernel + merge kernel):
-  long-context GQA decode, B=1, 32 query heads / 8 KV heads, d=128,
-  L = 1,048,576 cached tokens, bf16 K/V/Q ~ N(0,1) with one planted needle
-  key per KV head (scaled logit ~30), fp32 accumulation, fp32 O and lse.
+Default workload (the headline): long-context GQA decode, B=1, 32 query heads
+/ 8 KV heads, d=128, L = 1,048,576 cached tokens, bf16 K/V/Q ~ N(0,1) with one
+planted needle key per KV head (scaled logit ~30), fp32 accumulation, fp32 O
+and lse.  One step = one full decode call (split-KV kernel + merge kernel).
+Other workload shapes are selectable with --workload.
 
-Prints one JSON line: KV tokens/s (value), whole-path and split-kernel HBM
-GB/s against the 8 TB/s peak, the roofline record of the split kernel (its
-per-launch time from HIP events recorded on the stream it runs on), and the
-fp64 CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: KV tokens/s (value), whole-path HBM GB/s against the
+8 TB/s peak, the roofline record of the dominant kernel (its per-launch time
+from HIP events recorded on the stream it runs on), and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -24,10 +25,19 @@ if ROOT not in sys.path:
 
 METRIC = "KV tokens/s and achieved HBM GB/s (% of peak), 1M-token GQA decode"
 PEAK_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 WORKLOADS = {
-    "long_context_1m": dict(L=1 << 20, seed=31),
-    "long_context_5m": dict(L=5_120_000, seed=3),
+    "long_context_1m": "long-context GQA decode (1M tokens)",
+    "long_context_5m": "long-context GQA decode (5.12M tokens)",
+    "llama3_8b_gqa": "Llama-3-8B-shaped GQA decode (B=8, L=32768)",
+    "llama31_70b_ragged": "Llama-3.1-70B-shaped ragged decode (B=16, 4 causal query tokens)",
+    "single_query_fp32": "single-query fp32 decode (L=4096, 8 chunks)",
+    "bifurcated_prefix": "bifurcated shared-prefix sampling (64 samples, 16384 + 512 tokens)",
 }
+KERNEL_SOURCES = ("long_context_exact_split_amd/csrc/split_kv_valu.hip",
+                  "long_context_exact_split_amd/csrc/device_common.h",
+                  "long_context_exact_split_amd/csrc/kernels.h")
+COUNTERS = "profiles/split_kv_valu_long_context_1m.counters.txt"
 
 
 def parse():
@@ -38,20 +48,17 @@ def parse():
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this much wall time has passed (clock ramp)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="long_context_1m")
-    ap.add_argument("--cpu-heads", type=int, default=8,
-                    help="KV heads of the workload the CPU oracle baseline runs on")
+    ap.add_argument("--cpu-rows", type=int, default=32,
+                    help="query rows of the workload the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the HBM read-stream reference measurement")
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("long_context_exact_split_amd/csrc/split_kv_valu.hip",
-                  "long_context_exact_split_amd/csrc/device_common.h",
-                  "long_context_exact_split_amd/csrc/kernels.h")
-COUNTERS = "profiles/split_kv_valu_long_context_1m.counters.txt"
-
-
+# ----------------------------------------------------------------------------
+# Reference figures
+# ----------------------------------------------------------------------------
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -61,12 +68,13 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def counter_traffic():
+def counter_traffic(workload):
     """HBM bytes per split-kernel launch from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by its copy-kernel
-    calibration factor), or None when the kernel sources changed since."""
+    calibration factor), or None when the kernel sources changed since or the
+    summary covers another workload."""
     path = os.path.join(ROOT, COUNTERS)
-    if not os.path.exists(path):
+    if workload != "long_context_1m" or not os.path.exists(path):
         return None
     kv = {}
     with open(path) as fh:
@@ -104,28 +112,154 @@ def read_ceiling(torch):
     return best
 
 
-def cpu_baseline(w, heads, O_gpu, lse_gpu):
-    """Time the fp64 oracle on `heads` KV heads (all their query heads, all L
-    tokens) and check the GPU rows it produced."""
-    import numpy as np
-    import oracle
+def cpu_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = 1
-    rows = [(0, 0, h) for kvh in range(heads) for h in range(kvh * w.G, (kvh + 1) * w.G)]
+        return 1
+
+
+# ----------------------------------------------------------------------------
+# Workloads
+# ----------------------------------------------------------------------------
+def make_workload(name):
+    from long_context_exact_split_amd import inputs
+    if name == "long_context_1m":
+        return inputs.long_context_gqa(L=1 << 20, seed=31)
+    if name == "long_context_5m":
+        return inputs.long_context_gqa(L=5_120_000, seed=3)
+    if name == "llama3_8b_gqa":
+        return inputs.llama3_8b_gqa(seed=2)
+    if name == "llama31_70b_ragged":
+        return inputs.llama31_70b_ragged(seed=5)
+    if name == "single_query_fp32":
+        return inputs.single_query_fp32(seed=1)
+    if name == "bifurcated_prefix":
+        return inputs.bifurcated_prefix(seed=4)
+    raise ValueError(name)
+
+
+def dev(torch, a):
+    import numpy as np
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class DecodeRunner:
+    """One decode call split into its two launches (split kernel, merge)."""
+
+    def __init__(self, torch, w):
+        import numpy as np
+        from long_context_exact_split_amd import binding
+        self.w = w
+        q, k, v = dev(torch, w.q), dev(torch, w.k), dev(torch, w.v)
+        lens = None
+        if not (w.kv_lens == w.L_max).all():
+            lens = torch.from_numpy(w.kv_lens.astype(np.int32)).cuda()
+        self.ph = binding.Phases(q, k, v, lens, scale=w.scale, causal=w.causal,
+                                 chunk_len=w.chunk_len)
+        self.plan = self.ph.plan
+        esz = 2 if w.dtype == "bf16" else 4
+        self.kv_tokens = int(w.kv_lens.sum())
+        self.kv_bytes = 2 * self.kv_tokens * w.Hkv * w.D * esz
+        self.q_bytes = w.B * w.q_len * w.Hq * w.D * esz
+        self.out_bytes = w.B * w.q_len * w.Hq * (w.D + 1) * 4
+        rows = w.G * w.q_len
+        self.flops = 4 * rows * w.D * self.kv_tokens * w.Hkv
+        self.kernel = ("split_kv_mfma" if self.plan["kernel"] == 1 else "split_kv_valu") + \
+            f"<{w.dtype},{w.D},rows={self.plan['rows_per_block']}>"
+
+    def first(self):
+        self.ph.partials()
+
+    def second(self):
+        self.ph.merge()
+
+    def outputs(self):
+        return self.ph.out.cpu().numpy(), self.ph.lse.cpu().numpy()
+
+    def oracle_rows(self, n_rows):
+        w = self.w
+        rows = [(b, i, h) for b in range(w.B) for i in range(w.q_len) for h in range(w.Hq)]
+        step = max(1, len(rows) // n_rows)
+        return rows[::step][:n_rows]
+
+    def oracle(self, rows):
+        import oracle
+        w = self.w
+        return oracle.attend(w.q, w.k, w.v, w.kv_lens, w.scale, w.causal, rows=rows)
+
+
+class BifurcatedRunner:
+    """The shared-prefix call, timed as one unit (three launches)."""
+
+    def __init__(self, torch, w):
+        import ctypes
+        from long_context_exact_split_amd import binding
+        self.w, self.binding = w, binding
+        self.t = [dev(torch, x) for x in (w.q, w.kp, w.vp, w.ks, w.vs)]
+        self.out = torch.empty((w.S, w.Hq, w.D), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((w.S, w.Hq), dtype=torch.float32, device="cuda")
+        d = binding.bifurcated_desc(self.t[0], self.t[1], self.t[3], w.scale)
+        n = ctypes.c_size_t(0)
+        st = binding.load_library().attn_bifurcated_workspace_bytes(ctypes.byref(d),
+                                                                      ctypes.byref(n))
+        assert st == 0, st
+        self.ws = torch.empty(max(1, n.value), dtype=torch.uint8, device="cuda")
+        self.plan = {"prefix_rows": w.S * w.G, "workspace_bytes": n.value}
+        self.kv_tokens = w.S * (w.Lp + w.Ls)             # logical tokens attended
+        self.kv_bytes = 2 * (w.Lp + w.S * w.Ls) * w.Hkv * w.D * 2   # physical bytes read
+        self.q_bytes = w.S * w.Hq * w.D * 2
+        self.out_bytes = w.S * w.Hq * (w.D + 1) * 4
+        self.flops = 4 * w.S * w.Hq * w.D * (w.Lp + w.Ls)
+        self.kernel = "bifurcated (prefix split kernel + suffix split kernel + merge)"
+
+    def first(self):
+        q, kp, vp, ks, vs = self.t
+        self.binding.decode_bifurcated(q, kp, vp, ks, vs, scale=self.w.scale, out=self.out,
+                                       lse=self.lse, workspace=self.ws)
+
+    def second(self):
+        pass
+
+    def outputs(self):
+        return self.out.cpu().numpy()[:, None], self.lse.cpu().numpy()[:, None]
+
+    def oracle_rows(self, n_rows):
+        w = self.w
+        rows = [(s, 0, h) for s in range(w.S) for h in range(w.Hq)]
+        step = max(1, len(rows) // n_rows)
+        return rows[::step][:n_rows]
+
+    def oracle(self, rows):
+        import oracle
+        w = self.w
+        samples = sorted({s for (s, _, _) in rows})
+        O, lse = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale, samples=samples)
+        return O[:, None], lse[:, None]
+
+
+def cpu_baseline(run, n_rows, O_gpu, lse_gpu):
+    """Time the fp64 oracle on a sample of the workload's query rows (each row
+    over its full visible cache) and check the GPU's values on those rows."""
+    import numpy as np
+    rows = run.oracle_rows(n_rows)
     t0 = time.perf_counter()
-    Or, lr = oracle.attend(w.q, w.k, w.v, w.kv_lens, w.scale, False, rows=rows)
+    Or, lr = run.oracle(rows)
     dt = time.perf_counter() - t0
     idx = tuple(np.array(rows).T)
     dO = float(np.abs(O_gpu[idx] - Or[idx]).max())
-    dl = float((np.abs(lse_gpu[idx] - lr[idx]) / np.maximum(1.0, np.abs(lr[idx]))).max())
-    kv_tok = w.L_max * heads / w.Hkv
-    return {"value": kv_tok / dt, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} of {w.Hkv} KV heads ({heads * w.G} query heads) over all "
-                      f"{w.L_max} tokens; rate scaled to whole-cache KV tokens "
-                      f"(= L * {heads}/{w.Hkv} per {dt:.2f} s)",
+    fin = np.isfinite(lr[idx])
+    dl = float((np.abs(lse_gpu[idx][fin] - lr[idx][fin]) /
+                np.maximum(1.0, np.abs(lr[idx][fin]))).max()) if fin.any() else 0.0
+    total_rows = O_gpu.shape[0] * O_gpu.shape[1] * O_gpu.shape[2]
+    frac = len(rows) / total_rows
+    return {"value": run.kv_tokens * frac / dt, "unit": "KV tokens/s", "cores": int(cpu_threads()),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {total_rows} query rows, each over its whole visible cache "
+                      f"({dt:.2f} s); rate = KV tokens of the call x {len(rows)}/{total_rows} / time",
             "seconds": dt, "parity_max_abs_dO": dO, "parity_max_rel_dlse": dl}
 
 
@@ -135,33 +269,26 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                                    "(the multi-GPU sharding is described in DESIGN.md, not built)"}))
         sys.exit(2)
-    import numpy as np
     import torch
-    from long_context_exact_split_amd import binding, inputs
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
-    cfg = WORKLOADS[args.workload]
     t_gen = time.perf_counter()
-    w = inputs.long_context_gqa(L=cfg["L"], seed=cfg["seed"])
+    w = make_workload(args.workload)
     print(f"# generated {args.workload} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
+    run = (BifurcatedRunner if args.workload == "bifurcated_prefix" else DecodeRunner)(torch, w)
+    print(f"# plan {run.plan}", file=sys.stderr, flush=True)
 
-    def dev(a):
-        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-
-    q, k, v = dev(w.q), dev(w.k), dev(w.v)
-    ph = binding.Phases(q, k, v, scale=w.scale)
-    print(f"# plan {ph.plan}", file=sys.stderr, flush=True)
     # Untimed warm-up: at least --warmup steps and --min-warmup-s seconds.  From
     # idle the GPU needs ~30-40 back-to-back steps (~25 ms) to reach its
     # steady clocks; the timed region measures the steady state.
     warm, t_w = 0, time.perf_counter()
     while warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
-        ph.partials()
-        ph.merge()
+        run.first()
+        run.second()
         warm += 1
         if warm % 16 == 0:
             torch.cuda.synchronize()
@@ -170,30 +297,27 @@ def main():
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
+    torch.cuda.synchronize()  # barrier (one rank)
     t0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
-        ph.partials()
+        run.first()
         ev[i][1].record(stream)
-        ph.merge()
+        run.second()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    merge_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    first_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    second_ms = [e[1].elapsed_time(e[2]) for e in ev]
 
-    L, Hkv, D, Hq = w.L_max, w.Hkv, w.D, w.Hq
-    kv_bytes = 2 * L * Hkv * D * 2
-    q_bytes = Hq * D * 2
-    out_bytes = Hq * D * 4 + Hq * 4
     step_ms = wall * 1e3 / K
-    split_avg = statistics.mean(split_ms)
-    split_gbps = (kv_bytes + q_bytes) / (split_avg * 1e-3) / 1e9
-    path_gbps = (kv_bytes + q_bytes + out_bytes) / (step_ms * 1e-3) / 1e9
+    first_avg = statistics.mean(first_ms)
+    alg = run.kv_bytes + run.q_bytes
+    dom_gbps = alg / (first_avg * 1e-3) / 1e9
+    path_gbps = (alg + run.out_bytes) / (step_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
-        "value": L / (step_ms * 1e-3),
+        "value": run.kv_tokens / (step_ms * 1e-3),
         "unit": "KV tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -203,32 +327,28 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": getattr(w, "dtype", "bf16"),
         "data": "synthetic",
-        "config": {"workload": "long-context GQA decode (1M tokens)" if L == 1 << 20
-                   else "long-context GQA decode (5.12M tokens)",
-                   "batch": 1, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "kv_len": L,
-                   "kv_dtype": "bf16", "accumulate": "fp32", "needle_logit": 30,
-                   "chunk_len": ph.plan["chunk_len"], "work_items": ph.plan["work_items"]},
+        "config": {"workload": WORKLOADS[args.workload], **run.plan},
         "hbm_gbps": path_gbps,
         "hbm_frac_of_peak": path_gbps / PEAK_GBPS,
-        "split_kernel_ms": split_avg,
-        "split_kernel_ms_median": statistics.median(split_ms),
-        "merge_kernel_ms": statistics.mean(merge_ms),
-        "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": split_gbps / PEAK_GBPS, "traffic": counter_traffic(),
-                     "kernel": "split_kv_valu<bf16,128,rows=4>",
-                     "algorithmic_bytes_per_launch": kv_bytes + q_bytes},
+        "dominant_kernel_ms": first_avg,
+        "dominant_kernel_ms_median": statistics.median(first_ms),
+        "second_launch_ms": statistics.mean(second_ms),
+        "tflops": run.flops / (first_avg * 1e-3) / 1e12,
+        "roofline": {"bound": "hbm", "achieved": dom_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": dom_gbps / PEAK_GBPS, "traffic": counter_traffic(args.workload),
+                     "kernel": run.kernel, "algorithmic_bytes_per_launch": alg},
     }
+    if args.workload == "bifurcated_prefix":
+        result["kv_tokens_physical"] = w.Lp + w.S * w.Ls
     if not args.no_ceiling:
         ceil = read_ceiling(torch)
         result["hbm_read_ceiling_gbps"] = ceil
-        result["roofline"]["frac_of_read_ceiling"] = split_gbps / ceil
+        result["roofline"]["frac_of_read_ceiling"] = dom_gbps / ceil
     if not args.no_cpu_baseline:
-        O = ph.out.cpu().numpy()
-        lse = ph.lse.cpu().numpy()
-        del q, k, v
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads, O, lse)
+        O, lse = run.outputs()
+        result["cpu_baseline"] = cpu_baseline(run, args.cpu_rows, O, lse)
     print(json.dumps(result), flush=True)
 
 

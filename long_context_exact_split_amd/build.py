@@ -24,10 +24,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
 # Packed fp32 VALU ops are kept out of the generated code.
 HIP_ONLY = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-DEFINES = ["-DATTN_HAVE_MFMA=" + os.environ.get("ATTN_HAVE_MFMA", "0")]
 # Optional kernel tuning parameters (e.g. "-DATTN_SPLIT_KT_SMALL=16"); the
 # defaults in the sources are the measured choices.
-DEFINES += os.environ.get("ATTN_BUILD_DEFINES", "").split()
+DEFINES = os.environ.get("ATTN_BUILD_DEFINES", "").split()
 
 
 def hipcc() -> str:

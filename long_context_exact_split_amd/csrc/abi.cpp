@@ -14,10 +14,7 @@ namespace {
 
 using namespace attn;
 
-#ifndef ATTN_HAVE_MFMA
-#define ATTN_HAVE_MFMA 0
-#endif
-constexpr bool kMfma = ATTN_HAVE_MFMA != 0;
+constexpr bool kMfma = true;  // dense query blocks go to the MFMA kernel
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 constexpr int kMaxDevices = 64;
@@ -197,12 +194,6 @@ attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans
 }
 
 }  // namespace
-
-#if !ATTN_HAVE_MFMA
-hipError_t attn::launch_split_mfma(const attn_plan_t &, const SplitArgs &, int, bool, hipStream_t) {
-  return hipErrorInvalidValue;
-}
-#endif
 
 extern "C" {
 

@@ -80,6 +80,36 @@ def test_small_shapes(case):
     check_rows(O, lse, Or, lr, what=f"small {case}")
 
 
+# Dense query blocks (R = G * q_len > 8, bf16) run on the MFMA kernel.
+MFMA = [
+    # B, q_len, Hq, Hkv, D, L, causal, lens
+    (2, 4, 64, 8, 128, 4500, True, [4500, 4096]),
+    (1, 2, 8, 1, 128, 3000, True, None),
+    (3, 3, 4, 1, 64, 777, True, [777, 3, 100]),
+    (2, 1, 16, 1, 128, 2049, False, [2049, 31]),
+    (1, 8, 64, 8, 128, 1500, True, None),        # R = 64: two row blocks
+    (2, 5, 14, 2, 64, 1100, True, [1100, 600]),   # R = 35: padded second block
+    (1, 4, 16, 2, 128, 40000, True, None),
+]
+
+
+@pytest.mark.parametrize("case", MFMA, ids=[f"B{c[0]}_ql{c[1]}_Hq{c[2]}_Hkv{c[3]}_D{c[4]}_L{c[5]}" for c in MFMA])
+def test_mfma_query_blocks(case):
+    B, q_len, Hq, Hkv, D, L, causal, lens = case
+    w = inputs.make_decode("mfma", 300 + L, B=B, q_len=q_len, Hq=Hq, Hkv=Hkv, D=D, L_max=L,
+                           kv_lens=lens, causal=causal, nan_pad=True)
+    desc = binding.make_desc(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                             max_kv_len=L, causal=causal)
+    assert binding.plan(desc)["kernel"] == 1
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what=f"mfma {case}")
+    q, k, v, lens_t = workload_tensors(w)
+    lse_e = binding.decode_energy(q, k, lens_t, causal=causal)
+    torch.cuda.synchronize()
+    check_rows(None, lse_e.cpu().numpy(), None, lr, what=f"mfma energy {case}")
+
+
 @pytest.mark.parametrize("chunk_len", [64, 128, 512, 4096])
 def test_forced_chunk_lengths(chunk_len):
     w = inputs.make_decode("chunks", 7, B=2, q_len=1, Hq=8, Hkv=2, D=128, L_max=3000,
