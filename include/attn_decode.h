@@ -91,18 +91,24 @@ typedef struct {
   attn_dtype_t dtype;
 } attn_desc_t;
 
-/* The partitioner's decision for a descriptor (introspection and tests). */
+/* The partitioner's decision for a descriptor (introspection and tests).
+ * Segments are the (sequence, KV head, row block) triples; each is one KV
+ * head's L_b cached tokens read for one block of query rows. */
 typedef struct {
-  int32_t kernel;            /* 0: VALU split-KV kernel, 1: MFMA query-block kernel   */
-  int32_t rows;              /* R = (Hq / Hkv) * q_len query rows per (b, KV head)     */
-  int32_t rows_per_block;    /* query rows one work item carries                       */
-  int32_t row_blocks;        /* ceil(R / rows_per_block)                               */
-  int32_t chunk_len;         /* C: tokens per chunk                                    */
-  int32_t chunks_per_seq;    /* ceil(max_kv_len / C)                                   */
-  int64_t work_items;        /* B * Hkv * row_blocks * chunks_per_seq workgroups       */
-  int32_t threads_per_item;  /* threads per workgroup                                  */
-  int32_t cu_count;          /* compute units the plan was sized for                   */
-  size_t workspace_bytes;    /* partial (m, l, o) records: one per (item, row)         */
+  int32_t kernel;            /* 0: VALU split-KV kernel, 1: MFMA query-block kernel (32    */
+                             /*    rows), 2: MFMA shared-tile kernel (64-256 rows)          */
+  int32_t rows;              /* R = (Hq / Hkv) * q_len query rows per (b, KV head)          */
+  int32_t rows_per_block;    /* query rows one segment carries                              */
+  int32_t row_blocks;        /* ceil(R / rows_per_block)                                    */
+  int32_t balanced;          /* 1: every workgroup streams an equal share of all segments'  */
+                             /*    tokens (lengths read on the device); 0: fixed chunks     */
+  int32_t chunk_len;         /* fixed: C; balanced: tokens per workgroup if all L_b = L_max */
+  int32_t chunks_per_seq;    /* fixed: ceil(max_kv_len / C); balanced: 0                    */
+  int32_t threads_per_item;  /* threads per workgroup                                       */
+  int64_t work_items;        /* workgroups launched                                         */
+  int64_t record_slots;      /* partial-record slots (each holds rows_per_block rows)       */
+  int32_t cu_count;          /* compute units the plan was sized for                        */
+  size_t workspace_bytes;    /* partial (m, l, o) records                                   */
 } attn_plan_t;
 
 /* Partition a decode call for `cu_count` compute units (<= 0: those of the
@@ -134,16 +140,20 @@ attn_status_t attn_decode(const attn_desc_t *desc, const void *q, const void *k,
  * Attention computes local energies per device and then reduces them; Star
  * Attention's query host aggregates the hosts' softmax statistics).
  *
- * attn_decode_partials: one (m, l, o) record per (b, KV head, chunk, row)
- * into `workspace` (sized by attn_workspace_bytes).  With v == NULL only
- * (m, l) are produced (energy only).  Record layout, for the plan P returned
- * by attn_decode_plan (groups = B * Hkv, Rp = P.row_blocks * P.rows_per_block,
- * C = P.chunk_len, n = P.chunks_per_seq, X = roundup(4*groups*n*Rp, 256) bytes):
- *   float m[groups][n][Rp] at byte 0       -- chunk max, in log2 units
- *   float l[groups][n][Rp] at byte X       -- sum of 2^(s*log2e - m)
- *   float o[groups][n][Rp][D] at byte 2X   -- unnormalised output
- * Row r of group (b, kvh) is query token r / G, head kvh*G + r % G; chunk c
- * covers tokens [c*C, (c+1)*C) and exists for c < ceil(kv_lens[b] / C).
+ * attn_decode_partials: (m, l, o) records for every piece of work into
+ * `workspace` (sized by attn_workspace_bytes).  With v == NULL only (m, l)
+ * are produced (energy only).  For the plan P of attn_decode_plan, with
+ * Nr = P.record_slots * P.rows_per_block and X = roundup(4 * Nr, 256) bytes:
+ *   float m[Nr] at byte 0        -- piece max of the scaled logits, log2 units
+ *   float l[Nr] at byte X        -- sum of 2^(s * log2e - m) over the piece
+ *   float o[Nr][D] at byte 2X    -- unnormalised output of the piece
+ * Record slot k holds rows k*rows_per_block .. +rows_per_block-1 of one piece.
+ * Fixed chunks: slot = segment * chunks_per_seq + c covers tokens
+ * [c*C, (c+1)*C) and exists for c < ceil(L_b / C).  Balanced: the segments
+ * (segment = (b*Hkv + kvh)*row_blocks + row block) are laid end to end into
+ * U = Hkv*row_blocks*sum(L_b) tokens; workgroup w covers [floor(wU/W),
+ * floor((w+1)U/W)) and its piece of segment s sits at slot w + s.
+ * Row r of a row block is query token r / G, head kvh*G + r % G.
  *
  * attn_decode_merge: merges each row's records (exact in any order), then
  * O = o / l and lse = (m + log2 l) * ln 2.  o == NULL gives lse only; o !=

@@ -47,8 +47,9 @@ class AttnDesc(ctypes.Structure):
 class AttnPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
-                ("chunk_len", ctypes.c_int32), ("chunks_per_seq", ctypes.c_int32),
-                ("work_items", ctypes.c_int64), ("threads_per_item", ctypes.c_int32),
+                ("balanced", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
+                ("chunks_per_seq", ctypes.c_int32), ("threads_per_item", ctypes.c_int32),
+                ("work_items", ctypes.c_int64), ("record_slots", ctypes.c_int64),
                 ("cu_count", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self):
@@ -99,6 +100,12 @@ def load_library():
             getattr(lib, name).restype = c.c_int
         lib.attn_status_string.argtypes = [c.c_int]
         lib.attn_status_string.restype = c.c_char_p
+        lib.attn_testing_pieces.argtypes = [P(AttnDesc), c.c_void_p, c.c_int32, c.c_int64,
+                                            c.c_void_p, c.c_int64]
+        lib.attn_testing_pieces.restype = c.c_int64
+        lib.attn_testing_segment_slots.argtypes = [P(AttnDesc), c.c_void_p, c.c_int32, c.c_int64,
+                                                   c.c_void_p]
+        lib.attn_testing_segment_slots.restype = c.c_int
         _lib = lib
         return lib
 
@@ -125,6 +132,34 @@ def plan(desc: AttnDesc, cu_count: int = 0) -> dict:
     p = AttnPlan()
     _check(lib.attn_decode_plan(ctypes.byref(desc), cu_count, ctypes.byref(p)), "attn_decode_plan")
     return p.as_dict()
+
+
+def testing_pieces(desc: AttnDesc, lens, cu_count: int, w: int):
+    """Host view of workgroup w's pieces: [(segment, t0, t1, slot), ...]."""
+    import numpy as np
+    lib = load_library()
+    arr = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32)
+    cap = 64
+    while True:
+        out = np.zeros(4 * cap, dtype=np.int64)
+        n = lib.attn_testing_pieces(ctypes.byref(desc), None if arr is None else arr.ctypes.data,
+                                    cu_count, w, out.ctypes.data, cap)
+        if n < 0:
+            raise AttnError(int(-n), "attn_testing_pieces")
+        if n <= cap:
+            return [tuple(int(x) for x in out[4 * i:4 * i + 4]) for i in range(n)]
+        cap = int(n)
+
+
+def testing_segment_slots(desc: AttnDesc, lens, cu_count: int, segment: int):
+    import numpy as np
+    lib = load_library()
+    arr = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32)
+    out = np.zeros(3, dtype=np.int64)
+    _check(lib.attn_testing_segment_slots(ctypes.byref(desc), None if arr is None else arr.ctypes.data,
+                                          cu_count, segment, out.ctypes.data),
+           "attn_testing_segment_slots")
+    return tuple(int(x) for x in out)
 
 
 def workspace_bytes(desc: AttnDesc) -> int:

@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "attn_decode.h"
+#include "attn_decode_testing.h"
 #include "kernels.h"
 #include "plan.h"
 
@@ -43,16 +44,16 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Lay the (m, l, o) records of a plan out in a workspace slice.
-PartialLayout carve(char *base, const attn_plan_t &p, int64_t groups, int head_dim) {
+PartialLayout carve(char *base, const attn_plan_t &p, int head_dim) {
   PartialLayout pl{};
-  pl.chunks = p.chunks_per_seq;
-  pl.rows = p.row_blocks * p.rows_per_block;
-  const int64_t records = groups * (int64_t)pl.chunks * pl.rows;
+  pl.rows = p.rows_per_block;
+  const int64_t records = p.record_slots * p.rows_per_block;
   if (records <= 0 || !base) return pl;
   const int64_t ml = round_up(records * (int64_t)sizeof(float), 256);
   pl.m = reinterpret_cast<float *>(base);
   pl.l = reinterpret_cast<float *>(base + ml);
   pl.o = reinterpret_cast<float *>(base + 2 * ml);
+  (void)head_dim;
   return pl;
 }
 
@@ -62,18 +63,12 @@ SplitArgs split_args(const attn_desc_t *d, const attn_plan_t &p, const void *q, 
   a.q = q;
   a.k = k;
   a.v = v;
-  a.kv_lens = d->kv_lens;
+  a.map = work_map(d, p);
   a.part = part;
-  a.L_max = d->max_kv_len;
-  a.B = d->batch;
   a.q_len = d->q_len;
   a.Hq = d->num_q_heads;
-  a.Hkv = d->num_kv_heads;
   a.G = d->num_q_heads / d->num_kv_heads;
   a.R = p.rows;
-  a.row_blocks = p.row_blocks;
-  a.chunk_len = p.chunk_len;
-  a.n_chunks = p.chunks_per_seq;
   a.causal = d->causal;
   a.scale_log2 = d->scale * kLog2eHost;
   return a;
@@ -82,7 +77,7 @@ SplitArgs split_args(const attn_desc_t *d, const attn_plan_t &p, const void *q, 
 hipError_t launch_split(const attn_desc_t *d, const attn_plan_t &p, const SplitArgs &a,
                         bool energy, hipStream_t s) {
   if (p.work_items <= 0) return hipSuccess;
-  if (p.kernel == 1) return launch_split_mfma(p, a, d->head_dim, energy, s);
+  if (p.kernel >= 1) return launch_split_mfma(p, a, d->head_dim, energy, s);
   return launch_split_valu(p, a, d->dtype, d->head_dim, energy, s);
 }
 
@@ -103,7 +98,7 @@ attn_status_t prepare(const attn_desc_t *d, void *ws, size_t ws_bytes, attn_plan
   if (p->workspace_bytes > 0 && !ws) return ATTN_ERR_NULL;
   if (ws_bytes < p->workspace_bytes) return ATTN_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return ATTN_ERR_ALIGN;
-  *part = carve(static_cast<char *>(ws), *p, (int64_t)d->batch * d->num_kv_heads, d->head_dim);
+  *part = carve(static_cast<char *>(ws), *p, d->head_dim);
   return ATTN_OK;
 }
 
@@ -148,16 +143,12 @@ attn_status_t merge_impl(const attn_desc_t *d, float *o, float *lse, void *ws, s
   attn_status_t st = prepare(d, ws, ws_bytes, &p, &part, &empty);
   if (st != ATTN_OK || empty) return st;
   MergeArgs m{};
+  m.map = work_map(d, p);
   m.part = part;
-  m.kv_lens = d->kv_lens;
-  m.L_max = d->max_kv_len;
-  m.B = d->batch;
   m.q_len = d->q_len;
   m.Hq = d->num_q_heads;
-  m.Hkv = d->num_kv_heads;
   m.G = d->num_q_heads / d->num_kv_heads;
   m.R = p.rows;
-  m.chunk_len = p.chunk_len;
   m.o = o;
   m.lse = lse;
   (void)hipGetLastError();
@@ -313,10 +304,8 @@ attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const v
     if (workspace_bytes < b.total) return ATTN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
     char *ws = static_cast<char *>(workspace);
-    const PartialLayout pre = carve(ws, b.pp, (int64_t)desc->num_kv_heads, desc->head_dim);
-    const PartialLayout suf = carve(ws + b.pre_bytes, b.sp,
-                                    (int64_t)desc->num_samples * desc->num_kv_heads,
-                                    desc->head_dim);
+    const PartialLayout pre = carve(ws, b.pp, desc->head_dim);
+    const PartialLayout suf = carve(ws + b.pre_bytes, b.sp, desc->head_dim);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (launch_split(&b.pre, b.pp, split_args(&b.pre, b.pp, q, k_prefix, v_prefix, pre), false,
@@ -326,20 +315,76 @@ attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const v
                      s) != hipSuccess)
       return ATTN_ERR_HIP;
     MergeArgs m{};
+    m.map = work_map(&b.suf, b.sp);
     m.part = suf;
-    if (b.pp.work_items > 0) m.shared = pre;
-    m.kv_lens = nullptr;
-    m.L_max = desc->suffix_len;
-    m.B = desc->num_samples;
+    m.has_shared = b.pp.work_items > 0;
+    m.smap = work_map(&b.pre, b.pp);
+    m.shared = pre;
     m.q_len = 1;
     m.Hq = desc->num_q_heads;
-    m.Hkv = desc->num_kv_heads;
     m.G = desc->num_q_heads / desc->num_kv_heads;
     m.R = m.G;
-    m.chunk_len = b.sp.chunk_len;
     m.o = o;
     m.lse = lse;
     if (launch_merge(m, desc->head_dim, s) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+int64_t attn_testing_pieces(const attn_desc_t *desc, const int32_t *host_lens, int32_t cu_count,
+                            int64_t w, int64_t *out, int64_t max_pieces) {
+  try {
+    attn_plan_t p;
+    attn_status_t st = make_plan(desc, cu_count, kMfma, &p);
+    if (st != ATTN_OK) return -(int64_t)st;
+    if (w < 0 || w >= p.work_items || (!out && max_pieces > 0)) return -(int64_t)ATTN_ERR_VALUE;
+    attn_desc_t d = *desc;
+    d.kv_lens = host_lens;
+    const WorkMap m = work_map(&d, p);
+    int64_t n = 0;
+    auto emit = [&](int64_t sigma, int64_t t0, int64_t t1, int64_t slot) {
+      if (n < max_pieces) {
+        out[4 * n] = sigma;
+        out[4 * n + 1] = t0;
+        out[4 * n + 2] = t1;
+        out[4 * n + 3] = slot;
+      }
+      ++n;
+    };
+    if (m.mode == 0) {
+      const int64_t sigma = w / m.n_chunks, c = w % m.n_chunks;
+      const int b = (int)(sigma / segs_per_seq(m));
+      const int64_t L = seq_len(m, b), c0 = c * m.chunk_len;
+      if (c0 < L) emit(sigma, c0, c0 + m.chunk_len < L ? c0 + m.chunk_len : L, w);
+    } else {
+      const int64_t U = total_units(m);
+      PieceCursor cur = first_piece(m, U, w);
+      Piece pc;
+      while (next_piece(m, w, cur, &pc)) emit(pc.sigma, pc.t0, pc.t1, pc.slot);
+    }
+    return n;
+  } catch (...) {
+    return -(int64_t)ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_testing_segment_slots(const attn_desc_t *desc, const int32_t *host_lens,
+                                         int32_t cu_count, int64_t segment, int64_t out[3]) {
+  try {
+    attn_plan_t p;
+    attn_status_t st = make_plan(desc, cu_count, kMfma, &p);
+    if (st != ATTN_OK) return st;
+    if (!out) return ATTN_ERR_NULL;
+    attn_desc_t d = *desc;
+    d.kv_lens = host_lens;
+    const WorkMap m = work_map(&d, p);
+    if (segment < 0 || segment >= (int64_t)m.B * segs_per_seq(m)) return ATTN_ERR_VALUE;
+    const SlotRange r = segment_slots(m, total_units(m), (int)(segment / segs_per_seq(m)), segment);
+    out[0] = r.first;
+    out[1] = r.stride;
+    out[2] = r.count;
     return ATTN_OK;
   } catch (...) {
     return ATTN_ERR_HIP;

@@ -52,6 +52,12 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off *= 2) x += __shfl_xor(x, off);
+  return x;
+}
+
 // bfloat16 pair (little-endian: element 2e in the low half) -> two floats.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) {

@@ -5,46 +5,44 @@
 #include <stdint.h>
 
 #include "attn_decode.h"
+#include "work_map.h"
 
 namespace attn {
 
-// Where the partial (m, l, o) records of one decode call live in the
-// workspace: m and l are [groups][chunks][Rp] floats (m in log2 units), o is
-// [groups][chunks][Rp][D] floats; groups = B * Hkv, Rp = row_blocks * RB.
+// Partial (m, l, o) records in the workspace: record (slot, r) of a work
+// map holds rows r < rows of one segment piece; m and l are float[slots*rows]
+// (m in log2 units), o is float[slots*rows][D].
 struct PartialLayout {
   float *m;
   float *l;
   float *o;
-  int32_t chunks;   // chunk slots per group
-  int32_t rows;     // Rp
+  int32_t rows;  // rows per record slot (the rows of one row block)
 };
 
 struct SplitArgs {
   const void *q;
   const void *k;
   const void *v;
-  const int32_t *kv_lens;  // device, may be null
+  WorkMap map;
   PartialLayout part;
-  int64_t L_max;
-  int32_t B, q_len, Hq, Hkv, G, R, row_blocks;
-  int32_t chunk_len, n_chunks;
+  int32_t q_len, Hq, G, R;
   int32_t causal;
   float scale_log2;  // scale * log2(e)
 };
 
-// Merge of every record of a row, then normalisation.  Row r of group
-// (b, kvh) merges the chunk records [0, ceil(L_b / chunk_len)) of `part` and,
-// when shared.m is not null, all shared.chunks records of `shared` at group
-// kvh, row b * R + r (records computed once for every batch entry, e.g. a
-// shared prefix whose query rows are all samples' rows).
+// Merge of every record of a row, then normalisation.  Output row r of
+// (b, kvh) merges the records of segment ((b*Hkv + kvh)*row_blocks + r/rows)
+// and, when has_shared, the records of the shared layout for its row
+// b*R + r of KV head kvh (records computed once for all batch entries, e.g.
+// a shared prefix whose query rows are every sample's rows).
 struct MergeArgs {
+  WorkMap map;
   PartialLayout part;
+  int32_t has_shared;
+  WorkMap smap;
   PartialLayout shared;
-  const int32_t *kv_lens;  // device, may be null
-  int64_t L_max;
-  int32_t B, q_len, Hq, Hkv, G, R;
-  int32_t chunk_len;
-  float *o;                // may be null (energy only)
+  int32_t q_len, Hq, G, R;
+  float *o;  // may be null (energy only)
   float *lse;
 };
 

@@ -1,12 +1,12 @@
-// Host-side validation and KV-chunk partitioning (no HIP calls).
+// Host-side validation and KV partitioning (no HIP calls).
 //
-// The partitioner turns one decode call into work items (b, KV head, row
-// block, chunk).  Tree Attention computes one local energy per device and
-// Star Attention one block per host; on one GPU the unit of parallel work is
-// the workgroup, so the chunk length C is chosen so that the number of items
-// is a small multiple of the compute-unit count: every CU streams about the
-// same number of KV bytes, and the per-chunk records stay a tiny fraction of
-// the KV traffic.
+// The partitioner turns one decode call into workgroups.  Tree Attention
+// computes one local energy per device and Star Attention one block per host;
+// on one GPU the unit of parallel work is the workgroup.  By default the
+// balanced layout of work_map.h is used: one workgroup per CU, each streaming
+// an equal share of all (sequence, KV head, row block) segments' tokens, with
+// the lengths read on the device, so ragged batches stay balanced.  A forced
+// chunk_len gives fixed chunks of C tokens instead.
 #include "plan.h"
 
 #include <cmath>
@@ -29,10 +29,9 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
-int items_per_cu(bool ragged) {
-  static const int forced = env_int("ATTN_DECODE_ITEMS_PER_CU", 0, 1, 1024);
-  if (forced > 0) return forced;
-  return ragged ? kRaggedItemsPerCu : kDenseItemsPerCu;
+int items_per_cu() {
+  static const int v = env_int("ATTN_DECODE_ITEMS_PER_CU", kItemsPerCu, 1, 1024);
+  return v;
 }
 
 attn_status_t validate_desc(const attn_desc_t *d) {
@@ -64,35 +63,60 @@ attn_status_t make_plan(const attn_desc_t *d, int cu_count, bool mfma_available,
   p->threads_per_item = 256;
   // Dense query blocks (many rows per KV head) go to the MFMA kernel; a few
   // rows per KV head are a bandwidth-bound stream for the vector ALUs.
-  p->kernel = (mfma_available && d->dtype == ATTN_BF16 && R > kMaxValuRows) ? 1 : 0;
+  // More than one block of 32 rows: the shared-tile MFMA kernel, whose waves
+  // own 32 rows each and read every K/V tile once for all of them.
+  p->kernel = (mfma_available && d->dtype == ATTN_BF16 && R > kMaxValuRows)
+                  ? (R > kMfmaRows ? 2 : 1) : 0;
   if (p->kernel == 0) {
     p->rows_per_block = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : 8;
-  } else {
+  } else if (p->kernel == 1) {
     p->rows_per_block = kMfmaRows;
+  } else {
+    const int waves = (R + kMfmaRows - 1) / kMfmaRows;
+    p->rows_per_block = kMfmaRows * (waves <= 2 ? 2 : waves <= 4 ? 4 : 8);
+    p->threads_per_item = p->rows_per_block * 2;  // one 64-lane wave per 32 rows
   }
   p->row_blocks = (R + p->rows_per_block - 1) / p->rows_per_block;
-  const int64_t groups = (int64_t)d->batch * d->num_kv_heads;
+  const int64_t segs = (int64_t)d->batch * d->num_kv_heads * p->row_blocks;
   const int64_t L = d->max_kv_len;
-  int64_t C;
+  if (L > 0 && segs > kMaxUnits / L) return ATTN_ERR_UNSUPPORTED;
   if (d->chunk_len > 0) {
-    C = d->chunk_len;
+    p->balanced = 0;
+    p->chunk_len = d->chunk_len;
+    p->chunks_per_seq = (int32_t)(L > 0 ? (L + d->chunk_len - 1) / d->chunk_len : 0);
+    p->work_items = segs * p->chunks_per_seq;
   } else {
-    const int64_t work = groups * p->row_blocks * L;
-    const int64_t target = (int64_t)cu_count * items_per_cu(d->kv_lens != nullptr);
-    C = round_up((work + target - 1) / (target > 0 ? target : 1), kChunkGrain);
-    if (C < kChunkGrain) C = kChunkGrain;
-    const int64_t whole = round_up(L > 0 ? L : 1, kChunkGrain);
-    if (C > whole) C = whole;
+    p->balanced = 1;
+    p->chunks_per_seq = 0;
+    const int64_t units = segs * L;  // upper bound (all sequences full)
+    int64_t W = (int64_t)cu_count * items_per_cu();
+    if (W > 65535) W = 65535;
+    const int64_t by_size = (units + kMinPiece - 1) / kMinPiece;
+    if (W > by_size) W = by_size;
+    p->work_items = units > 0 ? W : 0;
+    const int64_t per = p->work_items > 0 ? (units + W - 1) / W : 0;
+    if (per > std::numeric_limits<int32_t>::max()) return ATTN_ERR_UNSUPPORTED;
+    p->chunk_len = (int32_t)per;
   }
-  if (C > std::numeric_limits<int32_t>::max()) return ATTN_ERR_UNSUPPORTED;
-  p->chunk_len = (int32_t)C;
-  const int64_t chunks = L > 0 ? (L + C - 1) / C : 0;
-  p->chunks_per_seq = (int32_t)chunks;
-  p->work_items = groups * p->row_blocks * chunks;
   if (p->work_items > std::numeric_limits<int32_t>::max()) return ATTN_ERR_UNSUPPORTED;
-  const int64_t records = groups * chunks * (int64_t)p->row_blocks * p->rows_per_block;
-  p->workspace_bytes = partial_bytes(records, d->head_dim);
+  const WorkMap m = work_map(d, *p);
+  p->record_slots = record_slots(m);
+  p->workspace_bytes = partial_bytes(p->record_slots * p->rows_per_block, d->head_dim);
   return ATTN_OK;
+}
+
+WorkMap work_map(const attn_desc_t *d, const attn_plan_t &p) {
+  WorkMap m{};
+  m.kv_lens = d->kv_lens;
+  m.L_max = d->max_kv_len;
+  m.B = d->batch;
+  m.Hkv = d->num_kv_heads;
+  m.row_blocks = p.row_blocks;
+  m.mode = p.balanced ? 1 : 0;
+  m.chunk_len = p.balanced ? 0 : p.chunk_len;
+  m.n_chunks = p.chunks_per_seq;
+  m.n_wg = p.balanced ? (int32_t)p.work_items : 0;
+  return m;
 }
 
 size_t partial_bytes(int64_t records, int head_dim) {

@@ -22,8 +22,9 @@
 // K and V tiles are loaded coalesced (LPK lanes per key row, 16 bytes each,
 // non-temporal) and staged in wave-private LDS; the next tile's loads are in
 // flight while the current one is computed.  The four waves' (m, l, o) are
-// merged through LDS at the end, giving one record per (item, row) in the
-// same layout as the vector-ALU kernel, so the same merge kernel follows.
+// merged through LDS at the end of each piece of work (work_map.h), giving
+// one record per (piece, row) in the same layout as the vector-ALU kernel, so
+// the same merge kernel follows.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -74,33 +75,124 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// One 32-key tile in one wave: S^T = K.Q^T, masked online softmax of the
+// lane's row, O^T += V^T.P^T (P as bf16 hi + lo parts).  ks / vs: the tile in
+// LDS (row pitches KROW / VROW); t0: token of the tile's first key; lim: the
+// lane's row sees keys t < lim.
 template <int D, bool ENERGY>
-__global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
+__device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs,
+                                          const bf16x8_t (&qf)[D / 16], int t0, int lim,
+                                          float scale_log2, float &m, float &lsum,
+                                          f32x16_t (&oacc)[ENERGY ? 1 : D / 32]) {
+  using T = Tiles<D>;
+  constexpr int KS = T::KS, NT = T::NT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int h = lane >> 5;
+  const int j = lane & 31;
+  // S^T = K . Q^T
+  f32x16_t sacc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const bf16x8_t kf = __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const u32x4 *>(ks + j * T::KROW + h * (D / 2) + 8 * s));
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+  }
+  // Scale, mask, online softmax (lane l: row j, keys 8(e/4) + 4h + e%4).
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
+    sacc[e] = t < lim ? sacc[e] * scale_log2 : -INFINITY;
+    tmax = fmaxf(tmax, sacc[e]);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  if (__any(tmax > m + kLazyRescale)) {
+    const float mn = fmaxf(m, tmax);
+    const float alpha = rescale_factor(m, mn);
+    lsum *= alpha;
+    if constexpr (!ENERGY) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[n][e] *= alpha;
+    }
+    m = mn;
+  }
+  const float mref = m == -INFINITY ? 0.0f : m;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    sacc[e] = fast_exp2(sacc[e] - mref);
+    lsum += sacc[e];
+  }
+  if constexpr (!ENERGY) {
+    // P^T fragments (B operand): k-step s holds accumulator entries 8s..8s+7.
+    bf16x8_t phi[2], plo[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 wh, wl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = sacc[8 * s + 2 * e], p1 = sacc[8 * s + 2 * e + 1];
+        const uint32_t hw = pack_bf16(p0, p1);
+        wh[e] = hw;
+        const float h0 = __builtin_bit_cast(float, hw << 16);
+        const float h1 = __builtin_bit_cast(float, hw & 0xFFFF0000u);
+        wl[e] = pack_bf16(p0 - h0, p1 - h1);
+      }
+      phi[s] = __builtin_bit_cast(bf16x8_t, wh);
+      plo[s] = __builtin_bit_cast(bf16x8_t, wl);
+    }
+    // V^T fragments (A operand) by transpose reads: in 16-lane group g,
+    // lane lg points at key k0 + lg/4, column n0 + 4(lg%4); it receives
+    // the four keys k0..k0+3 of column n0 + lg.
+    const int g = lane >> 4, lg = lane & 15;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        s16x4_t part[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int key = 16 * s + 8 * r + 4 * (g >> 1) + (lg >> 2);
+          const int col = 32 * n + 16 * (g & 1) + 4 * (lg & 3);
+          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t *)(vs + key * T::VROW + col));
+        }
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, u32x4{(uint32_t)(uint16_t)part[0][0] | ((uint32_t)(uint16_t)part[0][1] << 16),
+                            (uint32_t)(uint16_t)part[0][2] | ((uint32_t)(uint16_t)part[0][3] << 16),
+                            (uint32_t)(uint16_t)part[1][0] | ((uint32_t)(uint16_t)part[1][1] << 16),
+                            (uint32_t)(uint16_t)part[1][2] | ((uint32_t)(uint16_t)part[1][3] << 16)});
+        oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi[s], oacc[n], 0, 0, 0);
+        oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo[s], oacc[n], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int D, bool ENERGY>
+union MfmaSmem {
+  Smem<D, ENERGY> t;
+  SmemOut<D, ENERGY> out;
+};
+
+// One piece: tokens [c0, c1) of KV head kvh of sequence b, for row block rb;
+// writes the piece's record at `slot`.
+template <int D, bool ENERGY>
+__device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, int rb, int c0,
+                                           int c1, int64_t slot, MfmaSmem<D, ENERGY> &sh) {
   using T = Tiles<D>;
   constexpr int LPK = T::LPK, KPI = T::KPI, NL = T::NL, KS = T::KS, NT = T::NT;
-  __shared__ union {
-    Smem<D, ENERGY> t;
-    SmemOut<D, ENERGY> out;
-  } sh;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int h = lane >> 5;   // lane half
   const int j = lane & 31;   // query row owned by this lane (and key slot in A layouts)
-
-  int item = blockIdx.x;
-  const int chunk = item % a.n_chunks;
-  item /= a.n_chunks;
-  const int rb = item % a.row_blocks;
-  const int group = item / a.row_blocks;
-  const int b = group / a.Hkv;
-  const int kvh = group - b * a.Hkv;
-
-  int Lb = a.kv_lens ? a.kv_lens[b] : (int)a.L_max;
-  Lb = Lb < 0 ? 0 : (Lb > (int)a.L_max ? (int)a.L_max : Lb);
-  const int c0 = chunk * a.chunk_len;
-  if (c0 >= Lb) return;
-  const int c1 = min(c0 + a.chunk_len, Lb);
+  const int group = b * a.map.Hkv + kvh;
+  const int Lb = (int)seq_len(a.map, b);
+  __syncthreads();  // the previous piece's epilogue is done with the shared buffers
 
   // This lane's query row and its visibility limit (keys t < lim).
   const int row = rb * kRows + j;
@@ -137,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[n][e] = 0.0f;
 
-  const int64_t base = (int64_t)group * a.L_max * D;
+  const int64_t base = (int64_t)group * a.map.L_max * D;
   const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base + (lane % LPK) * 8;
   const uint16_t *vg = ENERGY ? nullptr : static_cast<const uint16_t *>(a.v) + base + (lane % LPK) * 8;
   uint16_t *ks = sh.t.k[wave];
@@ -172,87 +264,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
     const int t0 = c0 + tile * kTile;
     if (tile + kWaves < n_tiles) load(tile + kWaves);
 
-    // S^T = K . Q^T
-    f32x16_t sacc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8_t kf = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const u32x4 *>(ks + j * T::KROW + h * (D / 2) + 8 * s));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
-    }
-    // Scale, mask, online softmax (lane l: row j, keys 8(e/4) + 4h + e%4).
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
-      sacc[e] = t < lim ? sacc[e] * a.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sacc[e]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (__any(tmax > m + kLazyRescale)) {
-      const float mn = fmaxf(m, tmax);
-      const float alpha = rescale_factor(m, mn);
-      lsum *= alpha;
-      if constexpr (!ENERGY) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[n][e] *= alpha;
-      }
-      m = mn;
-    }
-    const float mref = m == -INFINITY ? 0.0f : m;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sacc[e] = fast_exp2(sacc[e] - mref);
-      lsum += sacc[e];
-    }
-    if constexpr (!ENERGY) {
-      // P^T fragments (B operand): k-step s holds accumulator entries 8s..8s+7.
-      bf16x8_t phi[2], plo[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u32x4 wh, wl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = sacc[8 * s + 2 * e], p1 = sacc[8 * s + 2 * e + 1];
-          const uint32_t hw = pack_bf16(p0, p1);
-          wh[e] = hw;
-          const float h0 = __builtin_bit_cast(float, hw << 16);
-          const float h1 = __builtin_bit_cast(float, hw & 0xFFFF0000u);
-          wl[e] = pack_bf16(p0 - h0, p1 - h1);
-        }
-        phi[s] = __builtin_bit_cast(bf16x8_t, wh);
-        plo[s] = __builtin_bit_cast(bf16x8_t, wl);
-      }
-      // V^T fragments (A operand) by transpose reads: in 16-lane group g,
-      // lane lg points at key k0 + lg/4, column n0 + 4(lg%4); it receives
-      // the four keys k0..k0+3 of column n0 + lg.
-      const int g = lane >> 4, lg = lane & 15;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          s16x4_t part[2];
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const int key = 16 * s + 8 * r + 4 * (g >> 1) + (lg >> 2);
-            const int col = 32 * n + 16 * (g & 1) + 4 * (lg & 3);
-            part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t *)(vs + key * T::VROW + col));
-          }
-          const bf16x8_t vf = __builtin_bit_cast(
-              bf16x8_t, u32x4{(uint32_t)(uint16_t)part[0][0] | ((uint32_t)(uint16_t)part[0][1] << 16),
-                              (uint32_t)(uint16_t)part[0][2] | ((uint32_t)(uint16_t)part[0][3] << 16),
-                              (uint32_t)(uint16_t)part[1][0] | ((uint32_t)(uint16_t)part[1][1] << 16),
-                              (uint32_t)(uint16_t)part[1][2] | ((uint32_t)(uint16_t)part[1][3] << 16)});
-          oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi[s], oacc[n], 0, 0, 0);
-          oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo[s], oacc[n], 0, 0, 0);
-        }
-      }
-    }
+    tile_step<D, ENERGY>(ks, vs, qf, t0, lim, a.scale_log2, m, lsum, oacc);
   }
 
   // Per-wave row statistics: lanes l and l + 32 hold the same m and halves of l.
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
         sh.out.o[wave][j][32 * n + 8 * (e >> 2) + 4 * h + (e & 3)] = oacc[n][e];
   }
   __syncthreads();
-  const int64_t rec0 = ((int64_t)group * a.part.chunks + chunk) * a.part.rows + rb * kRows;
+  const int64_t rec0 = slot * kRows;
   constexpr int kOut = ENERGY ? kRows : kRows * D;
   for (int idx = threadIdx.x; idx < kOut; idx += kThreads) {
     const int r = ENERGY ? idx : idx / D;
@@ -294,6 +306,231 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
 }
 
 template <int D, bool ENERGY>
+__global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
+  __shared__ MfmaSmem<D, ENERGY> sh;
+  const WorkMap &m = a.map;
+  if (m.mode == 0) {
+    const int w = blockIdx.x;
+    const int sigma = w / m.n_chunks, c = w - sigma * m.n_chunks;
+    const int group = sigma / m.row_blocks, rb = sigma - group * m.row_blocks;
+    const int b = group / m.Hkv, kvh = group - b * m.Hkv;
+    const int L = (int)seq_len(m, b);
+    const int c0 = c * m.chunk_len;
+    if (c0 >= L) return;
+    mfma_piece<D, ENERGY>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
+  } else {
+    const int64_t U = total_units(m);
+    PieceCursor cur = first_piece(m, U, blockIdx.x);
+    Piece p;
+    while (next_piece(m, blockIdx.x, cur, &p))
+      mfma_piece<D, ENERGY>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared-tile variant for many query rows per KV head (R > 32): a workgroup of
+// RW waves owns 32*RW rows, all waves walk the same keys, and each 32-key K/V
+// tile is loaded into LDS once (cooperatively, double-buffered) and used by
+// every wave.  For a shared prefix this reads the prefix once for all samples
+// instead of once per block of 32 rows.  No cross-wave merge: each wave
+// writes the records of its own 32 rows.
+// ---------------------------------------------------------------------------
+template <int D, int RW, bool ENERGY>
+union RowsSmem {
+  struct {
+    uint16_t k[2][kTile * Tiles<D>::KROW];
+    uint16_t v[2][ENERGY ? 1 : kTile * Tiles<D>::VROW];
+  } t;
+  float stage[RW][kRows * 32];  // epilogue: one 32 x 32 float slice per wave
+};
+
+template <int D, int RW, bool ENERGY>
+__device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, int rb, int c0,
+                                           int c1, int64_t slot, RowsSmem<D, RW, ENERGY> &sh) {
+  using T = Tiles<D>;
+  constexpr int KS = T::KS, NT = T::NT;
+  constexpr int NTH = RW * kWave;
+  constexpr int PIECES = kTile * D / 8;  // 16-byte pieces per tensor tile
+  constexpr int PER = (PIECES + NTH - 1) / NTH;  // pieces per thread per tensor
+  static_assert(PIECES % kWave == 0, "whole waves take part in the tile copy");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int h = lane >> 5;
+  const int j = lane & 31;
+  const int group = b * a.map.Hkv + kvh;
+  const int Lb = (int)seq_len(a.map, b);
+  __syncthreads();  // the previous piece is done with the tile buffers
+
+  const int row = rb * kRows * RW + wave * kRows + j;
+  const bool valid = row < a.R;
+  int lim = c0;
+  bf16x8_t qf[KS];
+  if (valid) {
+    const int i = row / a.G;
+    const int head = kvh * a.G + (row - i * a.G);
+    lim = a.causal ? Lb - a.q_len + i + 1 : Lb;
+    lim = lim < c0 ? c0 : (lim > c1 ? c1 : lim);
+    const uint16_t *q = static_cast<const uint16_t *>(a.q) +
+                        (((int64_t)b * a.q_len + i) * a.Hq + head) * D + h * (D / 2);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4 *>(q + 8 * s));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, u32x4{0, 0, 0, 0});
+  }
+  int hi;
+  {
+    const int last = min(a.R, (rb + 1) * kRows * RW) - 1;
+    const int ilast = last / a.G;
+    hi = a.causal ? Lb - a.q_len + ilast + 1 : Lb;
+    hi = hi < c0 ? c0 : (hi > c1 ? c1 : hi);
+  }
+
+  float m = -INFINITY, lsum = 0.0f;
+  f32x16_t oacc[ENERGY ? 1 : NT];
+#pragma unroll
+  for (int n = 0; n < (ENERGY ? 1 : NT); ++n)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[n][e] = 0.0f;
+
+  const int64_t base = (int64_t)group * a.map.L_max * D;
+  const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
+  const uint16_t *vg = ENERGY ? nullptr : static_cast<const uint16_t *>(a.v) + base;
+  const int n_tiles = (hi - c0 + kTile - 1) / kTile;
+
+  // Tiles in flight: a ring of NS register stages (tile t lives in stage
+  // t % NS) feeding two LDS buffers.  Stage indices are compile-time inside
+  // the unrolled inner loop, so the ring stays in registers.
+  constexpr int NS = RW >= 8 ? 3 : (RW >= 4 ? 2 : 1);
+  u32x4 kr[NS][PER], vr[NS][ENERGY ? 1 : PER];
+  auto load = [&](int tile, u32x4 (&kd)[PER], u32x4 (&vd)[ENERGY ? 1 : PER]) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int p = threadIdx.x + i * NTH;
+      if (PIECES % NTH != 0 && p >= PIECES) break;  // wave-uniform
+      const int key = p / (D / 8), col = (p % (D / 8)) * 8;
+      int t = c0 + tile * kTile + key;
+      t = t < hi ? t : hi - 1;
+      kd[i] = load_nt(kg + (int64_t)t * D + col);
+      if constexpr (!ENERGY) vd[i] = load_nt(vg + (int64_t)t * D + col);
+    }
+  };
+  auto store = [&](int buf, const u32x4 (&kd)[PER], const u32x4 (&vd)[ENERGY ? 1 : PER]) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int p = threadIdx.x + i * NTH;
+      if (PIECES % NTH != 0 && p >= PIECES) break;  // wave-uniform
+      const int key = p / (D / 8), col = (p % (D / 8)) * 8;
+      *reinterpret_cast<u32x4 *>(sh.t.k[buf] + key * T::KROW + col) = kd[i];
+      if constexpr (!ENERGY) *reinterpret_cast<u32x4 *>(sh.t.v[buf] + key * T::VROW + col) = vd[i];
+    }
+  };
+
+  // Prologue: tile 0 into LDS buffer 0, tiles 1..NS in flight.
+  if (n_tiles > 0) {
+    load(0, kr[0], vr[0]);
+    store(0, kr[0], vr[0]);
+#pragma unroll
+    for (int k = 1; k <= NS; ++k)
+      if (k < n_tiles) load(k, kr[k % NS], vr[k % NS]);
+  }
+  __syncthreads();
+  for (int base = 0; base < n_tiles; base += NS) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int tile = base + k;
+      if (tile >= n_tiles) break;  // uniform across the workgroup
+      tile_step<D, ENERGY>(sh.t.k[tile & 1], sh.t.v[tile & 1], qf, c0 + tile * kTile, lim,
+                           a.scale_log2, m, lsum, oacc);
+      if (tile + 1 < n_tiles) {
+        const int kn = (k + 1) % NS;  // stage of tile + 1 (constant once unrolled)
+        store((tile + 1) & 1, kr[kn], vr[kn]);
+        if (tile + 1 + NS < n_tiles) load(tile + 1 + NS, kr[kn], vr[kn]);
+      }
+      __syncthreads();
+    }
+  }
+
+  lsum += __shfl_xor(lsum, 32);
+  const int64_t rec0 = slot * (kRows * RW) + wave * kRows;  // this wave's first row
+  if (h == 0) {
+    a.part.m[rec0 + j] = m;
+    a.part.l[rec0 + j] = lsum;
+  }
+  if constexpr (!ENERGY) {
+    // Each wave turns its O^T tiles into row-contiguous stores through its own
+    // 32 x 32 float slice of the (now idle) tile buffers: lane l holds rows'
+    // dims 8(e/4) + 4h + e%4 of tile n; after the exchange every lane writes
+    // 16 contiguous bytes and each row's 32 dims form one 128-byte run.
+    // Slice row pitch 32 floats; 4-float column groups are XOR-swizzled by
+    // row (keeps float4 alignment, spreads the column writes over banks).
+    constexpr int OP = 32;
+    float *stage = sh.stage[wave];
+    const int swz_w = (j & 7) * 4;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        stage[j * OP + ((8 * (e >> 2) + 4 * h) ^ swz_w) + (e & 3)] = oacc[n][e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int idx = q * kWave + lane;   // 256 float4 = 32 rows x 8
+        const int rr = idx >> 3, c4 = (idx & 7) * 4;
+        const float4 v = *reinterpret_cast<const float4 *>(stage + rr * OP + (c4 ^ ((rr & 7) * 4)));
+        *reinterpret_cast<float4 *>(a.part.o + (rec0 + rr) * D + 32 * n + c4) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+template <int D, int RW, bool ENERGY>
+__global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
+  __shared__ RowsSmem<D, RW, ENERGY> sh;
+  const WorkMap &m = a.map;
+  if (m.mode == 0) {
+    const int w = blockIdx.x;
+    const int sigma = w / m.n_chunks, c = w - sigma * m.n_chunks;
+    const int group = sigma / m.row_blocks, rb = sigma - group * m.row_blocks;
+    const int b = group / m.Hkv, kvh = group - b * m.Hkv;
+    const int L = (int)seq_len(m, b);
+    const int c0 = c * m.chunk_len;
+    if (c0 >= L) return;
+    rows_piece<D, RW, ENERGY>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
+  } else {
+    const int64_t U = total_units(m);
+    PieceCursor cur = first_piece(m, U, blockIdx.x);
+    Piece p;
+    while (next_piece(m, blockIdx.x, cur, &p))
+      rows_piece<D, RW, ENERGY>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
+  }
+}
+
+template <int D, int RW, bool ENERGY>
+hipError_t launch_rows(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, ENERGY>), dim3((unsigned)plan.work_items),
+                     dim3(RW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool ENERGY>
+hipError_t launch_rows_rw(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+  switch (plan.rows_per_block) {
+    case 2 * kRows: return launch_rows<D, 2, ENERGY>(plan, a, stream);
+    case 4 * kRows: return launch_rows<D, 4, ENERGY>(plan, a, stream);
+    case 8 * kRows: return launch_rows<D, 8, ENERGY>(plan, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, bool ENERGY>
 hipError_t launch(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((split_kv_mfma<D, ENERGY>), dim3((unsigned)plan.work_items), dim3(kThreads),
                      0, stream, a);
@@ -305,6 +542,15 @@ hipError_t launch(const attn_plan_t &plan, const SplitArgs &a, hipStream_t strea
 hipError_t launch_split_mfma(const attn_plan_t &plan, const SplitArgs &a, int head_dim,
                              bool energy_only, hipStream_t stream) {
   if (plan.work_items <= 0) return hipSuccess;
+  if (plan.kernel == 2) {
+    if (head_dim == 64)
+      return energy_only ? launch_rows_rw<64, true>(plan, a, stream)
+                         : launch_rows_rw<64, false>(plan, a, stream);
+    if (head_dim == 128)
+      return energy_only ? launch_rows_rw<128, true>(plan, a, stream)
+                         : launch_rows_rw<128, false>(plan, a, stream);
+    return hipErrorInvalidValue;
+  }
   if (plan.rows_per_block != kRows) return hipErrorInvalidValue;
   if (head_dim == 64)
     return energy_only ? launch<64, true>(plan, a, stream) : launch<64, false>(plan, a, stream);

@@ -1,11 +1,12 @@
 // Split-KV decode on the vector ALUs (gfx950, wave64).
 //
-// One workgroup = one work item (sequence b, KV head, row block, chunk of C
-// tokens).  It streams the chunk's K and V rows from HBM exactly once and
-// serves every query row of the GQA group from them, producing the chunk's
-// softmax statistics m = max s, l = sum e^(s-m) and the unnormalised output
+// Each workgroup takes its pieces of work from the work map (work_map.h): a
+// piece is a token range of one (sequence b, KV head, row block) segment.  It
+// streams the piece's K and V rows from HBM exactly once and serves every
+// query row of the GQA group from them, producing the piece's softmax
+// statistics m = max s, l = sum e^(s-m) and the unnormalised output
 // o = sum e^(s-m) v ("attention acceleration" concept page, section 2.1,
-// online softmax; the chunks stand in for the per-device local energies of
+// online softmax; the pieces stand in for the per-device local energies of
 // the Tree Attention article and the per-host blocks of Star Attention's
 // phase 2).  A second kernel (merge_partials below) combines the records.
 //
@@ -16,7 +17,7 @@
 // across the LPK lanes with DPP row operations.  Every group of LPK lanes runs
 // its own online softmax over the keys it reads (tile-level rescaling, taken
 // only when the running max grows by more than 2^8), and the key slots and
-// waves are merged once at the end of the chunk.
+// waves are merged once at the end of the piece.
 //
 // Logits are kept in log2 units (scale * log2 e folded into one fp32
 // multiply after the fp32 dot product), so exponentials are v_exp_f32.
@@ -89,8 +90,17 @@ __device__ __forceinline__ float slice_dot(const uint4 &q, const uint4 &k) {
   }
 }
 
+template <int D, int RB, bool ENERGY>
+struct ValuSmem {
+  float m[kWaves][RB], l[kWaves][RB];
+  float o[ENERGY ? 1 : kWaves][ENERGY ? 1 : RB][ENERGY ? 1 : D];
+};
+
+// One piece: tokens [c0, c1) of KV head kvh of sequence b, for row block rb;
+// writes the piece's record at `slot`.
 template <typename T, int D, int RB, int KT, bool ENERGY>
-__global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
+__device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, int rb, int c0,
+                                           int c1, int64_t slot, ValuSmem<D, RB, ENERGY> &sh) {
   using Geo = Geometry<T, D>;
   constexpr int EPL = Geo::EPL, LPK = Geo::LPK, KPW = Geo::KPW;
   constexpr int TK = KPW * KT;  // keys per wave tile
@@ -99,20 +109,8 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   const int wave = threadIdx.x / kWave;
   const int kr = lane / LPK;  // key slot in a wave load
   const int kl = lane % LPK;  // slice of the key row
-
-  int item = blockIdx.x;
-  const int chunk = item % a.n_chunks;
-  item /= a.n_chunks;
-  const int rb = item % a.row_blocks;
-  const int group = item / a.row_blocks;
-  const int b = group / a.Hkv;
-  const int kvh = group - b * a.Hkv;
-
-  int Lb = a.kv_lens ? a.kv_lens[b] : (int)a.L_max;
-  Lb = Lb < 0 ? 0 : (Lb > (int)a.L_max ? (int)a.L_max : Lb);
-  const int c0 = chunk * a.chunk_len;
-  if (c0 >= Lb) return;  // past the sequence: the merge reads ceil(L_b / C) records only
-  const int c1 = min(c0 + a.chunk_len, Lb);
+  const int group = b * a.map.Hkv + kvh;
+  const int Lb = (int)seq_len(a.map, b);
 
   // Visibility limit per row (keys t < lim[r]) and the query slices.
   int lim[RB];
@@ -147,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
     }
   }
 
-  const int64_t row_base = (int64_t)group * a.L_max * D + kl * EPL;
+  const int64_t row_base = (int64_t)group * a.map.L_max * D + kl * EPL;
   const T *kbase = static_cast<const T *>(a.k) + row_base;
   const T *vbase = ENERGY ? nullptr : static_cast<const T *>(a.v) + row_base;
   const int n_tiles = (hi - c0 + TK - 1) / TK;
@@ -249,9 +247,12 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
     }
   }
 
-  // Merge the waves through LDS and write the chunk's record.
-  __shared__ float sm[kWaves][RB], sl[kWaves][RB];
-  __shared__ float so[ENERGY ? 1 : kWaves][ENERGY ? 1 : RB][ENERGY ? 1 : D];
+  // Merge the waves through LDS and write the piece's record (the barrier
+  // keeps the previous piece's readers of the buffers ahead of these writes).
+  auto &sm = sh.m;
+  auto &sl = sh.l;
+  auto &so = sh.o;
+  __syncthreads();
   if (kr == 0) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
     }
   }
   __syncthreads();
-  const int64_t rec0 = ((int64_t)group * a.part.chunks + chunk) * a.part.rows + rb * RB;
+  const int64_t rec0 = slot * RB;
   constexpr int kOut = ENERGY ? RB : RB * D;
   for (int idx = threadIdx.x; idx < kOut; idx += kThreads) {
     const int r = ENERGY ? idx : idx / D;
@@ -289,6 +290,28 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   }
 }
 
+template <typename T, int D, int RB, int KT, bool ENERGY>
+__global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
+  __shared__ ValuSmem<D, RB, ENERGY> sh;
+  const WorkMap &m = a.map;
+  if (m.mode == 0) {
+    const int w = blockIdx.x;
+    const int sigma = w / m.n_chunks, c = w - sigma * m.n_chunks;
+    const int group = sigma / m.row_blocks, rb = sigma - group * m.row_blocks;
+    const int b = group / m.Hkv, kvh = group - b * m.Hkv;
+    const int L = (int)seq_len(m, b);
+    const int c0 = c * m.chunk_len;
+    if (c0 >= L) return;  // past the sequence: the merge reads ceil(L_b / C) records only
+    valu_piece<T, D, RB, KT, ENERGY>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
+  } else {
+    const int64_t U = total_units(m);
+    PieceCursor cur = first_piece(m, U, blockIdx.x);
+    Piece p;
+    while (next_piece(m, blockIdx.x, cur, &p))
+      valu_piece<T, D, RB, KT, ENERGY>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
+  }
+}
+
 // One workgroup per output row.  The row's records are read in parallel:
 // 16 bytes of o per lane, kMergeThreads / (D/4) records per pass, so a row of
 // ~100 records takes a handful of passes instead of a serial walk.  The max
@@ -307,18 +330,48 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   const int64_t row = blockIdx.x;
   const int r = (int)(row % a.R);
   const int group = (int)(row / a.R);
-  const int b = group / a.Hkv;
-  const int kvh = group - b * a.Hkv;
+  const int b = group / a.map.Hkv;
+  const int kvh = group - b * a.map.Hkv;
 
-  int64_t Lb = a.kv_lens ? (int64_t)a.kv_lens[b] : a.L_max;
-  Lb = Lb < 0 ? 0 : (Lb > a.L_max ? a.L_max : Lb);
-  int P = (int)((Lb + a.chunk_len - 1) / a.chunk_len);
-  P = min(P, a.part.chunks);
-  const int S = a.shared.m ? a.shared.chunks : 0;
-  const int64_t pstride = a.part.rows;
-  const int64_t prow = (int64_t)group * a.part.chunks * pstride + r;
-  const int64_t sstride = a.shared.rows;
-  const int64_t srow = a.shared.m ? (int64_t)kvh * a.shared.chunks * sstride + (int64_t)b * a.R + r : 0;
+  // The row's records: its segment's pieces, then (optionally) the shared
+  // ones.  Wave 0 sums the sequence lengths (all, and those before b) in
+  // parallel; lane 0 locates the records; LDS broadcasts them.
+  __shared__ int64_t where[6];
+  if (wave == 0) {
+    int64_t tot = 0, pre = 0;
+    if (a.map.mode != 0) {
+      for (int bb = lane; bb < a.map.B; bb += kWave) {
+        const int64_t L = seq_len(a.map, bb);
+        tot += L;
+        pre += bb < b ? L : 0;
+      }
+      tot = wave_sum_i64(tot);
+      pre = wave_sum_i64(pre);
+    }
+    if (lane == 0) {
+      const int RBp = a.part.rows;
+      const int64_t sigma = (int64_t)group * a.map.row_blocks + r / RBp;
+      const SlotRange pr = segment_slots_at(a.map, tot * segs_per_seq(a.map), pre, b, sigma);
+      where[0] = pr.count;
+      where[1] = pr.first * RBp + r % RBp;
+      where[2] = pr.stride * RBp;
+      where[3] = 0;
+      where[4] = 0;
+      where[5] = 0;
+      if (a.has_shared) {
+        const int RBs = a.shared.rows;
+        const int rs = b * a.R + r;
+        const int64_t ssig = (int64_t)kvh * a.smap.row_blocks + rs / RBs;
+        const SlotRange sr = segment_slots(a.smap, total_units(a.smap), 0, ssig);
+        where[3] = sr.count;
+        where[4] = sr.first * RBs + rs % RBs;
+        where[5] = sr.stride * RBs;
+      }
+    }
+  }
+  __syncthreads();
+  const int P = (int)where[0], S = (int)where[3];
+  const int64_t prow = where[1], pstride = where[2], srow = where[4], sstride = where[5];
   auto rec_of = [&](int c) { return c < P ? prow + c * pstride : srow + (c - P) * sstride; };
   auto m_of = [&](int c) { return c < P ? a.part.m[prow + c * pstride] : a.shared.m[srow + (c - P) * sstride]; };
 
@@ -415,7 +468,7 @@ hipError_t launch_split_valu(const attn_plan_t &plan, const SplitArgs &a, attn_d
 }
 
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Hkv * a.R;
+  const int64_t rows = (int64_t)a.map.B * a.map.Hkv * a.R;
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)rows), block(kMergeThreads);
   const bool energy = a.o == nullptr;

@@ -23,14 +23,23 @@ def lib():
     return binding.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
 
 
+def all_declared_functions():
+    import glob
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        names.update(declared_functions(h))
+    return sorted(names)
+
+
 def test_header_declares_the_boundary():
     names = declared_functions()
+    assert "attn_testing_pieces" not in names  # the testing hook has its own header
     for n in ("attn_decode_energy", "attn_decode", "attn_decode_bifurcated"):
         assert n in names
     assert set(names) == set(binding.EXPORTS)
@@ -40,7 +49,8 @@ def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (attn_[a-z_]+)\b", out))
-    for name in declared_functions():
+    assert "attn_testing_pieces" in all_declared_functions()
+    for name in all_declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
 
@@ -57,7 +67,8 @@ int main(void) {
   F(attn_desc_t, max_kv_len) F(attn_desc_t, kv_lens) F(attn_desc_t, scale)
   F(attn_desc_t, chunk_len) F(attn_desc_t, dtype)
   printf("attn_plan_t %zu\\n", sizeof(attn_plan_t));
-  F(attn_plan_t, work_items) F(attn_plan_t, threads_per_item) F(attn_plan_t, workspace_bytes)
+  F(attn_plan_t, balanced) F(attn_plan_t, threads_per_item) F(attn_plan_t, work_items)
+  F(attn_plan_t, record_slots) F(attn_plan_t, cu_count) F(attn_plan_t, workspace_bytes)
   printf("attn_bifurcated_desc_t %zu\\n", sizeof(attn_bifurcated_desc_t));
   F(attn_bifurcated_desc_t, prefix_len) F(attn_bifurcated_desc_t, scale) F(attn_bifurcated_desc_t, dtype)
   return 0;

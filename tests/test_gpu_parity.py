@@ -90,7 +90,15 @@ MFMA = [
     (1, 8, 64, 8, 128, 1500, True, None),        # R = 64: two row blocks
     (2, 5, 14, 2, 64, 1100, True, [1100, 600]),   # R = 35: padded second block
     (1, 4, 16, 2, 128, 40000, True, None),
+    (2, 6, 16, 1, 128, 3000, True, [3000, 1000]),  # R = 96: shared-tile kernel, 4 waves
+    (1, 8, 25, 1, 64, 2500, True, None),           # R = 200: 8 waves, padded rows
+    (1, 4, 64, 1, 64, 1800, True, None),           # R = 256, D = 64
+    (1, 1, 256, 1, 128, 5000, False, None),        # R = 256: a shared-prefix shape
 ]
+
+
+def G_q(case):
+    return case[2] // case[3] * case[1]
 
 
 @pytest.mark.parametrize("case", MFMA, ids=[f"B{c[0]}_ql{c[1]}_Hq{c[2]}_Hkv{c[3]}_D{c[4]}_L{c[5]}" for c in MFMA])
@@ -100,7 +108,7 @@ def test_mfma_query_blocks(case):
                            kv_lens=lens, causal=causal, nan_pad=True)
     desc = binding.make_desc(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                              max_kv_len=L, causal=causal)
-    assert binding.plan(desc)["kernel"] == 1
+    assert binding.plan(desc)["kernel"] == (1 if G_q(case) <= 32 else 2)
     O, lse = run_decode(w)
     Or, lr = oracle_decode(w)
     check_rows(O, lse, Or, lr, what=f"mfma {case}")

@@ -1,73 +1,124 @@
-"""KV-chunk partitioner (pure host code, explicit CU count)."""
+"""KV partition (host code; the same work_map arithmetic the kernels run).
+
+Checked here, with host-side lengths through the testing hook:
+* every token of every (sequence, KV head, row block) segment is covered by
+  exactly one piece, and no piece is empty;
+* record slots are distinct and inside the workspace's slot count;
+* the slots the merge enumerates for a segment are exactly its pieces' slots,
+  in token order;
+* the balanced layout gives every workgroup the same number of tokens (+-1).
+"""
 import math
 
+import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
 from long_context_exact_split_amd import binding
 
 
-def plan(cu=256, **kw):
+def desc(**kw):
     base = dict(batch=1, q_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128, max_kv_len=4096)
     base.update(kw)
-    return binding.plan(binding.make_desc(**base), cu)
+    return binding.make_desc(**base)
+
+
+def plan(cu=256, **kw):
+    return binding.plan(desc(**kw), cu)
 
 
 def test_forced_chunk_len_single_query_fp32():
     p = plan(num_q_heads=1, num_kv_heads=1, head_dim=64, max_kv_len=4096, chunk_len=512,
              dtype=binding.ATTN_F32)
-    assert p["chunk_len"] == 512 and p["chunks_per_seq"] == 8 and p["work_items"] == 8
+    assert p["balanced"] == 0 and p["chunk_len"] == 512 and p["chunks_per_seq"] == 8
+    assert p["work_items"] == 8 and p["record_slots"] == 8
     assert p["kernel"] == 0 and p["rows"] == 1 and p["rows_per_block"] == 1
 
 
-def test_dense_decode_gives_one_item_per_cu():
-    # every sequence full: one contiguous chunk per CU
+def test_dense_decode_gives_one_share_per_cu():
     p = plan(batch=8, max_kv_len=32768)
-    assert p["rows"] == 4 and p["rows_per_block"] == 4 and p["row_blocks"] == 1
-    assert p["work_items"] == 256 and p["chunk_len"] == 8192
+    assert p["balanced"] == 1 and p["work_items"] == 256 and p["chunk_len"] == 8192
+    assert p["rows"] == 4 and p["rows_per_block"] == 4 and p["kernel"] == 0
     p = plan(max_kv_len=1 << 20)
     assert p["work_items"] == 256 and p["chunk_len"] == 32768
-    p = plan(max_kv_len=5_120_000)
-    assert 256 >= p["work_items"] > 240 and p["chunks_per_seq"] * p["chunk_len"] >= 5_120_000
+    assert p["record_slots"] == 256 + 8 - 1
 
 
-def test_ragged_lengths_get_finer_chunks():
-    # lengths on the device: the host plans on max_kv_len with ~4 items per CU
-    p = plan(batch=16, num_q_heads=32, num_kv_heads=8, max_kv_len=131072, kv_lens_ptr=0x1000)
-    assert p["work_items"] >= 4 * 256 * 0.9
+def test_query_blocks_go_to_mfma():
+    p = plan(batch=16, q_len=4, num_q_heads=64, num_kv_heads=8, max_kv_len=131072,
+             causal=True, kv_lens_ptr=0x1000)
+    assert p["kernel"] == 1 and p["rows"] == 32 and p["rows_per_block"] == 32
+    p = plan(dtype=binding.ATTN_F32, q_len=4, num_q_heads=64, num_kv_heads=8)
+    assert p["kernel"] == 0 and p["rows_per_block"] == 8 and p["row_blocks"] == 4
 
 
-def test_empty_and_tiny():
+def test_small_calls_use_fewer_workgroups():
+    p = plan(num_q_heads=1, num_kv_heads=1, max_kv_len=4096)
+    assert p["work_items"] == 16   # at least 256 tokens per workgroup
     p = plan(max_kv_len=0)
-    assert p["chunks_per_seq"] == 0 and p["work_items"] == 0 and p["workspace_bytes"] == 0
-    p = plan(max_kv_len=1)
-    assert p["chunks_per_seq"] == 1 and p["chunk_len"] == 256
+    assert p["work_items"] == 0 and p["workspace_bytes"] == 0
 
 
-@settings(max_examples=200, deadline=None)
-@given(B=st.integers(1, 32), Hkv=st.integers(1, 16), G=st.integers(1, 16), q_len=st.integers(1, 8),
-       L=st.integers(0, 3_000_000), cu=st.sampled_from([1, 8, 80, 256, 304]),
-       D=st.sampled_from([64, 128]))
-def test_every_token_covered_once(B, Hkv, G, q_len, L, cu, D):
-    p = plan(cu=cu, batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, q_len=q_len, head_dim=D,
-             max_kv_len=L)
-    R = G * q_len
-    assert p["rows"] == R
-    assert p["rows_per_block"] * p["row_blocks"] >= R
-    assert p["rows_per_block"] * (p["row_blocks"] - 1) < R
-    C, n = p["chunk_len"], p["chunks_per_seq"]
-    assert C > 0 and C % 64 == 0
-    # chunks [c*C, (c+1)*C) for c < n tile [0, L) exactly, with no empty chunk
-    assert n == (math.ceil(L / C) if L else 0)
-    assert n * C >= L and (n == 0 or (n - 1) * C < L)
-    assert p["work_items"] == B * Hkv * p["row_blocks"] * n
-    records = B * Hkv * n * p["row_blocks"] * p["rows_per_block"]
-    assert p["workspace_bytes"] >= records * (D + 2) * 4
-    if records:
-        assert p["workspace_bytes"] <= records * (D + 2) * 4 + 3 * 256
+def check_cover(d, lens, cu):
+    p = binding.plan(d, cu)
+    B, Hkv = d.batch, d.num_kv_heads
+    rbk = p["row_blocks"]
+    L = np.full(B, d.max_kv_len) if lens is None else np.minimum(np.maximum(lens, 0), d.max_kv_len)
+    segs = B * Hkv * rbk
+    covered = {s: [] for s in range(segs)}
+    slots = set()
+    per_wg = []
+    for w in range(p["work_items"]):
+        pieces = binding.testing_pieces(d, lens, cu, w)
+        per_wg.append(sum(t1 - t0 for (_, t0, t1, _) in pieces))
+        for (s, t0, t1, slot) in pieces:
+            assert 0 <= t0 < t1 <= L[s // (Hkv * rbk)], (s, t0, t1)
+            assert 0 <= slot < p["record_slots"], (slot, p["record_slots"])
+            assert slot not in slots
+            slots.add(slot)
+            covered[s].append((t0, t1, slot))
+    for s in range(segs):
+        iv = sorted(covered[s])
+        Ls = int(L[s // (Hkv * rbk)])
+        pos = 0
+        for (t0, t1, _) in iv:
+            assert t0 == pos
+            pos = t1
+        assert pos == Ls, (s, pos, Ls)
+        first, stride, count = binding.testing_segment_slots(d, lens, cu, s)
+        assert [first + k * stride for k in range(count)] == [slot for (_, _, slot) in iv]
+    if p["balanced"] and p["work_items"]:
+        assert max(per_wg) - min(per_wg) <= 1
+    return p
+
+
+@settings(max_examples=120, deadline=None)
+@given(B=st.integers(1, 6), Hkv=st.integers(1, 4), G=st.integers(1, 9), q_len=st.integers(1, 5),
+       L=st.integers(0, 5000), cu=st.sampled_from([1, 3, 8, 40, 256]),
+       forced=st.sampled_from([0, 0, 64, 448]), seed=st.integers(0, 2 ** 31),
+       ragged=st.booleans(), D=st.sampled_from([64, 128]))
+def test_pieces_tile_every_segment_exactly_once(B, Hkv, G, q_len, L, cu, forced, seed, ragged, D):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, L + 1, size=B).astype(np.int32) if ragged else None
+    if ragged and rng.random() < 0.3:
+        lens[rng.integers(0, B)] = 0
+    d = desc(batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, q_len=q_len, head_dim=D,
+             max_kv_len=L, chunk_len=forced, kv_lens_ptr=0x1000 if ragged else 0,
+             causal=q_len > 1)
+    check_cover(d, lens, cu)
+
+
+def test_ragged_70b_shape_is_balanced():
+    rng = np.random.default_rng(5)
+    lens = rng.integers(8192, 131072, endpoint=True, size=16).astype(np.int32)
+    d = desc(batch=16, q_len=4, num_q_heads=64, num_kv_heads=8, max_kv_len=131072, causal=True,
+             kv_lens_ptr=0x1000)
+    p = check_cover(d, lens, 256)
+    assert p["work_items"] == 256
 
 
 def test_plan_rejects_invalid_descriptor():
-    d = binding.make_desc(batch=1, q_len=1, num_q_heads=3, num_kv_heads=2, head_dim=64, max_kv_len=10)
+    d = binding.make_desc(batch=1, q_len=1, num_q_heads=3, num_kv_heads=2, head_dim=64,
+                          max_kv_len=10)
     with pytest.raises(binding.AttnError):
         binding.plan(d, 256)
