@@ -40,6 +40,7 @@ constexpr float kLazyRescale = 8.0f;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 load_nt(const void *p) {
@@ -54,7 +55,9 @@ struct Tiles {
   static constexpr int KS = D / 16;          // MFMA k-steps of Q.K (8 dims per lane half)
   static constexpr int NT = D / 32;          // 32-dim output tiles of O^T
   static constexpr int KROW = D + 8;         // LDS row pitch of the K tile (bf16 elements)
-  static constexpr int VROW = D + 16;        // LDS row pitch of the V tile (bf16 elements)
+  // LDS row pitch of the V tile (bf16 elements): consecutive rows 16 banks
+  // apart, so the two 16-lane groups of a transpose-read pass use disjoint banks.
+  static constexpr int VROW = D + 32;
 };
 
 template <int D, bool ENERGY>
@@ -70,9 +73,27 @@ struct SmemOut {
   float o[ENERGY ? 1 : kWaves][ENERGY ? 1 : kRows][ENERGY ? 1 : D + 4];
 };
 
+// Marks the Q fragments as produced here (after the loads that filled them
+// are known to be complete), so that the compiler's wait-count tracking does
+// not carry them into the tile loop as outstanding loads: otherwise it waits
+// for every prefetched tile in flight before the first Q.K MFMA of a tile.
+template <int KS>
+__device__ __forceinline__ void settle(bf16x8_t (&qf)[KS]) {
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 t = __builtin_bit_cast(u32x4, qf[s]);
+    uint32_t a0 = t.x, a1 = t.y, a2 = t.z, a3 = t.w;
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    qf[s] = __builtin_bit_cast(bf16x8_t, u32x4{a0, a1, a2, a3});
+  }
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
+
+// Two floats -> two bf16 (round to nearest even) in one packed conversion.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2v_t));
 }
 
 // One 32-key tile in one wave: S^T = K.Q^T, masked online softmax of the
@@ -100,12 +121,22 @@ __device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs
     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
   }
   // Scale, mask, online softmax (lane l: row j, keys 8(e/4) + 4h + e%4).
+  // Tiles wholly visible to every row of the wave skip the mask, and with a
+  // positive scale the max is taken on raw logits and the scale is fused into
+  // the exponent's argument.
+  const bool fast = scale_log2 > 0.0f && !__any(t0 + kTile > lim);
   float tmax = -INFINITY;
+  if (fast) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
-    sacc[e] = t < lim ? sacc[e] * scale_log2 : -INFINITY;
-    tmax = fmaxf(tmax, sacc[e]);
+    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
+    tmax *= scale_log2;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
+      sacc[e] = t < lim ? sacc[e] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sacc[e]);
+    }
   }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   if (__any(tmax > m + kLazyRescale)) {
@@ -121,10 +152,18 @@ __device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs
     m = mn;
   }
   const float mref = m == -INFINITY ? 0.0f : m;
+  if (fast) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    sacc[e] = fast_exp2(sacc[e] - mref);
-    lsum += sacc[e];
+    for (int e = 0; e < 16; ++e) {
+      sacc[e] = fast_exp2(fmaf(sacc[e], scale_log2, -mref));
+      lsum += sacc[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sacc[e] = fast_exp2(sacc[e] - mref);
+      lsum += sacc[e];
+    }
   }
   if constexpr (!ENERGY) {
     // P^T fragments (B operand): k-step s holds accumulator entries 8s..8s+7.
@@ -160,11 +199,9 @@ __device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs
           part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s16x4_t *)(vs + key * T::VROW + col));
         }
-        const bf16x8_t vf = __builtin_bit_cast(
-            bf16x8_t, u32x4{(uint32_t)(uint16_t)part[0][0] | ((uint32_t)(uint16_t)part[0][1] << 16),
-                            (uint32_t)(uint16_t)part[0][2] | ((uint32_t)(uint16_t)part[0][3] << 16),
-                            (uint32_t)(uint16_t)part[1][0] | ((uint32_t)(uint16_t)part[1][1] << 16),
-                            (uint32_t)(uint16_t)part[1][2] | ((uint32_t)(uint16_t)part[1][3] << 16)});
+        const bf16x8_t vf = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, part[0]),
+                                                  __builtin_bit_cast(bf16x4_t, part[1]), 0, 1, 2,
+                                                  3, 4, 5, 6, 7);
         oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi[s], oacc[n], 0, 0, 0);
         oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo[s], oacc[n], 0, 0, 0);
       }
@@ -249,6 +286,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
 
   int tile = wave;
   if (tile < n_tiles) load(tile);
+  settle<KS>(qf);
   for (; tile < n_tiles; tile += kWaves) {
     // Stage this tile in LDS (the wave's previous LDS reads are complete:
     // LDS instructions of one wave execute in order).
@@ -432,6 +470,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   if (n_tiles > 0) {
     load(0, kr[0], vr[0]);
     store(0, kr[0], vr[0]);
+    settle<KS>(qf);
 #pragma unroll
     for (int k = 1; k <= NS; ++k)
       if (k < n_tiles) load(k, kr[k % NS], vr[k % NS]);
