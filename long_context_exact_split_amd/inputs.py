@@ -302,3 +302,96 @@ def bifurcated_prefix(seed: int = 4, S: int = 64, Hq: int = 32, Hkv: int = 8, D:
     return BifurcatedWorkload(name="bifurcated_prefix", seed=seed, S=S, Hq=Hq, Hkv=Hkv, D=D,
                               Lp=Lp, Ls=Ls, scale=1.0 / math.sqrt(D), q=q, kp=kp[0], vp=vp[0],
                               ks=ks, vs=vs)
+
+
+# ----------------------------------------------------------------------------
+# Paged KV caches
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class PagedCache:
+    """K and V of a decode call stored in fixed-size pages.
+
+    ``k_pool`` / ``v_pool`` are flat element arrays (uint16 bf16 bits or
+    float32) of ``num_pages * page_stride`` elements.  Logical page j of
+    sequence b (tokens [j*P, (j+1)*P)) lives in physical page
+    ``block_table[b, j]``; element (token t, KV head kvh, dim e) of that
+    sequence sits at
+    ``block_table[b, t // P] * page_stride + kvh * head_stride + (t % P) * token_stride + e``.
+    Table entries past a sequence's last page are -1, and physical pages no
+    sequence uses are filled with NaN: neither may ever be read.
+    """
+
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    block_table: np.ndarray  # int32 [B][pages_per_seq]
+    page_size: int
+    num_pages: int
+    page_stride: int
+    head_stride: int
+    token_stride: int
+    layout: str  # "head_major" ([page][Hkv][P][D]) or "token_major" ([page][P][Hkv][D])
+    shared_pages: int = 0
+
+    @property
+    def pages_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def page_cache(w: Workload, page_size: int, layout: str = "head_major", seed: int = 0,
+               spare_pages: int = 0, share_prefix_tokens: int = 0) -> PagedCache:
+    """Scatter the (dense) cache of ``w`` into a pool of pages of ``page_size``
+    tokens, in a seeded random physical order.
+
+    With ``share_prefix_tokens`` = n > 0, every sequence first gets sequence
+    0's first n tokens (``w.k`` / ``w.v`` are changed in place, so the dense
+    arrays stay the logical cache), and the whole pages among them are stored
+    once and referenced by every sequence's table.  ``spare_pages`` extra
+    physical pages hold NaN.
+    """
+    assert layout in ("head_major", "token_major")
+    P = int(page_size)
+    assert P >= 1 and P & (P - 1) == 0, "page size must be a power of two"
+    B, Hkv, L_max, D = w.k.shape
+    lens = np.asarray(w.kv_lens, dtype=np.int64)
+    n_share = 0
+    if share_prefix_tokens:
+        n = int(min(share_prefix_tokens, lens.min()))
+        for b in range(1, B):
+            w.k[b, :, :n] = w.k[0, :, :n]
+            w.v[b, :, :n] = w.v[0, :, :n]
+        n_share = n // P  # whole pages only
+    pages_per_seq = max(1, (L_max + P - 1) // P)
+    used = [int((L + P - 1) // P) for L in lens]
+    # Physical pages: the shared ones once, then every sequence's own pages.
+    logical = [(0, j) for j in range(min(n_share, used[0]))]
+    for b in range(B):
+        logical += [(b, j) for j in range(n_share if b > 0 else min(n_share, used[0]), used[b])]
+    num_pages = len(logical) + int(spare_pages)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, P, num_pages])))
+    phys = rng.permutation(num_pages)[:len(logical)]
+    table = np.full((B, pages_per_seq), -1, dtype=np.int32)
+    for (b, j), p in zip(logical, phys):
+        table[b, j] = p
+        if b == 0 and j < n_share:
+            table[1:, j] = p
+    shape = (num_pages, Hkv, P, D) if layout == "head_major" else (num_pages, P, Hkv, D)
+    nan = BF16_NAN if w.k.dtype == np.uint16 else np.float32(np.nan)
+    pools = []
+    for src in (w.k, w.v):
+        pool = np.full(shape, nan, dtype=src.dtype)
+        for (b, j), p in zip(logical, phys):
+            t0 = j * P
+            t1 = min(int(lens[b]), t0 + P)
+            blk = src[b, :, t0:t1, :]                      # [Hkv][n][D]
+            if layout == "head_major":
+                pool[p, :, :t1 - t0, :] = blk
+            else:
+                pool[p, :t1 - t0, :, :] = blk.transpose(1, 0, 2)
+        pools.append(pool.reshape(-1))
+    if layout == "head_major":
+        strides = (Hkv * P * D, P * D, D)
+    else:
+        strides = (P * Hkv * D, D, Hkv * D)
+    return PagedCache(k_pool=pools[0], v_pool=pools[1], block_table=table, page_size=P,
+                      num_pages=num_pages, page_stride=strides[0], head_stride=strides[1],
+                      token_stride=strides[2], layout=layout, shared_pages=n_share)

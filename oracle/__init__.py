@@ -5,7 +5,8 @@ benchmark's CPU-baseline leg, never by the product path.  It shares no code
 with the HIP library.
 """
 from .attention import (attend, attend_bifurcated, attend_row, chunk_partial, energy,
-                        finalize, merge, visible)
+                        energy_rows, finalize, merge, visible)
+from .paging import attend_paged, gather
 
-__all__ = ["attend", "attend_bifurcated", "attend_row", "chunk_partial", "energy",
-           "finalize", "merge", "visible"]
+__all__ = ["attend", "attend_bifurcated", "attend_paged", "attend_row", "chunk_partial",
+           "energy", "energy_rows", "finalize", "gather", "merge", "visible"]

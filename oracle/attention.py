@@ -21,6 +21,8 @@ What it computes, and where that is stated:
   lost the decode formula in extraction; the reading used here is
   F(zeta) = ln sum_t exp(scale * q.k_t + zeta.v_t), the logsumexp form the
   article's associativity remark relies on.  F(0) is the row's logsumexp.
+* ``energy_rows`` -- F(zeta) for every row of a decode call, one zeta
+  vector per row, each row over its own visible keys.
 * ``chunk_partial`` / ``merge`` / ``finalize`` -- the per-chunk statistics
   (m, l, o) with o the unnormalised partial output, and the combination rule
   m = max(m_a, m_b), l = l_a e^(m_a - m) + l_b e^(m_b - m), same for o
@@ -175,6 +177,25 @@ def energy(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         x = x + v @ np.asarray(zeta, dtype=np.float64)
     M = x.max()
     return M + math.log(np.exp(x - M).sum())
+
+
+def energy_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_lens, scale: float,
+                zeta: np.ndarray, causal: bool = False,
+                rows: Optional[Iterable[Tuple[int, int, int]]] = None) -> np.ndarray:
+    """F(zeta) of every row of a decode call (or of the listed (b, i, h) rows),
+    each over that row's visible keys; zeta has the shape of q, one auxiliary
+    vector per row.  Returns float64 [B][q_len][Hq]; rows not listed hold NaN."""
+    B, q_len, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(B)
+    out = np.full((B, q_len, Hq), np.nan)
+    if rows is None:
+        rows = [(b, i, h) for b in range(B) for i in range(q_len) for h in range(Hq)]
+    for (b, i, h) in rows:
+        n = visible(int(lens[b]), q_len, i, causal)
+        out[b, i, h] = energy(q[b, i, h], k[b, h // G, :n], v[b, h // G, :n], scale,
+                              _widen(zeta[b, i, h]))
+    return out
 
 
 # ----------------------------------------------------------------------------

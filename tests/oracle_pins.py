@@ -13,7 +13,11 @@ raises AssertionError when ``impl`` disagrees with:
   causal block as truncated decode);
 * the energy view: central finite differences of F(zeta) give O;
 * associativity: random chunkings and random merge trees reproduce O and lse;
-* bifurcation: prefix/suffix merge equals attention over the concatenation.
+* bifurcation: prefix/suffix merge equals attention over the concatenation;
+* paging: hand-worked paged caches, and pools written by a pure-Python
+  scatter (both page layouts, shared pages) resolve to the dense cache;
+* row energies: F(0) is the row's logsumexp, and closed forms for constant
+  values and a single key.
 """
 from __future__ import annotations
 
@@ -348,5 +352,125 @@ def pin_bifurcated(impl, seed: int = 19):
             _close(lm, lse[s, h], what="bifurcated = prefix (+) suffix lse")
 
 
+# ----------------------------------------------------------------------------
+# Paged caches
+# ----------------------------------------------------------------------------
+def _elem(x) -> float:
+    return math.nan if x == "nan" else _num(x)
+
+
+def pin_paged_golden(impl):
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    for ex in g["paged"]:
+        kp = np.array([_elem(x) for x in ex["k_pool"]])
+        vp = np.array([_elem(x) for x in ex["v_pool"]])
+        table = np.array(ex["table"], dtype=np.int32)
+        L, Lm, Hkv, D = ex["kv_len"], ex["L_max"], ex["Hkv"], ex["D"]
+        geo = (ex["page_size"], ex["page_stride"], ex["head_stride"], ex["token_stride"])
+        dense = impl.gather(kp, table, [L], *geo, Hkv, D, Lm)
+        want = np.array([[[_num(x) for x in row] for row in hd] for hd in ex["dense_k"]])
+        _close(dense[0, :, :L], want, what=ex["name"] + " gathered K")
+        assert np.isnan(dense[0, :, L:]).all(), ex["name"] + ": positions past L must stay unread"
+        q = np.array(ex["q"])[None]
+        O, lse = impl.attend_paged(q, kp, vp, table, [L], ex["scale"], page_size=geo[0],
+                                   page_stride=geo[1], head_stride=geo[2], token_stride=geo[3],
+                                   num_kv_heads=Hkv, L_max=Lm)
+        want_O = np.array([[[_num(x) for x in row] for row in tok] for tok in ex["O"]])[None]
+        want_lse = np.array([[_ln_of(x) for x in tok] for tok in ex["lse_ln_of"]])[None]
+        _close(O, want_O, what=ex["name"] + " O")
+        _close(lse, want_lse, what=ex["name"] + " lse")
+
+
+def _scatter_by_loops(k, lens, P, layout, order, share_first_page):
+    """Pool and block table written element by element (independent of the
+    oracle's vectorised gather).  Physical page numbers follow ``order``."""
+    B, Hkv, _, D = k.shape
+    if layout == "head_major":
+        ps, hs, ts = Hkv * P * D, P * D, D
+    else:
+        ps, hs, ts = P * Hkv * D, D, Hkv * D
+    pages_per_seq = max(1, -(-k.shape[2] // P))
+    table = [[-1] * pages_per_seq for _ in range(B)]
+    nxt = 0
+    for b in range(B):
+        for j in range(-(-int(lens[b]) // P)):
+            if share_first_page and b > 0 and j == 0:
+                table[b][j] = table[0][0]
+                continue
+            table[b][j] = int(order[nxt])
+            nxt += 1
+    pool = [math.nan] * (len(order) * ps)
+    for b in range(B):
+        for t in range(int(lens[b])):
+            p = table[b][t // P]
+            for h in range(Hkv):
+                for e in range(D):
+                    pool[p * ps + h * hs + (t % P) * ts + e] = float(k[b, h, t, e])
+    return np.array(pool), np.array(table, dtype=np.int32), (P, ps, hs, ts)
+
+
+def pin_paged_scatter(impl, n_cases: int = 8, seed: int = 23):
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        layout = ("head_major", "token_major")[c % 2]
+        causal = c % 4 >= 2
+        share = c % 3 == 0
+        B = int(rng.integers(1, 4)); Hkv = int(rng.integers(1, 3)); G = int(rng.integers(1, 3))
+        D = int(rng.integers(1, 5)); P = 1 << int(rng.integers(0, 4))
+        q_len = 2 if causal else 1
+        Lm = int(rng.integers(q_len, 30))
+        lens = rng.integers(q_len if causal else 0, Lm + 1, size=B)
+        if share:
+            lens = np.maximum(lens, min(P, Lm))
+        k = rng.standard_normal((B, Hkv, Lm, D)); v = rng.standard_normal((B, Hkv, Lm, D))
+        if share:  # every sequence starts with sequence 0's first page
+            n0 = min(P, int(lens.min()))
+            k[1:, :, :n0] = k[0, :, :n0]; v[1:, :, :n0] = v[0, :, :n0]
+            share = n0 == P
+        q = rng.standard_normal((B, q_len, Hkv * G, D))
+        n_pages = sum(-(-int(L) // P) for L in lens) + 3
+        order = rng.permutation(n_pages)
+        kp, table, geo = _scatter_by_loops(k, lens, P, layout, order, share)
+        vp, _, _ = _scatter_by_loops(v, lens, P, layout, order, share)
+        dense = impl.gather(kp, table, lens, *geo, Hkv, D, Lm)
+        for b in range(B):
+            _close(dense[b, :, :lens[b]], k[b, :, :lens[b]], what=f"paged case {c} gather b={b}")
+            assert np.isnan(dense[b, :, lens[b]:]).all(), f"paged case {c}: read past L_b"
+        O, lse = impl.attend_paged(q, kp, vp, table, lens, 0.7, page_size=geo[0],
+                                   page_stride=geo[1], head_stride=geo[2], token_stride=geo[3],
+                                   num_kv_heads=Hkv, L_max=Lm, causal=causal)
+        Od, ld = impl.attend(q, k, v, lens, 0.7, causal)
+        _close(O, Od, what=f"paged case {c} O"); _close(lse, ld, what=f"paged case {c} lse")
+
+
+# ----------------------------------------------------------------------------
+# Row energies F(zeta) of a decode call
+# ----------------------------------------------------------------------------
+def pin_energy_rows(impl, seed: int = 29):
+    rng = np.random.default_rng(seed)
+    B, q_len, Hkv, G, D, Lm = 3, 2, 2, 3, 5, 17
+    q = rng.standard_normal((B, q_len, Hkv * G, D)); k = rng.standard_normal((B, Hkv, Lm, D))
+    v = rng.standard_normal((B, Hkv, Lm, D)); lens = np.array([17, 2, 9]); sc = 0.6
+    _, lse = impl.attend(q, k, v, lens, sc, True)
+    F0 = impl.energy_rows(q, k, v, lens, sc, np.zeros(q.shape), True)
+    _close(F0, lse, what="F(0) = lse for every row")
+    # Constant values u per KV head: F(zeta) = lse + zeta . u
+    u = rng.standard_normal((B, Hkv, D))
+    vc = np.repeat(u[:, :, None, :], Lm, axis=2)
+    zeta = rng.standard_normal(q.shape)
+    Fz = impl.energy_rows(q, k, vc, lens, sc, zeta, True)
+    want = lse + np.einsum("bihd,bhd->bih", zeta, np.repeat(u, G, axis=1))
+    _close(Fz, want, rtol=1e-12, atol=1e-12, what="F(zeta) with constant V")
+    # One visible key per row: F(zeta) = scale q.k_0 + zeta.v_0
+    l1 = np.array([1, 1, 1])
+    F1 = impl.energy_rows(q[:, :1], k, v, l1, sc, zeta[:, :1], False)
+    for b in range(B):
+        for h in range(Hkv * G):
+            s0 = sc * float(q[b, 0, h] @ k[b, h // G, 0]) + float(zeta[b, 0, h] @ v[b, h // G, 0])
+            _close(F1[b, 0, h], s0, what="single-key F(zeta)")
+
+
 ALL_PINS = [pin_golden, pin_brute_force, pin_library, pin_closed_forms, pin_invariants,
-            pin_causal_truncation, pin_energy_gradient, pin_chunk_merge, pin_bifurcated]
+            pin_causal_truncation, pin_energy_gradient, pin_chunk_merge, pin_bifurcated,
+            pin_paged_golden, pin_paged_scatter, pin_energy_rows]

@@ -2,6 +2,7 @@
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from long_context_exact_split_amd import inputs
@@ -84,3 +85,37 @@ def test_bifurcated_shapes():
     w = inputs.bifurcated_prefix(S=4, Lp=300, Ls=40)
     assert w.q.shape == (4, 32, 128) and w.kp.shape == (8, 300, 128)
     assert w.ks.shape == (4, 8, 40, 128) and w.scale == 1 / math.sqrt(128)
+
+
+@pytest.mark.parametrize("layout", ["head_major", "token_major"])
+def test_page_cache_resolves_to_the_dense_cache(layout):
+    import oracle
+    w = inputs.make_decode("t", 12, B=3, q_len=1, Hq=4, Hkv=2, D=8, L_max=70,
+                           kv_lens=[70, 0, 33])
+    pc = inputs.page_cache(w, 16, layout=layout, seed=1, spare_pages=5)
+    assert pc.num_pages == 5 + 3 + 5 and pc.pages_per_seq == 5
+    t = pc.block_table
+    assert (t[1] == -1).all() and (t[2, 3:] == -1).all() and (t[0] >= 0).all()
+    used = t[t >= 0]
+    assert len(set(used.tolist())) == used.size  # no page stored twice
+    dense = oracle.gather(pc.k_pool, t, w.kv_lens, pc.page_size, pc.page_stride, pc.head_stride,
+                          pc.token_stride, w.Hkv, w.D, w.L_max)
+    for b, L in enumerate(w.kv_lens):
+        assert np.array_equal(dense[b, :, :L], w.k[b, :, :L])
+    spare = np.setdiff1d(np.arange(pc.num_pages), used)
+    pool = pc.k_pool.reshape(pc.num_pages, -1)
+    assert (pool[spare] == inputs.BF16_NAN).all()
+
+
+def test_page_cache_shares_prefix_pages():
+    import oracle
+    w = inputs.make_decode("t", 13, B=3, q_len=1, Hq=2, Hkv=1, D=8, L_max=64, kv_lens=[64, 40, 50])
+    pc = inputs.page_cache(w, 8, share_prefix_tokens=20, seed=2)
+    assert pc.shared_pages == 2
+    t = pc.block_table
+    assert (t[1, :2] == t[0, :2]).all() and (t[2, :2] == t[0, :2]).all()
+    assert np.array_equal(w.k[1, :, :20], w.k[0, :, :20])  # the logical caches now share tokens
+    dense = oracle.gather(pc.v_pool, t, w.kv_lens, 8, pc.page_stride, pc.head_stride,
+                          pc.token_stride, 1, 8, 64)
+    for b, L in enumerate(w.kv_lens):
+        assert np.array_equal(dense[b, :, :L], w.v[b, :, :L])

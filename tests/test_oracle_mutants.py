@@ -1,8 +1,10 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the pins
 catch every one of them: a dropped scale, a wrong GQA index, an off-by-one
 causal window, K and V swapped, a log2 logsumexp, a missing normalisation,
-an unshifted exponential, a merge that forgets to rescale, and an energy that
-drops its zeta term.  None of these variants is used anywhere else."""
+an unshifted exponential, a merge that forgets to rescale, an energy that
+drops its zeta term, paged-cache lookups with swapped strides, an ignored
+block table or quotient and remainder exchanged, and row energies that ignore
+the causal window or the GQA grouping.  None of these variants is used anywhere else."""
 import math
 import types
 
@@ -106,18 +108,71 @@ def _bif_factory(attend):
     return attend_bifurcated
 
 
+def _gather_factory(mistake):
+    def gather(pool, table, kv_lens, P, ps, hs, ts, Hkv, D, L_max):
+        pool = np.asarray(pool).reshape(-1)
+        if mistake == "page_strides_swapped":
+            hs, ts = ts, hs
+        B = len(kv_lens)
+        out = np.full((B, Hkv, L_max, D), np.nan)
+        for b in range(B):
+            for t in range(int(kv_lens[b])):
+                j, slot = t // P, t % P
+                if mistake == "page_quotient_remainder_swapped":
+                    j, slot = slot % np.shape(table)[1], j % P
+                page = b * np.shape(table)[1] + j if mistake == "page_ignores_table" else table[b][j]
+                for h in range(Hkv):
+                    r = page * ps + h * hs + slot * ts
+                    out[b, h, t] = pool[r:r + D]
+        return out
+    return gather
+
+
+def _attend_paged_factory(attend, gather):
+    def attend_paged(q, k_pool, v_pool, table, kv_lens, scale, *, page_size, page_stride,
+                     head_stride, token_stride, num_kv_heads, L_max, causal=False, rows=None):
+        geo = (page_size, page_stride, head_stride, token_stride, num_kv_heads, q.shape[-1], L_max)
+        k = gather(k_pool, table, kv_lens, *geo)
+        v = None if v_pool is None else gather(v_pool, table, kv_lens, *geo)
+        return attend(q, k, v, kv_lens, scale, causal)
+    return attend_paged
+
+
+def _energy_rows_factory(energy, mistake):
+    def energy_rows(q, k, v, kv_lens, scale, zeta, causal=False, rows=None):
+        B, q_len, Hq, D = q.shape
+        Hkv = k.shape[1]
+        out = np.zeros((B, q_len, Hq))
+        for b in range(B):
+            for i in range(q_len):
+                Lb = int(kv_lens[b])
+                n = Lb if mistake == "energy_rows_no_causal" else oracle.visible(Lb, q_len, i, causal)
+                for h in range(Hq):
+                    kvh = h % Hkv if mistake == "energy_rows_gqa_modulo" else h // (Hq // Hkv)
+                    out[b, i, h] = energy(q[b, i, h], k[b, kvh, :n], v[b, kvh, :n], scale, zeta[b, i, h])
+        return out
+    return energy_rows
+
+
 ATTEND_MISTAKES = ["no_scale", "sign", "kv_swapped", "gqa_modulo", "causal_off_by_one",
                    "causal_ignored", "lse_log2", "lse_drops_max", "unnormalised", "no_max_shift"]
 MERGE_MISTAKES = ["merge_no_rescale_o", "merge_inverted_weight"]
 ENERGY_MISTAKES = ["energy_no_zeta", "energy_scaled_zeta"]
+PAGING_MISTAKES = ["page_strides_swapped", "page_quotient_remainder_swapped", "page_ignores_table"]
+ENERGY_ROWS_MISTAKES = ["energy_rows_no_causal", "energy_rows_gqa_modulo"]
 
 
 def _impl(mistake):
     att = _attend_factory(mistake if mistake in ATTEND_MISTAKES else None)
+    gather = _gather_factory(mistake)
+    energy = _energy_factory(mistake)
     return types.SimpleNamespace(
         attend=att,
         attend_bifurcated=_bif_factory(att),
-        energy=_energy_factory(mistake),
+        gather=gather,
+        attend_paged=_attend_paged_factory(att, gather),
+        energy=energy,
+        energy_rows=_energy_rows_factory(energy, mistake),
         chunk_partial=oracle.chunk_partial,
         merge=_merge_factory(mistake),
         finalize=oracle.finalize,
@@ -132,7 +187,8 @@ def test_faithful_variant_passes_all_pins():
         pin(impl)
 
 
-@pytest.mark.parametrize("mistake", ATTEND_MISTAKES + MERGE_MISTAKES + ENERGY_MISTAKES)
+@pytest.mark.parametrize("mistake", ATTEND_MISTAKES + MERGE_MISTAKES + ENERGY_MISTAKES +
+                         PAGING_MISTAKES + ENERGY_ROWS_MISTAKES)
 def test_pins_catch_planted_mistake(mistake):
     impl = _impl(mistake)
     caught = []
