@@ -33,6 +33,17 @@ WORKLOADS = {
     "llama31_70b_ragged": "Llama-3.1-70B-shaped ragged decode (B=16, 4 causal query tokens)",
     "single_query_fp32": "single-query fp32 decode (L=4096, 8 chunks)",
     "bifurcated_prefix": "bifurcated shared-prefix sampling (64 samples, 16384 + 512 tokens)",
+    "long_context_1m_energy": "long-context GQA energy only, lse from K (1M tokens)",
+    "long_context_1m_zeta": "long-context GQA energy F(zeta) from K and V (1M tokens)",
+    "paged_long_context_1m": "long-context GQA decode (1M tokens) in 16-token head-major pages",
+    "paged_llama31_70b_ragged": "Llama-3.1-70B-shaped ragged decode in 16-token token-major pages",
+}
+# Workloads that reuse another one's inputs: name -> (inputs of, call mode, paging)
+VARIANTS = {
+    "long_context_1m_energy": ("long_context_1m", "energy", None),
+    "long_context_1m_zeta": ("long_context_1m", "zeta", None),
+    "paged_long_context_1m": ("long_context_1m", "full", (16, "head_major")),
+    "paged_llama31_70b_ragged": ("llama31_70b_ragged", "full", (16, "token_major")),
 }
 KERNEL_SOURCES = ("long_context_exact_split_amd/csrc/split_kv_valu.hip",
                   "long_context_exact_split_amd/csrc/device_common.h",
@@ -125,6 +136,8 @@ def cpu_threads():
 # ----------------------------------------------------------------------------
 def make_workload(name):
     from long_context_exact_split_amd import inputs
+    if name in VARIANTS:
+        return make_workload(VARIANTS[name][0])
     if name == "long_context_1m":
         return inputs.long_context_gqa(L=1 << 20, seed=31)
     if name == "long_context_5m":
@@ -148,37 +161,84 @@ def dev(torch, a):
 
 
 class DecodeRunner:
-    """One decode call split into its two launches (split kernel, merge)."""
+    """One decode call split into its two launches (split kernel, merge).
 
-    def __init__(self, torch, w):
+    mode "full": O and lse; "energy": lse from K alone; "zeta": the energy
+    F(zeta) from K and V, one call (split + merge, timed together).  paging
+    (P, layout): the cache is scattered into P-token pages in a seeded random
+    physical order first (outside the timed region)."""
+
+    def __init__(self, torch, w, mode="full", paging=None):
         import numpy as np
-        from long_context_exact_split_amd import binding
-        self.w = w
-        q, k, v = dev(torch, w.q), dev(torch, w.k), dev(torch, w.v)
+        from long_context_exact_split_amd import binding, inputs
+        self.w, self.mode, self.binding = w, mode, binding
+        self.pc = None
+        q = dev(torch, w.q)
         lens = None
-        if not (w.kv_lens == w.L_max).all():
+        if not (w.kv_lens == w.L_max).all() or paging is not None:
             lens = torch.from_numpy(w.kv_lens.astype(np.int32)).cuda()
-        self.ph = binding.Phases(q, k, v, lens, scale=w.scale, causal=w.causal,
-                                 chunk_len=w.chunk_len)
-        self.plan = self.ph.plan
+        paged = None
+        if paging is not None:
+            P, layout = paging
+            self.pc = inputs.page_cache(w, P, layout=layout, seed=11)
+            shape = ((self.pc.num_pages, w.Hkv, P, w.D) if layout == "head_major"
+                     else (self.pc.num_pages, P, w.Hkv, w.D))
+            k = dev(torch, self.pc.k_pool.reshape(shape))
+            v = dev(torch, self.pc.v_pool.reshape(shape))
+            table = torch.from_numpy(self.pc.block_table).cuda()
+            paged = binding.PagedCache(k, v, table, layout=layout, max_kv_len=w.L_max)
+        else:
+            k, v = dev(torch, w.k), dev(torch, w.v)
+        self.q, self.k, self.v, self.lens = q, k, v, lens
+        if mode == "zeta":
+            rng = np.random.default_rng(17)
+            z = rng.standard_normal(w.q.shape).astype(np.float32) * np.float32(0.25)
+            if w.dtype == "bf16":
+                z = inputs.bf16_to_f32(inputs.f32_to_bf16(z))  # the values the GPU sees
+            self.zeta_host = z
+            self.zeta = dev(torch, inputs.f32_to_bf16(z) if w.dtype == "bf16" else z)
+            self.lse = torch.empty(w.q.shape[:3], dtype=torch.float32, device="cuda")
+            desc = binding.make_desc(batch=w.B, q_len=w.q_len, num_q_heads=w.Hq,
+                                     num_kv_heads=w.Hkv, head_dim=w.D, max_kv_len=w.L_max)
+            self.ws = torch.empty(max(1, binding.workspace_bytes(desc)), dtype=torch.uint8,
+                                  device="cuda")
+            self.plan = binding.plan(desc)
+            self.plan["kernel"] = 0  # F(zeta) always runs on the vector-ALU kernel
+        else:
+            self.ph = binding.Phases(q, k, None if mode == "energy" else v, lens, scale=w.scale,
+                                     causal=w.causal, chunk_len=w.chunk_len, paged=paged)
+            self.plan = self.ph.plan
         esz = 2 if w.dtype == "bf16" else 4
         self.kv_tokens = int(w.kv_lens.sum())
-        self.kv_bytes = 2 * self.kv_tokens * w.Hkv * w.D * esz
-        self.q_bytes = w.B * w.q_len * w.Hq * w.D * esz
-        self.out_bytes = w.B * w.q_len * w.Hq * (w.D + 1) * 4
+        tensors = 1 if mode == "energy" else 2
+        self.kv_bytes = tensors * self.kv_tokens * w.Hkv * w.D * esz
+        self.q_bytes = w.B * w.q_len * w.Hq * w.D * esz * (2 if mode == "zeta" else 1)
+        self.out_bytes = w.B * w.q_len * w.Hq * ((w.D + 1) if mode == "full" else 1) * 4
         rows = w.G * w.q_len
-        self.flops = 4 * rows * w.D * self.kv_tokens * w.Hkv
-        self.kernel = ("split_kv_mfma" if self.plan["kernel"] == 1 else "split_kv_valu") + \
-            f"<{w.dtype},{w.D},rows={self.plan['rows_per_block']}>"
+        self.flops = 2 * tensors * rows * w.D * self.kv_tokens * w.Hkv
+        name = {0: "split_kv_valu", 1: "split_kv_mfma", 2: "split_kv_mfma_rows"}[self.plan["kernel"]]
+        self.kernel = f"{name}<{w.dtype},{w.D},rows={self.plan['rows_per_block']}" + \
+            ("" if mode == "full" else f",{mode}") + \
+            ("" if paging is None else f",pages={paging[0]} {paging[1]}") + ">" + \
+            (" + merge (one call)" if mode == "zeta" else "")
 
     def first(self):
-        self.ph.partials()
+        if self.mode == "zeta":
+            w = self.w
+            self.binding.decode_energy_zeta(self.q, self.k, self.v, self.zeta, self.lens,
+                                            scale=w.scale, causal=w.causal, lse=self.lse,
+                                            workspace=self.ws)
+        else:
+            self.ph.partials()
 
     def second(self):
-        self.ph.merge()
+        if self.mode != "zeta":
+            self.ph.merge()
 
     def outputs(self):
-        return self.ph.out.cpu().numpy(), self.ph.lse.cpu().numpy()
+        if self.mode == "zeta":
+            return None, self.lse.cpu().numpy()
+        return (None if self.ph.out is None else self.ph.out.cpu().numpy()), self.ph.lse.cpu().numpy()
 
     def oracle_rows(self, n_rows):
         w = self.w
@@ -189,7 +249,18 @@ class DecodeRunner:
     def oracle(self, rows):
         import oracle
         w = self.w
-        return oracle.attend(w.q, w.k, w.v, w.kv_lens, w.scale, w.causal, rows=rows)
+        if self.mode == "zeta":
+            return None, oracle.energy_rows(w.q, w.k, w.v, w.kv_lens, w.scale, self.zeta_host,
+                                            w.causal, rows=rows)
+        v = None if self.mode == "energy" else w.v
+        if self.pc is not None:
+            pc = self.pc
+            return oracle.attend_paged(w.q, pc.k_pool, pc.v_pool, pc.block_table, w.kv_lens,
+                                       w.scale, page_size=pc.page_size,
+                                       page_stride=pc.page_stride, head_stride=pc.head_stride,
+                                       token_stride=pc.token_stride, num_kv_heads=w.Hkv,
+                                       L_max=w.L_max, causal=w.causal, rows=rows)
+        return oracle.attend(w.q, w.k, v, w.kv_lens, w.scale, w.causal, rows=rows)
 
 
 class BifurcatedRunner:
@@ -250,11 +321,11 @@ def cpu_baseline(run, n_rows, O_gpu, lse_gpu):
     Or, lr = run.oracle(rows)
     dt = time.perf_counter() - t0
     idx = tuple(np.array(rows).T)
-    dO = float(np.abs(O_gpu[idx] - Or[idx]).max())
+    dO = float(np.abs(O_gpu[idx] - Or[idx]).max()) if O_gpu is not None and Or is not None else None
     fin = np.isfinite(lr[idx])
     dl = float((np.abs(lse_gpu[idx][fin] - lr[idx][fin]) /
                 np.maximum(1.0, np.abs(lr[idx][fin]))).max()) if fin.any() else 0.0
-    total_rows = O_gpu.shape[0] * O_gpu.shape[1] * O_gpu.shape[2]
+    total_rows = lse_gpu.shape[0] * lse_gpu.shape[1] * lse_gpu.shape[2]
     frac = len(rows) / total_rows
     return {"value": run.kv_tokens * frac / dt, "unit": "KV tokens/s", "cores": int(cpu_threads()),
             "kind": "oracle",
@@ -279,7 +350,11 @@ def main():
     w = make_workload(args.workload)
     print(f"# generated {args.workload} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
-    run = (BifurcatedRunner if args.workload == "bifurcated_prefix" else DecodeRunner)(torch, w)
+    if args.workload == "bifurcated_prefix":
+        run = BifurcatedRunner(torch, w)
+    else:
+        _, mode, paging = VARIANTS.get(args.workload, (None, "full", None))
+        run = DecodeRunner(torch, w, mode, paging)
     print(f"# plan {run.plan}", file=sys.stderr, flush=True)
 
     # Untimed warm-up: at least --warmup steps and --min-warmup-s seconds.  From

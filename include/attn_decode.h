@@ -67,7 +67,8 @@ typedef enum {
   ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returned     */
   ATTN_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed          */
   ATTN_ERR_UNSUPPORTED = 7, /* head_dim other than 64 or 128, or a shape the kernels do not cover */
-  ATTN_ERR_VALUE = 8        /* non-finite scale, or chunk_len not a positive multiple of 64 */
+  ATTN_ERR_VALUE = 8        /* non-finite scale, chunk_len not a multiple of 64, or a bad */
+                            /* paging description (page size, strides, table extent)     */
 } attn_status_t;
 
 typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype_t;
@@ -118,8 +119,9 @@ typedef struct {
  * when cu_count > 0. */
 attn_status_t attn_decode_plan(const attn_desc_t *desc, int32_t cu_count, attn_plan_t *plan);
 
-/* Bytes of device workspace attn_decode / attn_decode_energy need for `desc`
- * on the current device (0 is possible for an empty call). */
+/* Bytes of device workspace that attn_decode, attn_decode_energy,
+ * attn_decode_energy_zeta and the paged variants need for `desc` on the
+ * current device (0 is possible for an empty call). */
 attn_status_t attn_workspace_bytes(const attn_desc_t *desc, size_t *bytes);
 
 /* lse only: the energy F at zeta = 0, i.e. the logsumexp of every row, read
@@ -164,6 +166,65 @@ attn_status_t attn_decode_partials(const attn_desc_t *desc, const void *q, const
                                    void *stream);
 attn_status_t attn_decode_merge(const attn_desc_t *desc, float *o, float *lse, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/* Energy at a given zeta (Tree Attention article, "an energy view of
+ * attention"): for every row, with the row's auxiliary vector zeta,
+ *     F(zeta) = ln sum_t exp(scale * q . k_t + zeta . v_t)
+ * over the row's visible keys.  F(0) is the row's lse, and the gradient of F
+ * in zeta at 0 is the row's attention output O, so central differences of
+ * this call reproduce attn_decode's O.  zeta: [B][q_len][Hq][D], element
+ * type and alignment of q.  lse receives F(zeta), float32 [B][q_len][Hq].
+ * Runs on the vector-ALU kernel for every row count; dense caches only. */
+attn_status_t attn_decode_energy_zeta(const attn_desc_t *desc, const void *q, const void *k,
+                                      const void *v, const void *zeta, float *lse,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Paged KV caches ("attention acceleration" concept page, section 3,
+ * PagedAttention): K and V live in pools of fixed-size pages of P tokens; a
+ * block table maps logical page j of sequence b (tokens [jP, (j+1)P)) to a
+ * physical page.  Pages need not be contiguous or in order, and several
+ * sequences may map the same page (a shared prompt prefix).  Element e of
+ * the row of token t, KV head kvh, sequence b is
+ *     pool[block_table[b * pages_per_seq + t / P] * page_stride
+ *          + kvh * head_stride + (t % P) * token_stride + e].
+ * Two common layouts: head-major pages [num_pages][Hkv][P][D]
+ * (page_stride = Hkv*P*D, head_stride = P*D, token_stride = D) and
+ * token-major pages [num_pages][P][Hkv][D] (P*Hkv*D, D, Hkv*D).
+ *   block_table     device int32 [B][pages_per_seq]; only the entries of pages
+ *                   that hold tokens t < kv_lens[b] are read; an entry outside
+ *                   [0, num_pages) is read as page 0 (memory-safe, result
+ *                   unspecified)
+ *   pages_per_seq   >= 1 and pages_per_seq * P >= max_kv_len
+ *   page_size       P, a power of two in [1, 2^20]
+ *   num_pages       pages in each pool (>= 1 when any token is cached)
+ *   strides         in elements, >= 0, each a multiple of 16 bytes; D
+ *                   consecutive elements per row; num_pages * page_stride
+ *                   below 2^48
+ * Everything else (descriptor, q, outputs, workspace, errors) is as for the
+ * dense entry points; desc->max_kv_len is the logical extent of the token
+ * axis.  Identical results to the dense call on the cache the table
+ * describes: paging changes where rows are read, not the arithmetic. */
+typedef struct {
+  const int32_t *block_table;
+  int32_t pages_per_seq;
+  int32_t page_size;
+  int64_t num_pages;
+  int64_t page_stride;
+  int64_t head_stride;
+  int64_t token_stride;
+} attn_paged_kv_t;
+
+attn_status_t attn_decode_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+                                const void *q, const void *k_pool, const void *v_pool, float *o,
+                                float *lse, void *workspace, size_t workspace_bytes, void *stream);
+attn_status_t attn_decode_energy_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+                                       const void *q, const void *k_pool, float *lse,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+/* The split phase alone on a paged cache (records as attn_decode_partials;
+ * attn_decode_merge then finishes the call). */
+attn_status_t attn_decode_partials_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+                                         const void *q, const void *k_pool, const void *v_pool,
+                                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Shared-prefix batch sampling (Bifurcated Attention, TL;DR): S samples of
  * one query token each attend over one shared prefix KV followed by their

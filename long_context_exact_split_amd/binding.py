@@ -22,8 +22,9 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DT
           4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP",
           7: "ATTN_ERR_UNSUPPORTED", 8: "ATTN_ERR_VALUE"}
 EXPORTS = ("attn_decode_plan", "attn_workspace_bytes", "attn_decode_energy", "attn_decode",
-           "attn_decode_partials", "attn_decode_merge", "attn_bifurcated_workspace_bytes",
-           "attn_decode_bifurcated", "attn_status_string")
+           "attn_decode_partials", "attn_decode_merge", "attn_decode_energy_zeta",
+           "attn_decode_paged", "attn_decode_energy_paged", "attn_decode_partials_paged",
+           "attn_bifurcated_workspace_bytes", "attn_decode_bifurcated", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -63,6 +64,13 @@ class AttnBifDesc(ctypes.Structure):
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
 
 
+class AttnPagedKv(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("pages_per_seq", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+                ("page_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("token_stride", ctypes.c_int64)]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -93,6 +101,14 @@ def load_library():
                                              c.c_void_p, c.c_size_t, c.c_void_p]
         lib.attn_decode_merge.argtypes = [P(AttnDesc), c.c_void_p, c.c_void_p, c.c_void_p,
                                           c.c_size_t, c.c_void_p]
+        lib.attn_decode_energy_zeta.argtypes = [P(AttnDesc)] + [c.c_void_p] * 6 + [
+            c.c_size_t, c.c_void_p]
+        lib.attn_decode_paged.argtypes = [P(AttnDesc), P(AttnPagedKv)] + [c.c_void_p] * 6 + [
+            c.c_size_t, c.c_void_p]
+        lib.attn_decode_energy_paged.argtypes = [P(AttnDesc), P(AttnPagedKv)] + [
+            c.c_void_p] * 4 + [c.c_size_t, c.c_void_p]
+        lib.attn_decode_partials_paged.argtypes = [P(AttnDesc), P(AttnPagedKv)] + [
+            c.c_void_p] * 4 + [c.c_size_t, c.c_void_p]
         lib.attn_bifurcated_workspace_bytes.argtypes = [P(AttnBifDesc), P(c.c_size_t)]
         lib.attn_decode_bifurcated.argtypes = [P(AttnBifDesc)] + [c.c_void_p] * 8 + [
             c.c_size_t, c.c_void_p]
@@ -261,16 +277,24 @@ def decode(q, k, v, kv_lens=None, *, scale: Optional[float] = None, causal: bool
 class Phases:
     """The two phases of one decode call on fixed buffers: ``partials()``
     launches the split-KV kernel (records into the workspace), ``merge()``
-    the merge + normalisation.  Used to time the kernels separately."""
+    the merge + normalisation.  Used to time the kernels separately.  With
+    ``v`` None the call is energy only (lse, no O).  With ``paged`` (a
+    ``PagedCache``) k and v are its pools."""
 
-    def __init__(self, q, k, v, kv_lens=None, *, scale=None, causal=False, chunk_len=0):
+    def __init__(self, q, k, v, kv_lens=None, *, scale=None, causal=False, chunk_len=0,
+                 paged=None):
         torch = _torch()
         self.lib = load_library()
         _check_tensors(q, k, v)
-        self.desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
+        self.paged = paged
+        if paged is None:
+            self.desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
+        else:
+            self.desc = _paged_desc(q, paged, kv_lens, scale, causal, chunk_len)
         B, q_len, Hq, D = q.shape
         self.q, self.k, self.v, self.kv_lens = q, k, v, kv_lens
-        self.out = torch.empty((B, q_len, Hq, D), dtype=torch.float32, device=q.device)
+        self.out = (None if v is None else
+                    torch.empty((B, q_len, Hq, D), dtype=torch.float32, device=q.device))
         self.lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
         self.ws = _workspace(workspace_bytes(self.desc), q.device, None)
         self.nbytes = 0 if self.ws is None else self.ws.numel()
@@ -278,6 +302,12 @@ class Phases:
         self.stream = _stream_ptr(q.device)
 
     def partials(self):
+        if self.paged is not None:
+            _check(self.lib.attn_decode_partials_paged(
+                ctypes.byref(self.desc), ctypes.byref(self.paged.kv), _ptr(self.q), _ptr(self.k),
+                _ptr(self.v), _ptr(self.ws), self.nbytes, self.stream),
+                "attn_decode_partials_paged")
+            return
         _check(self.lib.attn_decode_partials(ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k),
                                              _ptr(self.v), _ptr(self.ws), self.nbytes,
                                              self.stream), "attn_decode_partials")
@@ -303,6 +333,117 @@ def decode_energy(q, k, kv_lens=None, *, scale: Optional[float] = None, causal: 
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(lib.attn_decode_energy(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(ws),
                                       nbytes, _stream_ptr(q.device)), "attn_decode_energy")
+    return lse
+
+
+def decode_energy_zeta(q, k, v, zeta, kv_lens=None, *, scale: Optional[float] = None,
+                       causal: bool = False, chunk_len: int = 0, lse=None, workspace=None):
+    """F(zeta) = ln sum_t exp(scale q.k_t + zeta.v_t) per row: float32 [B, q_len, Hq].
+    ``zeta`` has the shape and dtype of ``q``."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensors(q, k, v, zeta)
+    if v.shape != k.shape or zeta.shape != q.shape:
+        raise ValueError("v must have the shape of k and zeta the shape of q")
+    desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
+    B, q_len, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        if lse is None:
+            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        ws = _workspace(workspace_bytes(desc), q.device, workspace)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib.attn_decode_energy_zeta(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(zeta), _ptr(lse), _ptr(ws), nbytes,
+                                           _stream_ptr(q.device)), "attn_decode_energy_zeta")
+    return lse
+
+
+# ----------------------------------------------------------------------------
+# Paged KV caches
+# ----------------------------------------------------------------------------
+class PagedCache:
+    """K/V pools of fixed-size pages plus a block table (device tensors).
+
+    ``layout`` "head_major": pools [num_pages, Hkv, P, D]; "token_major":
+    [num_pages, P, Hkv, D].  ``block_table``: int32 [B, pages_per_seq].
+    ``max_kv_len`` defaults to pages_per_seq * P."""
+
+    def __init__(self, k_pool, v_pool, block_table, *, layout="head_major", max_kv_len=None):
+        torch = _torch()
+        if layout not in ("head_major", "token_major"):
+            raise ValueError("layout must be 'head_major' or 'token_major'")
+        if k_pool.dim() != 4 or (v_pool is not None and v_pool.shape != k_pool.shape):
+            raise ValueError("pools must be 4-d and of one shape")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2:
+            raise ValueError("block_table must be int32 [B, pages_per_seq]")
+        if not block_table.is_contiguous() or block_table.device != k_pool.device:
+            raise ValueError("block_table must be contiguous and on the pools' device")
+        n, a, b, D = k_pool.shape
+        Hkv, P = (a, b) if layout == "head_major" else (b, a)
+        self.k_pool, self.v_pool, self.block_table = k_pool, v_pool, block_table
+        self.layout, self.num_kv_heads, self.page_size, self.head_dim = layout, Hkv, P, D
+        self.pages_per_seq = block_table.shape[1]
+        self.max_kv_len = self.pages_per_seq * P if max_kv_len is None else int(max_kv_len)
+        kv = AttnPagedKv()
+        kv.block_table = _ptr(block_table) or None
+        kv.pages_per_seq, kv.page_size, kv.num_pages = self.pages_per_seq, P, n
+        kv.page_stride = Hkv * P * D
+        kv.head_stride, kv.token_stride = (P * D, D) if layout == "head_major" else (D, Hkv * D)
+        self.kv = kv
+
+
+def _paged_desc(q, paged: PagedCache, kv_lens, scale, causal, chunk_len) -> AttnDesc:
+    if q.dim() != 4 or q.shape[3] != paged.head_dim:
+        raise ValueError("q must be [B, q_len, Hq, D] with the pools' D")
+    B, q_len, Hq, D = q.shape
+    if paged.block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    if kv_lens is not None:
+        torch = _torch()
+        if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
+            raise ValueError("kv_lens must be int32[B] on the device of q")
+    return make_desc(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=paged.num_kv_heads,
+                     head_dim=D, max_kv_len=paged.max_kv_len, kv_lens_ptr=_ptr(kv_lens),
+                     scale=scale, causal=causal, chunk_len=chunk_len, dtype=_dtype_code(q))
+
+
+def decode_paged(q, paged: PagedCache, kv_lens=None, *, scale: Optional[float] = None,
+                 causal: bool = False, chunk_len: int = 0, out=None, lse=None, workspace=None):
+    """Exact attention decode over a paged cache: (O float32 [B,q_len,Hq,D], lse)."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensors(q, paged.k_pool, paged.v_pool)
+    desc = _paged_desc(q, paged, kv_lens, scale, causal, chunk_len)
+    B, q_len, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty((B, q_len, Hq, D), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        ws = _workspace(workspace_bytes(desc), q.device, workspace)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib.attn_decode_paged(ctypes.byref(desc), ctypes.byref(paged.kv), _ptr(q),
+                                     _ptr(paged.k_pool), _ptr(paged.v_pool), _ptr(out), _ptr(lse),
+                                     _ptr(ws), nbytes, _stream_ptr(q.device)), "attn_decode_paged")
+    return out, lse
+
+
+def decode_energy_paged(q, paged: PagedCache, kv_lens=None, *, scale: Optional[float] = None,
+                        causal: bool = False, chunk_len: int = 0, lse=None, workspace=None):
+    """Energy only over a paged cache (reads the K pool): lse float32 [B, q_len, Hq]."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensors(q, paged.k_pool)
+    desc = _paged_desc(q, paged, kv_lens, scale, causal, chunk_len)
+    B, q_len, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        if lse is None:
+            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        ws = _workspace(workspace_bytes(desc), q.device, workspace)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib.attn_decode_energy_paged(ctypes.byref(desc), ctypes.byref(paged.kv), _ptr(q),
+                                            _ptr(paged.k_pool), _ptr(lse), _ptr(ws), nbytes,
+                                            _stream_ptr(q.device)), "attn_decode_energy_paged")
     return lse
 
 

@@ -58,11 +58,14 @@ PartialLayout carve(char *base, const attn_plan_t &p, int head_dim) {
 }
 
 SplitArgs split_args(const attn_desc_t *d, const attn_plan_t &p, const void *q, const void *k,
-                     const void *v, const PartialLayout &part) {
+                     const void *v, const void *zeta, const KvPaging &pg,
+                     const PartialLayout &part) {
   SplitArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
+  a.zeta = zeta;
+  a.pg = pg;
   a.map = work_map(d, p);
   a.part = part;
   a.q_len = d->q_len;
@@ -75,15 +78,33 @@ SplitArgs split_args(const attn_desc_t *d, const attn_plan_t &p, const void *q, 
 }
 
 hipError_t launch_split(const attn_desc_t *d, const attn_plan_t &p, const SplitArgs &a,
-                        bool energy, hipStream_t s) {
+                        SplitMode mode, hipStream_t s) {
   if (p.work_items <= 0) return hipSuccess;
-  if (p.kernel >= 1) return launch_split_mfma(p, a, d->head_dim, energy, s);
-  return launch_split_valu(p, a, d->dtype, d->head_dim, energy, s);
+  if (p.kernel >= 1) {
+    if (mode == SplitMode::kEnergyZeta) return hipErrorInvalidValue;
+    return launch_split_mfma(p, a, d->head_dim, mode == SplitMode::kEnergy, s);
+  }
+  return launch_split_valu(p, a, d->dtype, d->head_dim, mode, s);
+}
+
+// The energy at a given zeta runs on the vector-ALU kernel for every shape;
+// everything else may use the MFMA kernels.
+bool mfma_for(SplitMode mode) { return kMfma && mode != SplitMode::kEnergyZeta; }
+
+// Workspace every decode entry point accepts for a descriptor: the larger of
+// the two plans' record areas.
+attn_status_t workspace_need(const attn_desc_t *d, int cu, size_t *bytes) {
+  attn_plan_t a, b;
+  attn_status_t st;
+  if ((st = make_plan(d, cu, kMfma, &a)) != ATTN_OK) return st;
+  if ((st = make_plan(d, cu, false, &b)) != ATTN_OK) return st;
+  *bytes = a.workspace_bytes > b.workspace_bytes ? a.workspace_bytes : b.workspace_bytes;
+  return ATTN_OK;
 }
 
 // Shared preamble of the decode entry points: validate, plan, check the
 // workspace.  Returns ATTN_OK with *empty set when there is nothing to do.
-attn_status_t prepare(const attn_desc_t *d, void *ws, size_t ws_bytes, attn_plan_t *p,
+attn_status_t prepare(const attn_desc_t *d, bool mfma, void *ws, size_t ws_bytes, attn_plan_t *p,
                       PartialLayout *part, bool *empty) {
   *empty = false;
   attn_status_t st = validate_desc(d);
@@ -94,7 +115,7 @@ attn_status_t prepare(const attn_desc_t *d, void *ws, size_t ws_bytes, attn_plan
   }
   int cu = 0;
   if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
-  if ((st = make_plan(d, cu, kMfma, p)) != ATTN_OK) return st;
+  if ((st = make_plan(d, cu, mfma, p)) != ATTN_OK) return st;
   if (p->workspace_bytes > 0 && !ws) return ATTN_ERR_NULL;
   if (ws_bytes < p->workspace_bytes) return ATTN_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return ATTN_ERR_ALIGN;
@@ -121,26 +142,32 @@ attn_status_t check_outputs(const attn_desc_t *d, const float *o, const float *l
   return ATTN_OK;
 }
 
-attn_status_t partials_impl(const attn_desc_t *d, const void *q, const void *k, const void *v,
+// The split phase.  v == null in kFull mode means energy only (the public
+// partials entry points take "no V" as "no o").
+attn_status_t partials_impl(const attn_desc_t *d, const attn_paged_kv_t *paged, const void *q,
+                            const void *k, const void *v, const void *zeta, SplitMode mode,
                             void *ws, size_t ws_bytes, void *stream) {
+  KvPaging pg;
+  attn_status_t st = validate_paged(d, paged, &pg);
+  if (st != ATTN_OK) return st;
   attn_plan_t p;
   PartialLayout part;
   bool empty;
-  attn_status_t st = prepare(d, ws, ws_bytes, &p, &part, &empty);
-  if (st != ATTN_OK || empty) return st;
+  if ((st = prepare(d, mfma_for(mode), ws, ws_bytes, &p, &part, &empty)) != ATTN_OK || empty)
+    return st;
   (void)hipGetLastError();
-  if (launch_split(d, p, split_args(d, p, q, k, v, part), v == nullptr,
+  if (launch_split(d, p, split_args(d, p, q, k, v, zeta, pg, part), mode,
                    static_cast<hipStream_t>(stream)) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
-attn_status_t merge_impl(const attn_desc_t *d, float *o, float *lse, void *ws, size_t ws_bytes,
-                         void *stream) {
+attn_status_t merge_impl(const attn_desc_t *d, bool mfma, float *o, float *lse, void *ws,
+                         size_t ws_bytes, void *stream) {
   attn_plan_t p;
   PartialLayout part;
   bool empty;
-  attn_status_t st = prepare(d, ws, ws_bytes, &p, &part, &empty);
+  attn_status_t st = prepare(d, mfma, ws, ws_bytes, &p, &part, &empty);
   if (st != ATTN_OK || empty) return st;
   MergeArgs m{};
   m.map = work_map(d, p);
@@ -157,15 +184,21 @@ attn_status_t merge_impl(const attn_desc_t *d, float *o, float *lse, void *ws, s
   return ATTN_OK;
 }
 
-attn_status_t decode_impl(const attn_desc_t *d, const void *q, const void *k, const void *v,
-                          float *o, float *lse, void *ws, size_t ws_bytes, void *stream,
-                          bool energy) {
-  attn_status_t st = check_inputs(d, q, k, v, !energy);
+attn_status_t decode_impl(const attn_desc_t *d, const attn_paged_kv_t *paged, const void *q,
+                          const void *k, const void *v, const void *zeta, float *o, float *lse,
+                          void *ws, size_t ws_bytes, void *stream, SplitMode mode) {
+  const bool need_o = mode == SplitMode::kFull;
+  attn_status_t st = check_inputs(d, q, k, v, mode != SplitMode::kEnergy);
   if (st != ATTN_OK) return st;
-  if ((st = check_outputs(d, o, lse, !energy)) != ATTN_OK) return st;
-  if ((st = partials_impl(d, q, k, energy ? nullptr : v, ws, ws_bytes, stream)) != ATTN_OK)
+  if ((st = check_outputs(d, o, lse, need_o)) != ATTN_OK) return st;
+  if (mode == SplitMode::kEnergyZeta) {
+    if (d->batch > 0 && !zeta) return ATTN_ERR_NULL;
+    if (!aligned(zeta, 16)) return ATTN_ERR_ALIGN;
+  }
+  if ((st = partials_impl(d, paged, q, k, need_o || mode == SplitMode::kEnergyZeta ? v : nullptr,
+                          zeta, mode, ws, ws_bytes, stream)) != ATTN_OK)
     return st;
-  return merge_impl(d, energy ? nullptr : o, lse, ws, ws_bytes, stream);
+  return merge_impl(d, mfma_for(mode), need_o ? o : nullptr, lse, ws, ws_bytes, stream);
 }
 
 struct BifPlans {
@@ -210,10 +243,7 @@ attn_status_t attn_workspace_bytes(const attn_desc_t *desc, size_t *bytes) {
     if (desc->batch == 0) return ATTN_OK;
     int cu = 0;
     if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
-    attn_plan_t p;
-    if ((st = make_plan(desc, cu, kMfma, &p)) != ATTN_OK) return st;
-    *bytes = p.workspace_bytes;
-    return ATTN_OK;
+    return workspace_need(desc, cu, bytes);
   } catch (...) {
     return ATTN_ERR_HIP;
   }
@@ -223,8 +253,8 @@ attn_status_t attn_decode_energy(const attn_desc_t *desc, const void *q, const v
                                  float *lse, void *workspace, size_t workspace_bytes,
                                  void *stream) {
   try {
-    return decode_impl(desc, q, k, nullptr, nullptr, lse, workspace, workspace_bytes, stream,
-                       true);
+    return decode_impl(desc, nullptr, q, k, nullptr, nullptr, nullptr, lse, workspace,
+                       workspace_bytes, stream, SplitMode::kEnergy);
   } catch (...) {
     return ATTN_ERR_HIP;
   }
@@ -234,7 +264,8 @@ attn_status_t attn_decode(const attn_desc_t *desc, const void *q, const void *k,
                           float *o, float *lse, void *workspace, size_t workspace_bytes,
                           void *stream) {
   try {
-    return decode_impl(desc, q, k, v, o, lse, workspace, workspace_bytes, stream, false);
+    return decode_impl(desc, nullptr, q, k, v, nullptr, o, lse, workspace, workspace_bytes, stream,
+                       SplitMode::kFull);
   } catch (...) {
     return ATTN_ERR_HIP;
   }
@@ -246,7 +277,9 @@ attn_status_t attn_decode_partials(const attn_desc_t *desc, const void *q, const
   try {
     attn_status_t st = check_inputs(desc, q, k, v, false);
     if (st != ATTN_OK) return st;
-    return partials_impl(desc, q, k, v, workspace, workspace_bytes, stream);
+    return partials_impl(desc, nullptr, q, k, v, nullptr,
+                         v ? SplitMode::kFull : SplitMode::kEnergy, workspace, workspace_bytes,
+                         stream);
   } catch (...) {
     return ATTN_ERR_HIP;
   }
@@ -257,7 +290,58 @@ attn_status_t attn_decode_merge(const attn_desc_t *desc, float *o, float *lse, v
   try {
     attn_status_t st = check_outputs(desc, o, lse, false);
     if (st != ATTN_OK) return st;
-    return merge_impl(desc, o, lse, workspace, workspace_bytes, stream);
+    return merge_impl(desc, kMfma, o, lse, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode_energy_zeta(const attn_desc_t *desc, const void *q, const void *k,
+                                      const void *v, const void *zeta, float *lse,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    return decode_impl(desc, nullptr, q, k, v, zeta, nullptr, lse, workspace, workspace_bytes,
+                       stream, SplitMode::kEnergyZeta);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+                                const void *q, const void *k_pool, const void *v_pool, float *o,
+                                float *lse, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  try {
+    if (!paged) return ATTN_ERR_NULL;
+    return decode_impl(desc, paged, q, k_pool, v_pool, nullptr, o, lse, workspace,
+                       workspace_bytes, stream, SplitMode::kFull);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode_energy_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+                                       const void *q, const void *k_pool, float *lse,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    if (!paged) return ATTN_ERR_NULL;
+    return decode_impl(desc, paged, q, k_pool, nullptr, nullptr, nullptr, lse, workspace,
+                       workspace_bytes, stream, SplitMode::kEnergy);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_decode_partials_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+                                         const void *q, const void *k_pool, const void *v_pool,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    if (!paged) return ATTN_ERR_NULL;
+    attn_status_t st = check_inputs(desc, q, k_pool, v_pool, false);
+    if (st != ATTN_OK) return st;
+    return partials_impl(desc, paged, q, k_pool, v_pool, nullptr,
+                         v_pool ? SplitMode::kFull : SplitMode::kEnergy, workspace,
+                         workspace_bytes, stream);
   } catch (...) {
     return ATTN_ERR_HIP;
   }
@@ -308,11 +392,14 @@ attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const v
     const PartialLayout suf = carve(ws + b.pre_bytes, b.sp, desc->head_dim);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (launch_split(&b.pre, b.pp, split_args(&b.pre, b.pp, q, k_prefix, v_prefix, pre), false,
-                     s) != hipSuccess)
+    const KvPaging dense{};
+    if (launch_split(&b.pre, b.pp,
+                     split_args(&b.pre, b.pp, q, k_prefix, v_prefix, nullptr, dense, pre),
+                     SplitMode::kFull, s) != hipSuccess)
       return ATTN_ERR_HIP;
-    if (launch_split(&b.suf, b.sp, split_args(&b.suf, b.sp, q, k_suffix, v_suffix, suf), false,
-                     s) != hipSuccess)
+    if (launch_split(&b.suf, b.sp,
+                     split_args(&b.suf, b.sp, q, k_suffix, v_suffix, nullptr, dense, suf),
+                     SplitMode::kFull, s) != hipSuccess)
       return ATTN_ERR_HIP;
     MergeArgs m{};
     m.map = work_map(&b.suf, b.sp);
@@ -401,8 +488,9 @@ const char *attn_status_string(attn_status_t status) {
     case ATTN_ERR_WORKSPACE: return "workspace smaller than the size query returned";
     case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case ATTN_ERR_UNSUPPORTED: return "shape not covered by the kernels (head_dim must be 64 or 128)";
-    case ATTN_ERR_VALUE: return "invalid scalar: non-finite scale, causal not 0/1, or chunk_len "
-                                "not a non-negative multiple of 64";
+    case ATTN_ERR_VALUE: return "invalid scalar: non-finite scale, causal not 0/1, chunk_len "
+                                "not a non-negative multiple of 64, or an invalid paging "
+                                "description";
   }
   return "unknown status";
 }

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "attn_decode.h"
+#include "kv_paging.h"
 #include "work_map.h"
 
 namespace attn {
@@ -23,6 +24,8 @@ struct SplitArgs {
   const void *q;
   const void *k;
   const void *v;
+  const void *zeta;  // energy with an auxiliary vector per row (layout of q), or null
+  KvPaging pg;
   WorkMap map;
   PartialLayout part;
   int32_t q_len, Hq, G, R;
@@ -46,8 +49,12 @@ struct MergeArgs {
   float *lse;
 };
 
+// What a split launch produces: (m, l, o) records, (m, l) only, or (m, l) of
+// the logits shifted by zeta . v (energy with zeta; vector-ALU kernel only).
+enum class SplitMode { kFull, kEnergy, kEnergyZeta };
+
 hipError_t launch_split_valu(const attn_plan_t &plan, const SplitArgs &a, attn_dtype_t dtype,
-                             int head_dim, bool energy_only, hipStream_t stream);
+                             int head_dim, SplitMode mode, hipStream_t stream);
 hipError_t launch_split_mfma(const attn_plan_t &plan, const SplitArgs &a, int head_dim,
                              bool energy_only, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream);

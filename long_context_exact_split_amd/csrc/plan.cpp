@@ -50,6 +50,41 @@ attn_status_t validate_desc(const attn_desc_t *d) {
   return ATTN_OK;
 }
 
+attn_status_t validate_paged(const attn_desc_t *d, const attn_paged_kv_t *paged, KvPaging *pg) {
+  *pg = KvPaging{};
+  if (!paged) return ATTN_OK;
+  const int64_t P = paged->page_size;
+  if (P < 1 || P > (int64_t(1) << kMaxPageShift) || (P & (P - 1)) != 0) return ATTN_ERR_VALUE;
+  if (paged->pages_per_seq < 1 || (int64_t)paged->pages_per_seq * P < d->max_kv_len)
+    return ATTN_ERR_VALUE;
+  if (paged->num_pages < 0 || paged->page_stride < 0 || paged->head_stride < 0 ||
+      paged->token_stride < 0)
+    return ATTN_ERR_VALUE;
+  const bool any_kv = d->batch > 0 && d->max_kv_len > 0;
+  if (any_kv && (paged->num_pages < 1 || !paged->block_table)) {
+    return paged->block_table ? ATTN_ERR_VALUE : ATTN_ERR_NULL;
+  }
+  // Every row starts on a 16-byte boundary.
+  const int64_t q = d->dtype == ATTN_BF16 ? 8 : 4;
+  if (paged->page_stride % q || paged->head_stride % q || paged->token_stride % q)
+    return ATTN_ERR_ALIGN;
+  constexpr int64_t kLimit = int64_t(1) << 48;
+  if (paged->page_stride > 0 && paged->num_pages > kLimit / paged->page_stride)
+    return ATTN_ERR_VALUE;
+  if (paged->head_stride > kLimit / d->num_kv_heads || paged->token_stride > kLimit / P)
+    return ATTN_ERR_VALUE;
+  pg->block_table = any_kv ? paged->block_table : nullptr;
+  pg->num_pages = paged->num_pages;
+  pg->page_stride = paged->page_stride;
+  pg->head_stride = paged->head_stride;
+  pg->token_stride = paged->token_stride;
+  pg->pages_per_seq = paged->pages_per_seq;
+  int shift = 0;
+  while ((int64_t(1) << shift) < P) ++shift;
+  pg->page_shift = shift;
+  return ATTN_OK;
+}
+
 attn_status_t make_plan(const attn_desc_t *d, int cu_count, bool mfma_available, attn_plan_t *p) {
   attn_status_t st = validate_desc(d);
   if (st != ATTN_OK) return st;

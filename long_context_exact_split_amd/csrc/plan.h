@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "attn_decode.h"
+#include "kv_paging.h"
 #include "work_map.h"
 
 namespace attn {
@@ -22,6 +23,10 @@ constexpr int kItemsPerCu = 1;
 
 int items_per_cu();
 attn_status_t validate_desc(const attn_desc_t *d);
+// Host checks of a paging description against its descriptor (null paged:
+// dense caches, always valid).  Fills *pg for the kernels.
+constexpr int kMaxPageShift = 20;
+attn_status_t validate_paged(const attn_desc_t *d, const attn_paged_kv_t *paged, KvPaging *pg);
 attn_status_t make_plan(const attn_desc_t *d, int cu_count, bool mfma_available, attn_plan_t *p);
 size_t partial_bytes(int64_t records, int head_dim);
 WorkMap work_map(const attn_desc_t *d, const attn_plan_t &p);

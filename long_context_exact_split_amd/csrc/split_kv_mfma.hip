@@ -27,6 +27,7 @@
 // the same merge kernel follows.
 #include "device_common.h"
 #include "kernels.h"
+#include "kv_rows.h"
 
 namespace attn {
 namespace {
@@ -217,7 +218,7 @@ union MfmaSmem {
 
 // One piece: tokens [c0, c1) of KV head kvh of sequence b, for row block rb;
 // writes the piece's record at `slot`.
-template <int D, bool ENERGY>
+template <int D, bool ENERGY, bool PAGED>
 __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, int rb, int c0,
                                            int c1, int64_t slot, MfmaSmem<D, ENERGY> &sh) {
   using T = Tiles<D>;
@@ -227,7 +228,6 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
   const int wave = threadIdx.x / kWave;
   const int h = lane >> 5;   // lane half
   const int j = lane & 31;   // query row owned by this lane (and key slot in A layouts)
-  const int group = b * a.map.Hkv + kvh;
   const int Lb = (int)seq_len(a.map, b);
   __syncthreads();  // the previous piece's epilogue is done with the shared buffers
 
@@ -266,26 +266,42 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[n][e] = 0.0f;
 
-  const int64_t base = (int64_t)group * a.map.L_max * D;
-  const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base + (lane % LPK) * 8;
-  const uint16_t *vg = ENERGY ? nullptr : static_cast<const uint16_t *>(a.v) + base + (lane % LPK) * 8;
+  const KvRows<PAGED, D> rows(a, b, kvh);
+  const uint16_t *kg = static_cast<const uint16_t *>(a.k) + rows.origin + (lane % LPK) * 8;
+  const uint16_t *vg =
+      ENERGY ? nullptr : static_cast<const uint16_t *>(a.v) + rows.origin + (lane % LPK) * 8;
   uint16_t *ks = sh.t.k[wave];
   uint16_t *vs = sh.t.v[wave];
   const int n_tiles = (hi - c0 + kTile - 1) / kTile;
 
+  // Token of load i of a tile, clamped so masked keys read a valid row.
+  auto token = [&](int tile, int i) {
+    const int t = c0 + tile * kTile + i * KPI + lane / LPK;
+    return t < hi ? t : hi - 1;
+  };
+  auto lookup = [&](int tile, int32_t (&pg)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) pg[i] = rows.lookup(token(tile, i));
+  };
   u32x4 kr[NL], vr[ENERGY ? 1 : NL];
-  auto load = [&](int tile) {
+  auto load = [&](int tile, const int32_t (&pg)[NL]) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      int t = c0 + tile * kTile + i * KPI + lane / LPK;
-      t = t < hi ? t : hi - 1;
-      kr[i] = load_nt(kg + (int64_t)t * D);
-      if constexpr (!ENERGY) vr[i] = load_nt(vg + (int64_t)t * D);
+      const int64_t off = rows.offset(token(tile, i), pg[i]);
+      kr[i] = load_nt(kg + off);
+      if constexpr (!ENERGY) vr[i] = load_nt(vg + off);
     }
   };
 
+  // Paged caches: block-table loads run one tile ahead of the K/V loads.
   int tile = wave;
-  if (tile < n_tiles) load(tile);
+  int32_t pn[NL];
+  if (tile < n_tiles) {
+    int32_t pc[NL];
+    lookup(tile, pc);
+    load(tile, pc);
+    lookup(tile + kWaves, pn);
+  }
   settle<KS>(qf);
   for (; tile < n_tiles; tile += kWaves) {
     // Stage this tile in LDS (the wave's previous LDS reads are complete:
@@ -300,7 +316,13 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int t0 = c0 + tile * kTile;
-    if (tile + kWaves < n_tiles) load(tile + kWaves);
+    int32_t pnn[NL];
+    if constexpr (PAGED) lookup(tile + 2 * kWaves, pnn);
+    if (tile + kWaves < n_tiles) load(tile + kWaves, pn);
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) pn[i] = pnn[i];
+    }
 
     tile_step<D, ENERGY>(ks, vs, qf, t0, lim, a.scale_log2, m, lsum, oacc);
   }
@@ -343,7 +365,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
   }
 }
 
-template <int D, bool ENERGY>
+template <int D, bool ENERGY, bool PAGED>
 __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   __shared__ MfmaSmem<D, ENERGY> sh;
   const WorkMap &m = a.map;
@@ -355,13 +377,13 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
     const int L = (int)seq_len(m, b);
     const int c0 = c * m.chunk_len;
     if (c0 >= L) return;
-    mfma_piece<D, ENERGY>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
+    mfma_piece<D, ENERGY, PAGED>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
   } else {
     const int64_t U = total_units(m);
     PieceCursor cur = first_piece(m, U, blockIdx.x);
     Piece p;
     while (next_piece(m, blockIdx.x, cur, &p))
-      mfma_piece<D, ENERGY>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
+      mfma_piece<D, ENERGY, PAGED>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
   }
 }
 
@@ -382,7 +404,7 @@ union RowsSmem {
   float stage[RW][kRows * 32];  // epilogue: one 32 x 32 float slice per wave
 };
 
-template <int D, int RW, bool ENERGY>
+template <int D, int RW, bool ENERGY, bool PAGED>
 __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, int rb, int c0,
                                            int c1, int64_t slot, RowsSmem<D, RW, ENERGY> &sh) {
   using T = Tiles<D>;
@@ -396,7 +418,6 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   const int wave = threadIdx.x / kWave;
   const int h = lane >> 5;
   const int j = lane & 31;
-  const int group = b * a.map.Hkv + kvh;
   const int Lb = (int)seq_len(a.map, b);
   __syncthreads();  // the previous piece is done with the tile buffers
 
@@ -433,9 +454,9 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[n][e] = 0.0f;
 
-  const int64_t base = (int64_t)group * a.map.L_max * D;
-  const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
-  const uint16_t *vg = ENERGY ? nullptr : static_cast<const uint16_t *>(a.v) + base;
+  const KvRows<PAGED, D> rows(a, b, kvh);
+  const uint16_t *kg = static_cast<const uint16_t *>(a.k) + rows.origin;
+  const uint16_t *vg = ENERGY ? nullptr : static_cast<const uint16_t *>(a.v) + rows.origin;
   const int n_tiles = (hi - c0 + kTile - 1) / kTile;
 
   // Tiles in flight: a ring of NS register stages (tile t lives in stage
@@ -443,16 +464,28 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   // the unrolled inner loop, so the ring stays in registers.
   constexpr int NS = RW >= 8 ? 3 : (RW >= 4 ? 2 : 1);
   u32x4 kr[NS][PER], vr[NS][ENERGY ? 1 : PER];
-  auto load = [&](int tile, u32x4 (&kd)[PER], u32x4 (&vd)[ENERGY ? 1 : PER]) {
+  // Token of this thread's copy piece i of a tile (clamped to a valid row).
+  auto token = [&](int tile, int i) {
+    const int p = threadIdx.x + i * NTH;
+    const int t = c0 + tile * kTile + p / (D / 8);
+    return t < hi ? t : hi - 1;
+  };
+  auto lookup = [&](int tile, int32_t (&pg)[PER]) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (PIECES % NTH != 0 && threadIdx.x + i * NTH >= PIECES) break;  // wave-uniform
+      pg[i] = rows.lookup(token(tile, i));
+    }
+  };
+  auto load = [&](int tile, const int32_t (&pg)[PER], u32x4 (&kd)[PER],
+                  u32x4 (&vd)[ENERGY ? 1 : PER]) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int p = threadIdx.x + i * NTH;
       if (PIECES % NTH != 0 && p >= PIECES) break;  // wave-uniform
-      const int key = p / (D / 8), col = (p % (D / 8)) * 8;
-      int t = c0 + tile * kTile + key;
-      t = t < hi ? t : hi - 1;
-      kd[i] = load_nt(kg + (int64_t)t * D + col);
-      if constexpr (!ENERGY) vd[i] = load_nt(vg + (int64_t)t * D + col);
+      const int64_t off = rows.offset(token(tile, i), pg[i]) + (p % (D / 8)) * 8;
+      kd[i] = load_nt(kg + off);
+      if constexpr (!ENERGY) vd[i] = load_nt(vg + off);
     }
   };
   auto store = [&](int buf, const u32x4 (&kd)[PER], const u32x4 (&vd)[ENERGY ? 1 : PER]) {
@@ -466,14 +499,31 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
     }
   };
 
+  // Paged caches: the block-table loads of tile x are issued in the
+  // iteration of tile x - 2*NS, NS - 1 iterations before the K/V loads of x,
+  // so that waiting for them never waits for K/V loads still in the ring.
+  // Their results live in a ring of page-id stages (tile x in stage x % NS).
+  int32_t pr[NS][PER];
+  for (int s2 = 0; s2 < NS; ++s2)
+    for (int i = 0; i < PER; ++i) pr[s2][i] = 0;
   // Prologue: tile 0 into LDS buffer 0, tiles 1..NS in flight.
   if (n_tiles > 0) {
-    load(0, kr[0], vr[0]);
+    int32_t p0[PER];
+    lookup(0, p0);
+    load(0, p0, kr[0], vr[0]);
     store(0, kr[0], vr[0]);
     settle<KS>(qf);
+    int32_t pk[NS + 1][PER];
 #pragma unroll
     for (int k = 1; k <= NS; ++k)
-      if (k < n_tiles) load(k, kr[k % NS], vr[k % NS]);
+      if (k < n_tiles) lookup(k, pk[k]);
+#pragma unroll
+    for (int k = 1; k <= NS; ++k)
+      if (k < n_tiles) load(k, pk[k], kr[k % NS], vr[k % NS]);
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int x = NS + 1; x < 2 * NS; ++x) lookup(x, pr[x % NS]);
+    }
   }
   __syncthreads();
   for (int base = 0; base < n_tiles; base += NS) {
@@ -481,12 +531,13 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
     for (int k = 0; k < NS; ++k) {
       const int tile = base + k;
       if (tile >= n_tiles) break;  // uniform across the workgroup
+      if constexpr (PAGED) lookup(tile + 2 * NS, pr[k]);  // stage (tile + 2NS) % NS = k
       tile_step<D, ENERGY>(sh.t.k[tile & 1], sh.t.v[tile & 1], qf, c0 + tile * kTile, lim,
                            a.scale_log2, m, lsum, oacc);
       if (tile + 1 < n_tiles) {
         const int kn = (k + 1) % NS;  // stage of tile + 1 (constant once unrolled)
         store((tile + 1) & 1, kr[kn], vr[kn]);
-        if (tile + 1 + NS < n_tiles) load(tile + 1 + NS, kr[kn], vr[kn]);
+        if (tile + 1 + NS < n_tiles) load(tile + 1 + NS, pr[kn], kr[kn], vr[kn]);
       }
       __syncthreads();
     }
@@ -530,7 +581,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   }
 }
 
-template <int D, int RW, bool ENERGY>
+template <int D, int RW, bool ENERGY, bool PAGED>
 __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
   __shared__ RowsSmem<D, RW, ENERGY> sh;
   const WorkMap &m = a.map;
@@ -542,38 +593,50 @@ __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
     const int L = (int)seq_len(m, b);
     const int c0 = c * m.chunk_len;
     if (c0 >= L) return;
-    rows_piece<D, RW, ENERGY>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
+    rows_piece<D, RW, ENERGY, PAGED>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
   } else {
     const int64_t U = total_units(m);
     PieceCursor cur = first_piece(m, U, blockIdx.x);
     Piece p;
     while (next_piece(m, blockIdx.x, cur, &p))
-      rows_piece<D, RW, ENERGY>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
+      rows_piece<D, RW, ENERGY, PAGED>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
   }
 }
 
-template <int D, int RW, bool ENERGY>
+template <int D, int RW, bool ENERGY, bool PAGED>
 hipError_t launch_rows(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, ENERGY>), dim3((unsigned)plan.work_items),
+  hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, ENERGY, PAGED>), dim3((unsigned)plan.work_items),
                      dim3(RW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool ENERGY>
+template <int D, bool ENERGY, bool PAGED>
 hipError_t launch_rows_rw(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
   switch (plan.rows_per_block) {
-    case 2 * kRows: return launch_rows<D, 2, ENERGY>(plan, a, stream);
-    case 4 * kRows: return launch_rows<D, 4, ENERGY>(plan, a, stream);
-    case 8 * kRows: return launch_rows<D, 8, ENERGY>(plan, a, stream);
+    case 2 * kRows: return launch_rows<D, 2, ENERGY, PAGED>(plan, a, stream);
+    case 4 * kRows: return launch_rows<D, 4, ENERGY, PAGED>(plan, a, stream);
+    case 8 * kRows: return launch_rows<D, 8, ENERGY, PAGED>(plan, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int D, bool ENERGY>
-hipError_t launch(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kv_mfma<D, ENERGY>), dim3((unsigned)plan.work_items), dim3(kThreads),
-                     0, stream, a);
+template <int D, bool ENERGY, bool PAGED>
+hipError_t launch_kernel(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+  if (plan.kernel == 2) return launch_rows_rw<D, ENERGY, PAGED>(plan, a, stream);
+  if (plan.rows_per_block != kRows) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((split_kv_mfma<D, ENERGY, PAGED>), dim3((unsigned)plan.work_items),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const attn_plan_t &plan, const SplitArgs &a, bool energy, hipStream_t stream) {
+  const bool paged = a.pg.block_table != nullptr;
+  if (energy)
+    return paged ? launch_kernel<D, true, true>(plan, a, stream)
+                 : launch_kernel<D, true, false>(plan, a, stream);
+  return paged ? launch_kernel<D, false, true>(plan, a, stream)
+               : launch_kernel<D, false, false>(plan, a, stream);
 }
 
 }  // namespace
@@ -581,20 +644,8 @@ hipError_t launch(const attn_plan_t &plan, const SplitArgs &a, hipStream_t strea
 hipError_t launch_split_mfma(const attn_plan_t &plan, const SplitArgs &a, int head_dim,
                              bool energy_only, hipStream_t stream) {
   if (plan.work_items <= 0) return hipSuccess;
-  if (plan.kernel == 2) {
-    if (head_dim == 64)
-      return energy_only ? launch_rows_rw<64, true>(plan, a, stream)
-                         : launch_rows_rw<64, false>(plan, a, stream);
-    if (head_dim == 128)
-      return energy_only ? launch_rows_rw<128, true>(plan, a, stream)
-                         : launch_rows_rw<128, false>(plan, a, stream);
-    return hipErrorInvalidValue;
-  }
-  if (plan.rows_per_block != kRows) return hipErrorInvalidValue;
-  if (head_dim == 64)
-    return energy_only ? launch<64, true>(plan, a, stream) : launch<64, false>(plan, a, stream);
-  if (head_dim == 128)
-    return energy_only ? launch<128, true>(plan, a, stream) : launch<128, false>(plan, a, stream);
+  if (head_dim == 64) return launch_d<64>(plan, a, energy_only, stream);
+  if (head_dim == 128) return launch_d<128>(plan, a, energy_only, stream);
   return hipErrorInvalidValue;
 }
 

@@ -24,6 +24,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "kv_rows.h"
 
 namespace attn {
 namespace {
@@ -97,10 +98,17 @@ struct ValuSmem {
 };
 
 // One piece: tokens [c0, c1) of KV head kvh of sequence b, for row block rb;
-// writes the piece's record at `slot`.
-template <typename T, int D, int RB, int KT, bool ENERGY>
+// writes the piece's record at `slot`.  MODE: what is produced (SplitMode);
+// with kEnergyZeta each logit gains zeta . v_t, zeta being the row's
+// auxiliary vector (Tree Attention article, an energy view of attention: the
+// energy's gradient in zeta at 0 is the attention output).
+template <typename T, int D, int RB, int KT, SplitMode MODE, bool PAGED>
 __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, int rb, int c0,
-                                           int c1, int64_t slot, ValuSmem<D, RB, ENERGY> &sh) {
+                                           int c1, int64_t slot,
+                                           ValuSmem<D, RB, MODE != SplitMode::kFull> &sh) {
+  constexpr bool ENERGY = MODE != SplitMode::kFull;
+  constexpr bool ZETA = MODE == SplitMode::kEnergyZeta;
+  constexpr bool LOADV = MODE != SplitMode::kEnergy;
   using Geo = Geometry<T, D>;
   constexpr int EPL = Geo::EPL, LPK = Geo::LPK, KPW = Geo::KPW;
   constexpr int TK = KPW * KT;  // keys per wave tile
@@ -109,26 +117,27 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
   const int wave = threadIdx.x / kWave;
   const int kr = lane / LPK;  // key slot in a wave load
   const int kl = lane % LPK;  // slice of the key row
-  const int group = b * a.map.Hkv + kvh;
   const int Lb = (int)seq_len(a.map, b);
 
   // Visibility limit per row (keys t < lim[r]) and the query slices.
   int lim[RB];
   int hi = c0;
-  uint4 q[RB];
+  uint4 q[RB], z[ZETA ? RB : 1];
   const T *Q = static_cast<const T *>(a.q);
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int rg = rb * RB + r;
     int n = c0;
     q[r] = make_uint4(0, 0, 0, 0);
+    if constexpr (ZETA) z[r] = make_uint4(0, 0, 0, 0);
     if (rg < a.R) {
       const int i = rg / a.G;
       const int h = kvh * a.G + (rg - i * a.G);
       n = a.causal ? Lb - a.q_len + i + 1 : Lb;
       n = n < c0 ? c0 : (n > c1 ? c1 : n);
-      const T *qrow = Q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + kl * EPL;
-      q[r] = *reinterpret_cast<const uint4 *>(qrow);
+      const int64_t qoff = (((int64_t)b * a.q_len + i) * a.Hq + h) * D + kl * EPL;
+      q[r] = *reinterpret_cast<const uint4 *>(Q + qoff);
+      if constexpr (ZETA) z[r] = *reinterpret_cast<const uint4 *>(static_cast<const T *>(a.zeta) + qoff);
     }
     lim[r] = n;
     hi = max(hi, n);
@@ -145,34 +154,60 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
     }
   }
 
-  const int64_t row_base = (int64_t)group * a.map.L_max * D + kl * EPL;
-  const T *kbase = static_cast<const T *>(a.k) + row_base;
-  const T *vbase = ENERGY ? nullptr : static_cast<const T *>(a.v) + row_base;
+  const KvRows<PAGED, D> rows(a, b, kvh);
+  const T *kbase = static_cast<const T *>(a.k) + rows.origin + kl * EPL;
+  const T *vbase = LOADV ? static_cast<const T *>(a.v) + rows.origin + kl * EPL : nullptr;
   const int n_tiles = (hi - c0 + TK - 1) / TK;
 
-  uint4 kc[KT], vc[ENERGY ? 1 : KT];
-  auto load_tile = [&](int tile, uint4 (&kd)[KT], uint4 (&vd)[ENERGY ? 1 : KT]) {
+  // Token of key slot j of a wave tile, clamped so masked keys read a valid row.
+  auto token = [&](int tile, int j) {
+    const int t = c0 + tile * TK + j * KPW + kr;
+    return t < hi ? t : hi - 1;
+  };
+  auto lookup_tile = [&](int tile, int32_t (&pg)[KT]) {
+#pragma unroll
+    for (int j = 0; j < KT; ++j) pg[j] = rows.lookup(token(tile, j));
+  };
+  uint4 kc[KT], vc[LOADV ? KT : 1];
+  auto load_tile = [&](int tile, const int32_t (&pg)[KT], uint4 (&kd)[KT],
+                       uint4 (&vd)[LOADV ? KT : 1]) {
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
-      int t = c0 + tile * TK + j * KPW + kr;
-      t = t < hi ? t : hi - 1;  // clamp: masked keys read a valid row
-      kd[j] = load16(kbase + (int64_t)t * D);
-      if constexpr (!ENERGY) vd[j] = load16(vbase + (int64_t)t * D);
+      const int64_t off = rows.offset(token(tile, j), pg[j]);
+      kd[j] = load16(kbase + off);
+      if constexpr (LOADV) vd[j] = load16(vbase + off);
     }
   };
+  // The wave's tile after `tile` (or `tile` again, an L2 hit, on the last).
+  auto next_of = [&](int tile) { return tile + kWaves < n_tiles ? tile + kWaves : tile; };
 
+  // Paged caches: the block-table loads of a tile are issued one iteration
+  // ahead of its K/V loads, so no wait for them stalls the K/V stream.
   int tile = wave;
-  if (tile < n_tiles) load_tile(tile, kc, vc);
+  int32_t pn[KT];
+  if (tile < n_tiles) {
+    int32_t pc[KT];
+    lookup_tile(tile, pc);
+    load_tile(tile, pc, kc, vc);
+    lookup_tile(next_of(tile), pn);
+  }
   for (; tile < n_tiles; tile += kWaves) {
-    // Prefetch the wave's next tile (or re-read this one, an L2 hit, on the last).
-    uint4 kn[KT], vn[ENERGY ? 1 : KT];
-    load_tile(tile + kWaves < n_tiles ? tile + kWaves : tile, kn, vn);
+    int32_t pnn[KT];
+    if constexpr (PAGED) lookup_tile(next_of(next_of(tile)), pnn);
+    uint4 kn[KT], vn[LOADV ? KT : 1];
+    load_tile(next_of(tile), pn, kn, vn);
 
     float s[KT][RB];
 #pragma unroll
     for (int j = 0; j < KT; ++j)
 #pragma unroll
-      for (int r = 0; r < RB; ++r) s[j][r] = group_sum<LPK>(slice_dot<T>(q[r], kc[j]));
+      for (int r = 0; r < RB; ++r) {
+        if constexpr (ZETA)
+          s[j][r] = group_sum<LPK>(slice_dot<T>(q[r], kc[j]) * a.scale_log2 +
+                                   slice_dot<T>(z[r], vc[j]) * kLog2e);
+        else
+          s[j][r] = group_sum<LPK>(slice_dot<T>(q[r], kc[j]));
+      }
 
     float tmax[RB];
 #pragma unroll
@@ -182,7 +217,7 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
       const int t = c0 + tile * TK + j * KPW + kr;
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
-        s[j][r] = t < lim[r] ? s[j][r] * a.scale_log2 : -INFINITY;
+        s[j][r] = t < lim[r] ? (ZETA ? s[j][r] : s[j][r] * a.scale_log2) : -INFINITY;
         tmax[r] = fmaxf(tmax[r], s[j][r]);
       }
     }
@@ -222,7 +257,8 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
       kc[j] = kn[j];
-      if constexpr (!ENERGY) vc[j] = vn[j];
+      if constexpr (LOADV) vc[j] = vn[j];
+      if constexpr (PAGED) pn[j] = pnn[j];
     }
   }
 
@@ -290,9 +326,9 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
   }
 }
 
-template <typename T, int D, int RB, int KT, bool ENERGY>
+template <typename T, int D, int RB, int KT, SplitMode MODE, bool PAGED>
 __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
-  __shared__ ValuSmem<D, RB, ENERGY> sh;
+  __shared__ ValuSmem<D, RB, MODE != SplitMode::kFull> sh;
   const WorkMap &m = a.map;
   if (m.mode == 0) {
     const int w = blockIdx.x;
@@ -302,13 +338,13 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
     const int L = (int)seq_len(m, b);
     const int c0 = c * m.chunk_len;
     if (c0 >= L) return;  // past the sequence: the merge reads ceil(L_b / C) records only
-    valu_piece<T, D, RB, KT, ENERGY>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
+    valu_piece<T, D, RB, KT, MODE, PAGED>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
   } else {
     const int64_t U = total_units(m);
     PieceCursor cur = first_piece(m, U, blockIdx.x);
     Piece p;
     while (next_piece(m, blockIdx.x, cur, &p))
-      valu_piece<T, D, RB, KT, ENERGY>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
+      valu_piece<T, D, RB, KT, MODE, PAGED>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
   }
 }
 
@@ -429,42 +465,54 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   }
 }
 
-template <typename T, int D, int RB, bool ENERGY>
+template <typename T, int D, int RB, SplitMode MODE, bool PAGED>
 hipError_t launch_t(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
   constexpr int KT = RB <= 4 ? ATTN_SPLIT_KT_SMALL : ATTN_SPLIT_KT_LARGE;
   if (plan.work_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL((split_kv_valu<T, D, RB, KT, ENERGY>), dim3((unsigned)plan.work_items),
+  hipLaunchKernelGGL((split_kv_valu<T, D, RB, KT, MODE, PAGED>), dim3((unsigned)plan.work_items),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool ENERGY>
+template <typename T, int D, SplitMode MODE, bool PAGED>
 hipError_t launch_rb(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
   switch (plan.rows_per_block) {
-    case 1: return launch_t<T, D, 1, ENERGY>(plan, a, stream);
-    case 2: return launch_t<T, D, 2, ENERGY>(plan, a, stream);
-    case 4: return launch_t<T, D, 4, ENERGY>(plan, a, stream);
-    case 8: return launch_t<T, D, 8, ENERGY>(plan, a, stream);
+    case 1: return launch_t<T, D, 1, MODE, PAGED>(plan, a, stream);
+    case 2: return launch_t<T, D, 2, MODE, PAGED>(plan, a, stream);
+    case 4: return launch_t<T, D, 4, MODE, PAGED>(plan, a, stream);
+    case 8: return launch_t<T, D, 8, MODE, PAGED>(plan, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, bool ENERGY>
-hipError_t launch_d(const attn_plan_t &plan, const SplitArgs &a, int D, hipStream_t stream) {
-  return D == 64 ? launch_rb<T, 64, ENERGY>(plan, a, stream)
-                 : launch_rb<T, 128, ENERGY>(plan, a, stream);
+template <typename T, int D>
+hipError_t launch_mode(const attn_plan_t &plan, const SplitArgs &a, SplitMode mode,
+                       hipStream_t stream) {
+  const bool paged = a.pg.block_table != nullptr;
+  switch (mode) {
+    case SplitMode::kFull:
+      return paged ? launch_rb<T, D, SplitMode::kFull, true>(plan, a, stream)
+                   : launch_rb<T, D, SplitMode::kFull, false>(plan, a, stream);
+    case SplitMode::kEnergy:
+      return paged ? launch_rb<T, D, SplitMode::kEnergy, true>(plan, a, stream)
+                   : launch_rb<T, D, SplitMode::kEnergy, false>(plan, a, stream);
+    case SplitMode::kEnergyZeta:  // dense caches only
+      return paged ? hipErrorInvalidValue
+                   : launch_rb<T, D, SplitMode::kEnergyZeta, false>(plan, a, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_split_valu(const attn_plan_t &plan, const SplitArgs &a, attn_dtype_t dtype,
-                             int head_dim, bool energy_only, hipStream_t stream) {
+                             int head_dim, SplitMode mode, hipStream_t stream) {
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
   if (dtype == ATTN_BF16)
-    return energy_only ? launch_d<uint16_t, true>(plan, a, head_dim, stream)
-                       : launch_d<uint16_t, false>(plan, a, head_dim, stream);
-  return energy_only ? launch_d<float, true>(plan, a, head_dim, stream)
-                     : launch_d<float, false>(plan, a, head_dim, stream);
+    return head_dim == 64 ? launch_mode<uint16_t, 64>(plan, a, mode, stream)
+                          : launch_mode<uint16_t, 128>(plan, a, mode, stream);
+  return head_dim == 64 ? launch_mode<float, 64>(plan, a, mode, stream)
+                        : launch_mode<float, 128>(plan, a, mode, stream);
 }
 
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream) {

@@ -71,6 +71,9 @@ int main(void) {
   F(attn_plan_t, record_slots) F(attn_plan_t, cu_count) F(attn_plan_t, workspace_bytes)
   printf("attn_bifurcated_desc_t %zu\\n", sizeof(attn_bifurcated_desc_t));
   F(attn_bifurcated_desc_t, prefix_len) F(attn_bifurcated_desc_t, scale) F(attn_bifurcated_desc_t, dtype)
+  printf("attn_paged_kv_t %zu\\n", sizeof(attn_paged_kv_t));
+  F(attn_paged_kv_t, pages_per_seq) F(attn_paged_kv_t, page_size) F(attn_paged_kv_t, num_pages)
+  F(attn_paged_kv_t, page_stride) F(attn_paged_kv_t, head_stride) F(attn_paged_kv_t, token_stride)
   return 0;
 }
 """)
@@ -80,7 +83,7 @@ int main(void) {
     got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True,
                                                                text=True, check=True).stdout.split("\n") if line)
     structs = {"attn_desc_t": binding.AttnDesc, "attn_plan_t": binding.AttnPlan,
-               "attn_bifurcated_desc_t": binding.AttnBifDesc}
+               "attn_bifurcated_desc_t": binding.AttnBifDesc, "attn_paged_kv_t": binding.AttnPagedKv}
     for key, val in got.items():
         if "." in key:
             s, f = key.split(".")
@@ -159,6 +162,72 @@ def test_bifurcated_validation(lib):
     assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *([16] * 6 + [0, 16, 1, None]))] == "ATTN_ERR_NULL"
     d.num_samples = 0
     assert lib.attn_decode_bifurcated(ctypes.byref(d), *args) == 0
+
+
+def _paged(**kw):
+    # head-major pages of 16 tokens for Hkv=2, D=128: page 4096 elements
+    pk = binding.AttnPagedKv()
+    base = dict(block_table=64, pages_per_seq=63, page_size=16, num_pages=200, page_stride=4096,
+                head_stride=2048, token_stride=128)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(pk, k, v)
+    return pk
+
+
+BAD_PAGED = [
+    (dict(page_size=12), "ATTN_ERR_VALUE"),
+    (dict(page_size=0), "ATTN_ERR_VALUE"),
+    (dict(page_size=1 << 21, pages_per_seq=1), "ATTN_ERR_VALUE"),
+    (dict(pages_per_seq=62), "ATTN_ERR_VALUE"),   # 62 * 16 < max_kv_len = 1000
+    (dict(pages_per_seq=0), "ATTN_ERR_VALUE"),
+    (dict(num_pages=0), "ATTN_ERR_VALUE"),
+    (dict(num_pages=-1), "ATTN_ERR_VALUE"),
+    (dict(token_stride=-128), "ATTN_ERR_VALUE"),
+    (dict(page_stride=1 << 40, num_pages=1 << 10), "ATTN_ERR_VALUE"),
+    (dict(block_table=None), "ATTN_ERR_NULL"),
+    (dict(token_stride=100), "ATTN_ERR_ALIGN"),   # rows must start on 16 bytes
+    (dict(head_stride=2044), "ATTN_ERR_ALIGN"),
+    (dict(page_size=1, pages_per_seq=1000), None),
+    (dict(), None),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_PAGED)
+def test_paged_validation_before_any_hip_call(lib, kw, status):
+    d = _desc()
+    pk = _paged(**kw)
+    codes = [lib.attn_decode_paged(ctypes.byref(d), ctypes.byref(pk), 16, 16, 16, 16, 16, 16,
+                                   1 << 30, None),
+             lib.attn_decode_energy_paged(ctypes.byref(d), ctypes.byref(pk), 16, 16, 16, 16,
+                                          1 << 30, None),
+             lib.attn_decode_partials_paged(ctypes.byref(d), ctypes.byref(pk), 16, 16, 16, 16,
+                                            1 << 30, None)]
+    for code in codes:
+        if status is None:
+            assert code not in (1, 2, 3, 4, 7, 8)  # may be ATTN_ERR_HIP without a GPU
+        else:
+            assert binding.STATUS[code] == status, (kw, code)
+
+
+def test_paged_and_zeta_null_checks(lib):
+    d = _desc()
+    assert binding.STATUS[lib.attn_decode_paged(ctypes.byref(d), None, 16, 16, 16, 16, 16, 16,
+                                                1, None)] == "ATTN_ERR_NULL"
+    # fp32 pools need 16-byte rows too: 4-element multiples
+    f = _desc(dtype=binding.ATTN_F32)
+    pk = _paged(token_stride=132, head_stride=16 * 132, page_stride=2 * 16 * 132)
+    assert lib.attn_decode_paged(ctypes.byref(f), ctypes.byref(pk), 16, 16, 16, 16, 16, 16,
+                                 1 << 30, None) not in (1, 2, 3, 4, 7, 8)
+    args = [16, 16, 16, 16, 16, 16, 1 << 30, None]
+    assert binding.STATUS[lib.attn_decode_energy_zeta(ctypes.byref(d), *args)] not in (
+        "ATTN_ERR_NULL", "ATTN_ERR_ALIGN")
+    z = list(args); z[3] = 0
+    assert binding.STATUS[lib.attn_decode_energy_zeta(ctypes.byref(d), *z)] == "ATTN_ERR_NULL"
+    z[3] = 24
+    assert binding.STATUS[lib.attn_decode_energy_zeta(ctypes.byref(d), *z)] == "ATTN_ERR_ALIGN"
+    z = list(args); z[2] = 0  # F(zeta) reads V
+    assert binding.STATUS[lib.attn_decode_energy_zeta(ctypes.byref(d), *z)] == "ATTN_ERR_NULL"
 
 
 def test_status_strings(lib):
