@@ -45,10 +45,15 @@ VARIANTS = {
     "paged_long_context_1m": ("long_context_1m", "full", (16, "head_major")),
     "paged_llama31_70b_ragged": ("llama31_70b_ragged", "full", (16, "token_major")),
 }
-KERNEL_SOURCES = ("long_context_exact_split_amd/csrc/split_kv_valu.hip",
-                  "long_context_exact_split_amd/csrc/device_common.h",
-                  "long_context_exact_split_amd/csrc/kernels.h")
-COUNTERS = "profiles/split_kv_valu_long_context_1m.counters.txt"
+# rocprofv3 counter summaries (HBM bytes per launch of the dominant kernel),
+# one per workload.  A summary's figures are used only while the kernel
+# sources it lists still hash to its source_sha256.
+COUNTERS = {
+    "long_context_1m": "profiles/split_kv_valu_long_context_1m.counters.txt",
+    "long_context_1m_energy": "profiles/split_kv_valu_energy_long_context_1m.counters.txt",
+    "paged_long_context_1m": "profiles/split_kv_valu_paged_long_context_1m.counters.txt",
+    "llama31_70b_ragged": "profiles/split_kv_mfma_llama31_70b_ragged.counters.txt",
+}
 
 
 def parse():
@@ -70,22 +75,22 @@ def parse():
 # ----------------------------------------------------------------------------
 # Reference figures
 # ----------------------------------------------------------------------------
-def kernel_source_hash():
+def source_hash(files):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
 def counter_traffic(workload):
-    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE, each scaled by its copy-kernel
-    calibration factor), or None when the kernel sources changed since or the
-    summary covers another workload."""
-    path = os.path.join(ROOT, COUNTERS)
-    if workload != "long_context_1m" or not os.path.exists(path):
+    """HBM bytes per dominant-kernel launch from the workload's committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by its
+    copy-kernel calibration factor), or None when there is none or the kernel
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, COUNTERS.get(workload, "-"))
+    if not os.path.exists(path):
         return None
     kv = {}
     with open(path) as fh:
@@ -93,7 +98,8 @@ def counter_traffic(workload):
             if "=" in line and not line.lstrip().startswith("#"):
                 key, val = line.split("=", 1)
                 kv[key.strip()] = val.strip()
-    if kv.get("source_sha256") != kernel_source_hash():
+    files = [f.strip() for f in kv.get("sources", "").split(",") if f.strip()]
+    if not files or kv.get("source_sha256") != source_hash(files):
         return None
     return float(kv["traffic_bytes_per_launch"])
 
