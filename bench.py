@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the HBM read-stream reference measurement")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged workloads: tokens per page (0: the workload's own, 16)")
     return ap.parse_args()
 
 
@@ -360,6 +362,8 @@ def main():
         run = BifurcatedRunner(torch, w)
     else:
         _, mode, paging = VARIANTS.get(args.workload, (None, "full", None))
+        if paging is not None and args.page_size:
+            paging = (args.page_size, paging[1])
         run = DecodeRunner(torch, w, mode, paging)
     print(f"# plan {run.plan}", file=sys.stderr, flush=True)
 

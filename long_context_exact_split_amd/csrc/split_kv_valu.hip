@@ -91,6 +91,76 @@ __device__ __forceinline__ float slice_dot(const uint4 &q, const uint4 &k) {
   }
 }
 
+// Reduce-scatter of RB per-row partial dot products over the LPK lanes of one
+// key row: afterwards the lane holds the full sum of one row only
+// (scatter_row gives which), so the softmax steps that follow run once per
+// (key, row) on RB-times fewer lanes than after an all-reduce.  The steps are
+// the DPP butterfly of group_sum (quad xor 1, quad xor 2, half-row mirror,
+// row mirror, then xor 16), each step keeping half of the lane's rows and
+// pulling the partner's partials for them.  The partners of the two mirror
+// steps sit at the reflected quad position, so the rows a lane keeps are
+// chosen from its quad position XOR 3 in odd quads; with that choice every
+// lane's sum is bit-identical to what group_sum leaves in it for its row.
+__device__ __forceinline__ int quad_pos(int kl) { return (kl & 3) ^ (((kl >> 2) & 1) ? 3 : 0); }
+
+template <int LPK, int RB>
+__device__ __forceinline__ int scatter_row(int kl) {
+  const int pq = quad_pos(kl);
+  int r = 0;
+  if constexpr (RB >= 2) r += (pq & 1) * (RB / 2);
+  if constexpr (RB >= 4) r += ((pq >> 1) & 1) * (RB / 4);
+  if constexpr (RB >= 8) r += (LPK >= 16 ? (((kl >> 2) ^ (kl >> 3)) & 1) : ((kl >> 2) & 1));
+  return r;
+}
+
+template <int LPK, int RB>
+__device__ __forceinline__ float row_scatter_sum(const float (&x)[RB], int kl) {
+  static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8, "rows per block");
+  static_assert(LPK >= 8 && LPK >= RB, "lanes per key row");
+  const int pq = quad_pos(kl);
+  float v[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) v[r] = x[r];
+  // Step 1 (quad xor 1).
+  if constexpr (RB >= 2) {
+    const bool up = pq & 1;
+#pragma unroll
+    for (int k = 0; k < RB / 2; ++k) {
+      const float keep = up ? v[RB / 2 + k] : v[k];
+      const float send = up ? v[k] : v[RB / 2 + k];
+      v[k] = keep + dpp_f32<kDppQuadXor1>(send);
+    }
+  } else {
+    v[0] += dpp_f32<kDppQuadXor1>(v[0]);
+  }
+  // Step 2 (quad xor 2).
+  if constexpr (RB >= 4) {
+    const bool up = (pq >> 1) & 1;
+#pragma unroll
+    for (int k = 0; k < RB / 4; ++k) {
+      const float keep = up ? v[RB / 4 + k] : v[k];
+      const float send = up ? v[k] : v[RB / 4 + k];
+      v[k] = keep + dpp_f32<kDppQuadXor2>(send);
+    }
+  } else {
+    v[0] += dpp_f32<kDppQuadXor2>(v[0]);
+  }
+  // Step 3 (half-row mirror).
+  if constexpr (RB >= 8) {
+    const bool up = LPK >= 16 ? (((kl >> 2) ^ (kl >> 3)) & 1) : ((kl >> 2) & 1);
+    const float keep = up ? v[1] : v[0];
+    const float send = up ? v[0] : v[1];
+    v[0] = keep + dpp_f32<kDppRowHalfMirror>(send);
+  } else {
+    v[0] += dpp_f32<kDppRowHalfMirror>(v[0]);
+  }
+  // Steps 4 and 5: all-reduce over the rest of the key row.
+  if constexpr (LPK >= 16) v[0] += dpp_f32<kDppRowMirror>(v[0]);
+  if constexpr (LPK >= 32) v[0] += __shfl_xor(v[0], 16);
+  if constexpr (LPK >= 64) v[0] += __shfl_xor(v[0], 32);
+  return v[0];
+}
+
 template <int D, int RB, bool ENERGY>
 struct ValuSmem {
   float m[kWaves][RB], l[kWaves][RB];
@@ -143,16 +213,26 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
     hi = max(hi, n);
   }
 
-  float m[RB], l[RB], o[RB][ENERGY ? 1 : EPL];
+  // Softmax state.  Full decode: every lane keeps (m, l, o) for all RB rows
+  // (the o slices differ per lane).  Energy: after the reduce-scatter a lane
+  // owns one row, my_row, and keeps (m, l) for it alone.
+  constexpr int NS_ROWS = ENERGY ? 1 : RB;
+  float m[NS_ROWS], l[NS_ROWS], o[RB][ENERGY ? 1 : EPL];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
+  for (int r = 0; r < NS_ROWS; ++r) {
     m[r] = -INFINITY;
     l[r] = 0.0f;
-    if constexpr (!ENERGY) {
+  }
+  if constexpr (!ENERGY) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[r][e] = 0.0f;
-    }
   }
+  const int my_row = ENERGY ? scatter_row<LPK, RB>(kl) : 0;
+  int my_lim = lim[0];
+#pragma unroll
+  for (int r = 1; r < RB; ++r) my_lim = my_row == r ? lim[r] : my_lim;
 
   const KvRows<PAGED, D> rows(a, b, kvh);
   const T *kbase = static_cast<const T *>(a.k) + rows.origin + kl * EPL;
@@ -168,7 +248,6 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
 #pragma unroll
     for (int j = 0; j < KT; ++j) pg[j] = rows.lookup(token(tile, j));
   };
-  uint4 kc[KT], vc[LOADV ? KT : 1];
   auto load_tile = [&](int tile, const int32_t (&pg)[KT], uint4 (&kd)[KT],
                        uint4 (&vd)[LOADV ? KT : 1]) {
 #pragma unroll
@@ -178,95 +257,157 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
       if constexpr (LOADV) vd[j] = load16(vbase + off);
     }
   };
-  // The wave's tile after `tile` (or `tile` again, an L2 hit, on the last).
+
+  // Loads run ahead of the arithmetic (tiles past the end read the last
+  // visible row again, an L2 hit).  With K and V: the next tile's loads are
+  // issued before the arithmetic on this one.  K only: a ring of NSTG = 3
+  // register stages, each refilled with the tile one round later as soon as
+  // it has been consumed, so two tiles are in flight (the same bytes per wave
+  // as with K and V); stage indices are compile-time in the unrolled round,
+  // so no register copy has to wait for a load.  (The K+V loop keeps the
+  // copy form: unrolled, the branch of the lazy rescale makes the compiler
+  // wait for every load in flight at the join.)  Paged caches: block-table
+  // loads are issued a tile ahead of the K/V loads that use them.
+  constexpr int NSTG = 3;
+  constexpr int RSTEP = NSTG * kWaves;  // tiles per round of one wave (K only)
   auto next_of = [&](int tile) { return tile + kWaves < n_tiles ? tile + kWaves : tile; };
 
-  // Paged caches: the block-table loads of a tile are issued one iteration
-  // ahead of its K/V loads, so no wait for them stalls the K/V stream.
-  int tile = wave;
-  int32_t pn[KT];
-  if (tile < n_tiles) {
-    int32_t pc[KT];
-    lookup_tile(tile, pc);
-    load_tile(tile, pc, kc, vc);
-    lookup_tile(next_of(tile), pn);
-  }
-  for (; tile < n_tiles; tile += kWaves) {
-    int32_t pnn[KT];
-    if constexpr (PAGED) lookup_tile(next_of(next_of(tile)), pnn);
-    uint4 kn[KT], vn[LOADV ? KT : 1];
-    load_tile(next_of(tile), pn, kn, vn);
-
-    float s[KT][RB];
+  auto compute = [&](int tile, const uint4 (&kc)[KT], const uint4 (&vc)[LOADV ? KT : 1]) {
+    if constexpr (ENERGY) {
+      // One row per lane: reduce-scatter the slice dot products, then the
+      // masked online softmax of that row.
+      float s[KT];
 #pragma unroll
-    for (int j = 0; j < KT; ++j)
+      for (int j = 0; j < KT; ++j) {
+        float x[RB];
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if constexpr (ZETA)
-          s[j][r] = group_sum<LPK>(slice_dot<T>(q[r], kc[j]) * a.scale_log2 +
-                                   slice_dot<T>(z[r], vc[j]) * kLog2e);
-        else
-          s[j][r] = group_sum<LPK>(slice_dot<T>(q[r], kc[j]));
+        for (int r = 0; r < RB; ++r) {
+          if constexpr (ZETA)
+            x[r] = slice_dot<T>(q[r], kc[j]) * a.scale_log2 + slice_dot<T>(z[r], vc[j]) * kLog2e;
+          else
+            x[r] = slice_dot<T>(q[r], kc[j]);
+        }
+        s[j] = row_scatter_sum<LPK, RB>(x, kl);
       }
-
-    float tmax[RB];
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) tmax[r] = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < KT; ++j) {
-      const int t = c0 + tile * TK + j * KPW + kr;
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        s[j][r] = t < lim[r] ? (ZETA ? s[j][r] : s[j][r] * a.scale_log2) : -INFINITY;
-        tmax[r] = fmaxf(tmax[r], s[j][r]);
+      for (int j = 0; j < KT; ++j) {
+        const int t = c0 + tile * TK + j * KPW + kr;
+        s[j] = t < my_lim ? (ZETA ? s[j] : s[j] * a.scale_log2) : -INFINITY;
+        tmax = fmaxf(tmax, s[j]);
       }
-    }
-    bool need = false;
+      if (__any(tmax > m[0] + kLazyRescale)) {
+        const float mn = fmaxf(m[0], tmax);
+        l[0] *= rescale_factor(m[0], mn);
+        m[0] = mn;
+      }
+      const float mref = m[0] == -INFINITY ? 0.0f : m[0];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) need |= tmax[r] > m[r] + kLazyRescale;
-    if (__any(need)) {
+      for (int j = 0; j < KT; ++j) l[0] += fast_exp2(s[j] - mref);
+    } else {
+      float s[KT][RB];
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const float mn = fmaxf(m[r], tmax[r]);
-        const float alpha = rescale_factor(m[r], mn);
-        l[r] *= alpha;
-        if constexpr (!ENERGY) {
+      for (int j = 0; j < KT; ++j)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) s[j][r] = group_sum<LPK>(slice_dot<T>(q[r], kc[j]));
+
+      float tmax[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) tmax[r] = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        const int t = c0 + tile * TK + j * KPW + kr;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          s[j][r] = t < lim[r] ? s[j][r] * a.scale_log2 : -INFINITY;
+          tmax[r] = fmaxf(tmax[r], s[j][r]);
+        }
+      }
+      bool need = false;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) need |= tmax[r] > m[r] + kLazyRescale;
+      if (__any(need)) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const float mn = fmaxf(m[r], tmax[r]);
+          const float alpha = rescale_factor(m[r], mn);
+          l[r] *= alpha;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+          m[r] = mn;
         }
-        m[r] = mn;
       }
-    }
-    float mref[RB];
+      float mref[RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) mref[r] = m[r] == -INFINITY ? 0.0f : m[r];
+      for (int r = 0; r < RB; ++r) mref[r] = m[r] == -INFINITY ? 0.0f : m[r];
 #pragma unroll
-    for (int j = 0; j < KT; ++j) {
-      float vf[EPL];
-      if constexpr (!ENERGY) widen<T>(vc[j], vf);
+      for (int j = 0; j < KT; ++j) {
+        float vf[EPL];
+        widen<T>(vc[j], vf);
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const float p = fast_exp2(s[j][r] - mref[r]);
-        l[r] += p;
-        if constexpr (!ENERGY) {
+        for (int r = 0; r < RB; ++r) {
+          const float p = fast_exp2(s[j][r] - mref[r]);
+          l[r] += p;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
         }
       }
     }
+  };
+
+  if constexpr (LOADV) {
+    uint4 kc[KT], vc[KT];
+    int32_t pn[KT];
+    int tile = wave;
+    if (tile < n_tiles) {
+      int32_t pc[KT];
+      lookup_tile(tile, pc);
+      load_tile(tile, pc, kc, vc);
+      lookup_tile(next_of(tile), pn);
+    }
+    for (; tile < n_tiles; tile += kWaves) {
+      int32_t pnn[KT];
+      if constexpr (PAGED) lookup_tile(next_of(next_of(tile)), pnn);
+      uint4 kn[KT], vn[KT];
+      load_tile(next_of(tile), pn, kn, vn);
+      compute(tile, kc, vc);
 #pragma unroll
-    for (int j = 0; j < KT; ++j) {
-      kc[j] = kn[j];
-      if constexpr (LOADV) vc[j] = vn[j];
-      if constexpr (PAGED) pn[j] = pnn[j];
+      for (int j = 0; j < KT; ++j) {
+        kc[j] = kn[j];
+        vc[j] = vn[j];
+        if constexpr (PAGED) pn[j] = pnn[j];
+      }
+    }
+  } else {
+    uint4 kb[NSTG][KT], vb[NSTG][1];
+    int32_t pb[NSTG][KT];
+    if (wave < n_tiles) {
+#pragma unroll
+      for (int st = 0; st < NSTG; ++st) {
+        int32_t p0[KT];
+        lookup_tile(wave + st * kWaves, p0);
+        load_tile(wave + st * kWaves, p0, kb[st], vb[st]);
+        if constexpr (PAGED) lookup_tile(wave + st * kWaves + RSTEP, pb[st]);
+      }
+    }
+    for (int base = wave; base < n_tiles; base += RSTEP) {
+#pragma unroll
+      for (int st = 0; st < NSTG; ++st) {
+        const int tile = base + st * kWaves;
+        if (tile >= n_tiles) break;  // wave-uniform
+        compute(tile, kb[st], vb[st]);
+        load_tile(tile + RSTEP, pb[st], kb[st], vb[st]);
+        if constexpr (PAGED) lookup_tile(tile + 2 * RSTEP, pb[st]);
+      }
     }
   }
 
-  // Merge the KPW key slots of the wave (lanes with equal kl).
+  // Merge the KPW key slots of the wave (lanes with equal kl, hence the same
+  // rows).
 #pragma unroll
   for (int off = LPK; off < kWave; off *= 2) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
+    for (int r = 0; r < NS_ROWS; ++r) {
       const float mo = __shfl_xor(m[r], off);
       const float lo = __shfl_xor(l[r], off);
       const float M = fmaxf(m[r], mo);
@@ -290,15 +431,20 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
   auto &so = sh.o;
   __syncthreads();
   if (kr == 0) {
+    if constexpr (ENERGY) {
+      if (kl < RB) {  // lanes 0 .. RB-1 of a key row own distinct rows
+        sm[wave][my_row] = m[0];
+        sl[wave][my_row] = l[0];
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      if constexpr (!ENERGY) {
+      for (int r = 0; r < RB; ++r) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) so[wave][r][kl * EPL + e] = o[r][e];
-      }
-      if (kl == 0) {
-        sm[wave][r] = m[r];
-        sl[wave][r] = l[r];
+        if (kl == 0) {
+          sm[wave][r] = m[r];
+          sl[wave][r] = l[r];
+        }
       }
     }
   }
