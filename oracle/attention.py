@@ -35,6 +35,14 @@ What it computes, and where that is stated:
   attention into one GEMM over the shared prefilled KV and one over each
   sample's decoded KV, as an exact rewrite.  The oracle therefore does not
   split: it attends each sample over the concatenation [prefix ; suffix].
+* ``attend_anchor_blocks`` -- Star Attention's context encoding (phase 1 on
+  the Star Attention page): the context is cut into blocks and every block
+  but the first is processed with the first block, the anchor, placed in
+  front of it.  Reading fixed here where the page is silent: within the
+  block attention is causal, and every anchor key is visible to every query
+  of the block (the anchor precedes it), so block b's query token i attends
+  over [anchor ; block b] causally, i.e. ``attend`` with q_len = Lb over the
+  concatenation.
 
 Conventions fixed where the pages are silent:
   * natural-log logsumexp of the *scaled* logits;
@@ -160,6 +168,28 @@ def attend_bifurcated(q: np.ndarray, kp: np.ndarray, vp: np.ndarray, ks: np.ndar
             vcat = np.concatenate([vp64[kvh], _widen(vs[s, kvh])], axis=0)
             for h in range(kvh * G, (kvh + 1) * G):
                 O[s, h], lse[s, h] = attend_row(q[s, h], kcat, vcat, scale)
+    return O, lse
+
+
+def attend_anchor_blocks(q: np.ndarray, ka: np.ndarray, va: np.ndarray, kb: np.ndarray,
+                         vb: np.ndarray, scale: float, blocks: Optional[Sequence[int]] = None):
+    """Context encoding with an anchor block, per block of queries.
+
+    q [N][Lb][Hq][D] (the queries of N context blocks); ka, va [Hkv][A][D]
+    (the anchor block); kb, vb [N][Hkv][Lb][D] (each block's own keys and
+    values).  Block b's query token i attends over [anchor ; block b] with
+    every anchor key visible and the block's own keys t <= i.
+    Returns (O [N][Lb][Hq][D], lse [N][Lb][Hq]); blocks not listed hold NaN.
+    """
+    N, Lb, Hq, D = q.shape
+    Hkv, A, _ = ka.shape
+    O = np.full((N, Lb, Hq, D), np.nan)
+    lse = np.full((N, Lb, Hq), np.nan)
+    for b in (range(N) if blocks is None else blocks):
+        kc = np.concatenate([_widen(ka), _widen(kb[b])], axis=1)[None]  # [1][Hkv][A+Lb][D]
+        vc = np.concatenate([_widen(va), _widen(vb[b])], axis=1)[None]
+        Ob, lb = attend(q[b][None], kc, vc, [A + Lb], scale, causal=True)
+        O[b], lse[b] = Ob[0], lb[0]
     return O, lse
 
 

@@ -17,7 +17,9 @@ raises AssertionError when ``impl`` disagrees with:
 * paging: hand-worked paged caches, and pools written by a pure-Python
   scatter (both page layouts, shared pages) resolve to the dense cache;
 * row energies: F(0) is the row's logsumexp, and closed forms for constant
-  values and a single key.
+  values and a single key;
+* anchor-block context encoding: brute force on tiny inputs, and for two
+  blocks the second block's result equals global causal attention.
 """
 from __future__ import annotations
 
@@ -471,6 +473,51 @@ def pin_energy_rows(impl, seed: int = 29):
             _close(F1[b, 0, h], s0, what="single-key F(zeta)")
 
 
+# ----------------------------------------------------------------------------
+# Anchor-block context encoding (Star Attention, phase 1)
+# ----------------------------------------------------------------------------
+def _brute_anchor(q, ka, va, kb, vb, scale):
+    N, Lb, Hq, D = q.shape
+    Hkv, A, _ = ka.shape
+    G = Hq // Hkv
+    O = np.zeros(q.shape); lse = np.zeros((N, Lb, Hq))
+    for b in range(N):
+        for i in range(Lb):
+            for h in range(Hq):
+                kv = h // G
+                keys = [ka[kv, t] for t in range(A)] + [kb[b, kv, t] for t in range(i + 1)]
+                vals = [va[kv, t] for t in range(A)] + [vb[b, kv, t] for t in range(i + 1)]
+                s = [scale * math.fsum(float(q[b, i, h, j]) * float(k[j]) for j in range(D)) for k in keys]
+                M = max(s); Z = math.fsum(math.exp(x - M) for x in s)
+                lse[b, i, h] = M + math.log(Z)
+                for j in range(D):
+                    O[b, i, h, j] = math.fsum(math.exp(s[t] - M) / Z * float(vals[t][j]) for t in range(len(s)))
+    return O, lse
+
+
+def pin_anchor_blocks(impl, seed: int = 31):
+    rng = np.random.default_rng(seed)
+    # brute force on tiny inputs
+    for (N, Lb, Hkv, G, D, A) in ((2, 3, 1, 2, 3, 4), (3, 2, 2, 1, 2, 1), (1, 4, 1, 1, 5, 0)):
+        q = rng.standard_normal((N, Lb, Hkv * G, D)); ka = rng.standard_normal((Hkv, A, D))
+        va = rng.standard_normal((Hkv, A, D)); kb = rng.standard_normal((N, Hkv, Lb, D))
+        vb = rng.standard_normal((N, Hkv, Lb, D))
+        O, lse = impl.attend_anchor_blocks(q, ka, va, kb, vb, 0.6)
+        Ob, lb = _brute_anchor(q, ka, va, kb, vb, 0.6)
+        _close(O, Ob, what="anchor blocks vs brute force O")
+        _close(lse, lb, what="anchor blocks vs brute force lse")
+    # With two blocks, block 1 with block 0 as its anchor sees exactly what
+    # global causal attention over the whole context shows it.
+    Lb, Hkv, G, D = 6, 2, 2, 4
+    q = rng.standard_normal((1, 2 * Lb, Hkv * G, D)); k = rng.standard_normal((1, Hkv, 2 * Lb, D))
+    v = rng.standard_normal((1, Hkv, 2 * Lb, D))
+    Og, lg = impl.attend(q, k, v, [2 * Lb], 0.5, True)
+    O1, l1 = impl.attend_anchor_blocks(q[0, Lb:][None], k[0, :, :Lb], v[0, :, :Lb],
+                                       k[0, :, Lb:][None], v[0, :, Lb:][None], 0.5)
+    _close(O1[0], Og[0, Lb:], what="block 1 with anchor = global causal O")
+    _close(l1[0], lg[0, Lb:], what="block 1 with anchor = global causal lse")
+
+
 ALL_PINS = [pin_golden, pin_brute_force, pin_library, pin_closed_forms, pin_invariants,
             pin_causal_truncation, pin_energy_gradient, pin_chunk_merge, pin_bifurcated,
-            pin_paged_golden, pin_paged_scatter, pin_energy_rows]
+            pin_paged_golden, pin_paged_scatter, pin_energy_rows, pin_anchor_blocks]

@@ -3,8 +3,9 @@ catch every one of them: a dropped scale, a wrong GQA index, an off-by-one
 causal window, K and V swapped, a log2 logsumexp, a missing normalisation,
 an unshifted exponential, a merge that forgets to rescale, an energy that
 drops its zeta term, paged-cache lookups with swapped strides, an ignored
-block table or quotient and remainder exchanged, and row energies that ignore
-the causal window or the GQA grouping.  None of these variants is used anywhere else."""
+block table or quotient and remainder exchanged, row energies that ignore
+the causal window or the GQA grouping, and an anchor placed after the block
+or a block attended without its causal mask.  None of these variants is used anywhere else."""
 import math
 import types
 
@@ -160,6 +161,24 @@ MERGE_MISTAKES = ["merge_no_rescale_o", "merge_inverted_weight"]
 ENERGY_MISTAKES = ["energy_no_zeta", "energy_scaled_zeta"]
 PAGING_MISTAKES = ["page_strides_swapped", "page_quotient_remainder_swapped", "page_ignores_table"]
 ENERGY_ROWS_MISTAKES = ["energy_rows_no_causal", "energy_rows_gqa_modulo"]
+ANCHOR_MISTAKES = ["anchor_after_block", "anchor_block_not_causal"]
+
+
+def _anchor_factory(attend, mistake):
+    def attend_anchor_blocks(q, ka, va, kb, vb, scale, blocks=None):
+        N, Lb, Hq, D = q.shape
+        A = ka.shape[1]
+        O = np.zeros(q.shape); lse = np.zeros((N, Lb, Hq))
+        for b in range(N):
+            if mistake == "anchor_after_block":
+                kc = np.concatenate([kb[b], ka], axis=1)[None]; vc = np.concatenate([vb[b], va], axis=1)[None]
+            else:
+                kc = np.concatenate([ka, kb[b]], axis=1)[None]; vc = np.concatenate([va, vb[b]], axis=1)[None]
+            causal = mistake != "anchor_block_not_causal"
+            o, l = attend(q[b][None], kc, vc, [A + Lb], scale, causal)
+            O[b], lse[b] = o[0], l[0]
+        return O, lse
+    return attend_anchor_blocks
 
 
 def _impl(mistake):
@@ -169,6 +188,7 @@ def _impl(mistake):
     return types.SimpleNamespace(
         attend=att,
         attend_bifurcated=_bif_factory(att),
+        attend_anchor_blocks=_anchor_factory(att, mistake),
         gather=gather,
         attend_paged=_attend_paged_factory(att, gather),
         energy=energy,
@@ -188,7 +208,7 @@ def test_faithful_variant_passes_all_pins():
 
 
 @pytest.mark.parametrize("mistake", ATTEND_MISTAKES + MERGE_MISTAKES + ENERGY_MISTAKES +
-                         PAGING_MISTAKES + ENERGY_ROWS_MISTAKES)
+                         PAGING_MISTAKES + ENERGY_ROWS_MISTAKES + ANCHOR_MISTAKES)
 def test_pins_catch_planted_mistake(mistake):
     impl = _impl(mistake)
     caught = []
