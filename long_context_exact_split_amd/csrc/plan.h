@@ -20,8 +20,10 @@ constexpr int64_t kMaxUnits = int64_t(1) << 46;  // B * Hkv * row_blocks * max_k
 // tokens per CU, which measured fastest on MI355X (each CU streams one long
 // run of K/V).  Overridable with ATTN_DECODE_ITEMS_PER_CU for experiments.
 constexpr int kItemsPerCu = 1;
+// Tokens per CU below which the vector-ALU kernel gets twice the workgroups.
+constexpr int64_t kShortShare = 2048;
 
-int items_per_cu();
+int items_per_cu(int kernel, int64_t units, int cu_count);
 attn_status_t validate_desc(const attn_desc_t *d);
 // Host checks of a paging description against its descriptor (null paged:
 // dense caches, always valid).  Fills *pg for the kernels.

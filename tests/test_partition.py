@@ -52,6 +52,15 @@ def test_query_blocks_go_to_mfma():
     assert p["kernel"] == 0 and p["rows_per_block"] == 8 and p["row_blocks"] == 4
 
 
+def test_short_shares_get_two_workgroups_per_cu():
+    # 64 sequences x 8 KV heads x 512 tokens: 1024 tokens per CU
+    p = plan(batch=64, max_kv_len=512)
+    assert p["kernel"] == 0 and p["work_items"] == 512
+    # the MFMA kernels keep one workgroup per CU
+    p = plan(batch=64, q_len=4, num_q_heads=64, max_kv_len=512, causal=True)
+    assert p["kernel"] == 1 and p["work_items"] == 256
+
+
 def test_small_calls_use_fewer_workgroups():
     p = plan(num_q_heads=1, num_kv_heads=1, max_kv_len=4096)
     assert p["work_items"] == 16   # at least 256 tokens per workgroup
