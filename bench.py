@@ -37,6 +37,8 @@ WORKLOADS = {
     "long_context_1m_zeta": "long-context GQA energy F(zeta) from K and V (1M tokens)",
     "paged_long_context_1m": "long-context GQA decode (1M tokens) in 16-token head-major pages",
     "paged_llama31_70b_ragged": "Llama-3.1-70B-shaped ragged decode in 16-token token-major pages",
+    "anchor_prefill": "anchor-block context encoding: 2 blocks of 8192 tokens behind an 8192-token "
+                      "anchor (Hq=32, Hkv=8, d=128)",
 }
 # Workloads that reuse another one's inputs: name -> (inputs of, call mode, paging)
 VARIANTS = {
@@ -158,6 +160,8 @@ def make_workload(name):
         return inputs.single_query_fp32(seed=1)
     if name == "bifurcated_prefix":
         return inputs.bifurcated_prefix(seed=4)
+    if name == "anchor_prefill":
+        return inputs.anchor_blocks(seed=6)
     raise ValueError(name)
 
 
@@ -320,6 +324,57 @@ class BifurcatedRunner:
         return O[:, None], lse[:, None]
 
 
+class AnchorRunner:
+    """One anchor-block context encoding call (anchor split, local split,
+    merge), timed as one unit; bound by the matrix cores."""
+
+    def __init__(self, torch, w):
+        from long_context_exact_split_amd import binding
+        self.w, self.binding = w, binding
+        self.t = [dev(torch, x) for x in (w.q, w.ka, w.va, w.kb, w.vb)]
+        N, Lb, Hq, D = w.q.shape
+        Hkv, A = w.Hkv, w.A
+        self.out = torch.empty((N, Lb, Hq, D), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((N, Lb, Hq), dtype=torch.float32, device="cuda")
+        desc = binding.anchor_desc(self.t[0], self.t[1], self.t[3], w.scale)
+        import ctypes
+        n = ctypes.c_size_t(0)
+        assert binding.load_library().attn_anchor_workspace_bytes(ctypes.byref(desc),
+                                                                  ctypes.byref(n)) == 0
+        self.ws = torch.empty(max(1, n.value), dtype=torch.uint8, device="cuda")
+        self.plan = {"blocks": N, "block_len": Lb, "anchor_len": A, "workspace_bytes": n.value}
+        self.kv_tokens = N * (A + Lb)
+        self.kv_bytes = 2 * (A + N * Lb) * Hkv * D * 2
+        self.q_bytes = N * Lb * Hq * D * 2
+        self.out_bytes = N * Lb * Hq * (D + 1) * 4
+        G = Hq // Hkv
+        # visible (query row, key) pairs: every anchor key, and the causal triangle
+        pairs = N * Hkv * G * (Lb * A + Lb * (Lb + 1) // 2)
+        self.flops = 4 * D * pairs
+        self.kernel = "anchor prefill (anchor split + local causal split + merge)"
+
+    def first(self):
+        self.binding.prefill_anchor(*self.t, scale=self.w.scale, out=self.out, lse=self.lse,
+                                    workspace=self.ws)
+
+    def second(self):
+        pass
+
+    def outputs(self):
+        return self.out.cpu().numpy(), self.lse.cpu().numpy()
+
+    def oracle_rows(self, n_rows):
+        w = self.w
+        N, Lb, Hq, _ = w.q.shape
+        rows = [(b, i, h) for b in range(N) for i in (0, Lb // 3, Lb - 1) for h in range(Hq)]
+        return rows[:: max(1, len(rows) // n_rows)][:n_rows]
+
+    def oracle(self, rows):
+        import oracle
+        w = self.w
+        return oracle.attend_anchor_blocks(w.q, w.ka, w.va, w.kb, w.vb, w.scale, rows=rows)
+
+
 def cpu_baseline(run, n_rows, O_gpu, lse_gpu):
     """Time the fp64 oracle on a sample of the workload's query rows (each row
     over its full visible cache) and check the GPU's values on those rows."""
@@ -360,6 +415,8 @@ def main():
           flush=True)
     if args.workload == "bifurcated_prefix":
         run = BifurcatedRunner(torch, w)
+    elif args.workload == "anchor_prefill":
+        run = AnchorRunner(torch, w)
     else:
         _, mode, paging = VARIANTS.get(args.workload, (None, "full", None))
         if paging is not None and args.page_size:
@@ -427,6 +484,13 @@ def main():
     }
     if args.workload == "bifurcated_prefix":
         result["kv_tokens_physical"] = w.Lp + w.S * w.Ls
+    if args.workload == "anchor_prefill":
+        # A dense contraction (256 and more query rows per KV tile): bound by
+        # the bf16 matrix cores, priced against their dense peak.
+        tf = result["tflops"]
+        result["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                              "kernel": run.kernel, "algorithmic_flops_per_launch": run.flops}
     if not args.no_ceiling:
         ceil = read_ceiling(torch)
         result["hbm_read_ceiling_gbps"] = ceil

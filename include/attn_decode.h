@@ -253,6 +253,36 @@ attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const v
                                      float *lse, void *workspace, size_t workspace_bytes,
                                      void *stream);
 
+/* Context encoding with an anchor block (Star Attention, phase 1: the
+ * context is cut into blocks, and every block after the first is processed
+ * with the first block, the anchor, placed in front of it).  Block b's query
+ * token i attends over [anchor ; block b]: every anchor key, and the block's
+ * own keys t <= i (causal within the block).  The anchor is read in place
+ * by every block (no copy), its part of each row is merged exactly with the
+ * block's own part.  bf16 only; D in {64, 128}; (Hq/Hkv) * block_len <=
+ * 65536.  The first block itself is the case anchor_len = 0.
+ *     Q  [N][Lb][Hq][D]; Ka, Va [Hkv][A][D]; Kb, Vb [N][Hkv][Lb][D]  (bf16)
+ *     O  [N][Lb][Hq][D] float32;  lse [N][Lb][Hq] float32
+ * Errors as for the decode entry points. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int64_t anchor_len;
+  float scale;
+  attn_dtype_t dtype;
+} attn_anchor_desc_t;
+
+attn_status_t attn_anchor_workspace_bytes(const attn_anchor_desc_t *desc, size_t *bytes);
+
+attn_status_t attn_prefill_anchor(const attn_anchor_desc_t *desc, const void *q,
+                                  const void *k_anchor, const void *v_anchor,
+                                  const void *k_blocks, const void *v_blocks, float *o,
+                                  float *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* Static text for a status code. */
 const char *attn_status_string(attn_status_t status);
 

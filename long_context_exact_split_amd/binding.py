@@ -24,7 +24,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DT
 EXPORTS = ("attn_decode_plan", "attn_workspace_bytes", "attn_decode_energy", "attn_decode",
            "attn_decode_partials", "attn_decode_merge", "attn_decode_energy_zeta",
            "attn_decode_paged", "attn_decode_energy_paged", "attn_decode_partials_paged",
-           "attn_bifurcated_workspace_bytes", "attn_decode_bifurcated", "attn_status_string")
+           "attn_bifurcated_workspace_bytes", "attn_decode_bifurcated",
+           "attn_anchor_workspace_bytes", "attn_prefill_anchor", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -61,6 +62,13 @@ class AttnBifDesc(ctypes.Structure):
     _fields_ = [("num_samples", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("prefix_len", ctypes.c_int64), ("suffix_len", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+class AttnAnchorDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_len", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("anchor_len", ctypes.c_int64),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
 
 
@@ -110,6 +118,9 @@ def load_library():
         lib.attn_decode_partials_paged.argtypes = [P(AttnDesc), P(AttnPagedKv)] + [
             c.c_void_p] * 4 + [c.c_size_t, c.c_void_p]
         lib.attn_bifurcated_workspace_bytes.argtypes = [P(AttnBifDesc), P(c.c_size_t)]
+        lib.attn_anchor_workspace_bytes.argtypes = [P(AttnAnchorDesc), P(c.c_size_t)]
+        lib.attn_prefill_anchor.argtypes = [P(AttnAnchorDesc)] + [c.c_void_p] * 8 + [
+            c.c_size_t, c.c_void_p]
         lib.attn_decode_bifurcated.argtypes = [P(AttnBifDesc)] + [c.c_void_p] * 8 + [
             c.c_size_t, c.c_void_p]
         for name in EXPORTS[:-1]:
@@ -484,4 +495,49 @@ def decode_bifurcated(q, k_prefix, v_prefix, k_suffix, v_suffix, *, scale: Optio
                                           _ptr(v_prefix), _ptr(k_suffix), _ptr(v_suffix),
                                           _ptr(out), _ptr(lse), _ptr(ws), nbytes,
                                           _stream_ptr(q.device)), "attn_decode_bifurcated")
+    return out, lse
+
+
+def anchor_desc(q, k_anchor, k_blocks, scale=None) -> AttnAnchorDesc:
+    if q.dim() != 4 or k_anchor.dim() != 3 or k_blocks.dim() != 4:
+        raise ValueError("q [N,Lb,Hq,D], k_anchor [Hkv,A,D], k_blocks [N,Hkv,Lb,D]")
+    N, Lb, Hq, D = q.shape
+    Hkv, A, Da = k_anchor.shape
+    if tuple(k_blocks.shape) != (N, Hkv, Lb, D) or Da != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k_anchor{tuple(k_anchor.shape)} "
+                         f"k_blocks{tuple(k_blocks.shape)}")
+    d = AttnAnchorDesc()
+    d.num_blocks, d.block_len, d.num_q_heads, d.num_kv_heads, d.head_dim = N, Lb, Hq, Hkv, D
+    d.anchor_len = A
+    d.scale = (1.0 / math.sqrt(D)) if scale is None else scale
+    d.dtype = _dtype_code(q)
+    return d
+
+
+def prefill_anchor(q, k_anchor, v_anchor, k_blocks, v_blocks, *, scale: Optional[float] = None,
+                   out=None, lse=None, workspace=None):
+    """Context encoding with an anchor block: returns (O float32 [N,Lb,Hq,D],
+    lse float32 [N,Lb,Hq]); block b's query i sees the whole anchor and its
+    block's keys t <= i."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensors(q, k_anchor, v_anchor, k_blocks, v_blocks)
+    if v_anchor.shape != k_anchor.shape or v_blocks.shape != k_blocks.shape:
+        raise ValueError("v tensors must match k tensors")
+    desc = anchor_desc(q, k_anchor, k_blocks, scale)
+    N, Lb, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty((N, Lb, Hq, D), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((N, Lb, Hq), dtype=torch.float32, device=q.device)
+        n = ctypes.c_size_t(0)
+        _check(lib.attn_anchor_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+               "attn_anchor_workspace_bytes")
+        ws = _workspace(n.value, q.device, workspace)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib.attn_prefill_anchor(ctypes.byref(desc), _ptr(q), _ptr(k_anchor), _ptr(v_anchor),
+                                       _ptr(k_blocks), _ptr(v_blocks), _ptr(out), _ptr(lse),
+                                       _ptr(ws), nbytes, _stream_ptr(q.device)),
+               "attn_prefill_anchor")
     return out, lse

@@ -217,6 +217,25 @@ attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans
   return ATTN_OK;
 }
 
+// Anchor-block context encoding: the anchor part as one call over a cache
+// shared by every block (sequence stride 0), the local part as a causal call
+// over each block's own cache; both leave records for the same rows.
+struct AnchorPlans {
+  attn_desc_t anc, loc;
+  attn_plan_t ap, lp;
+  size_t anc_bytes, total;
+};
+
+attn_status_t anchor_plans(const attn_anchor_desc_t *d, int cu, AnchorPlans *a) {
+  anchor_descs(d, &a->anc, &a->loc);
+  attn_status_t st;
+  if ((st = make_plan(&a->anc, cu, kMfma, &a->ap)) != ATTN_OK) return st;
+  if ((st = make_plan(&a->loc, cu, kMfma, &a->lp)) != ATTN_OK) return st;
+  a->anc_bytes = (size_t)round_up((int64_t)a->ap.workspace_bytes, 256);
+  a->total = a->anc_bytes + a->lp.workspace_bytes;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,13 +411,14 @@ attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const v
     const PartialLayout suf = carve(ws + b.pre_bytes, b.sp, desc->head_dim);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const KvPaging dense{};
     if (launch_split(&b.pre, b.pp,
-                     split_args(&b.pre, b.pp, q, k_prefix, v_prefix, nullptr, dense, pre),
+                     split_args(&b.pre, b.pp, q, k_prefix, v_prefix, nullptr,
+                                dense_paging(&b.pre), pre),
                      SplitMode::kFull, s) != hipSuccess)
       return ATTN_ERR_HIP;
     if (launch_split(&b.suf, b.sp,
-                     split_args(&b.suf, b.sp, q, k_suffix, v_suffix, nullptr, dense, suf),
+                     split_args(&b.suf, b.sp, q, k_suffix, v_suffix, nullptr,
+                                dense_paging(&b.suf), suf),
                      SplitMode::kFull, s) != hipSuccess)
       return ATTN_ERR_HIP;
     MergeArgs m{};
@@ -411,6 +431,82 @@ attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const v
     m.Hq = desc->num_q_heads;
     m.G = desc->num_q_heads / desc->num_kv_heads;
     m.R = m.G;
+    m.o = o;
+    m.lse = lse;
+    if (launch_merge(m, desc->head_dim, s) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_anchor_workspace_bytes(const attn_anchor_desc_t *desc, size_t *bytes) {
+  try {
+    attn_status_t st = validate_anchor(desc);
+    if (st != ATTN_OK) return st;
+    if (!bytes) return ATTN_ERR_NULL;
+    *bytes = 0;
+    if (desc->num_blocks == 0) return ATTN_OK;
+    int cu = 0;
+    if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
+    AnchorPlans a;
+    if ((st = anchor_plans(desc, cu, &a)) != ATTN_OK) return st;
+    *bytes = a.total;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+attn_status_t attn_prefill_anchor(const attn_anchor_desc_t *desc, const void *q,
+                                  const void *k_anchor, const void *v_anchor,
+                                  const void *k_blocks, const void *v_blocks, float *o,
+                                  float *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  try {
+    attn_status_t st = validate_anchor(desc);
+    if (st != ATTN_OK) return st;
+    const bool any = desc->num_blocks > 0;
+    if (any && (!q || !k_blocks || !v_blocks || !o || !lse ||
+                (desc->anchor_len > 0 && (!k_anchor || !v_anchor))))
+      return ATTN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_anchor, 16) || !aligned(v_anchor, 16) ||
+        !aligned(k_blocks, 16) || !aligned(v_blocks, 16) || !aligned(o, 4) || !aligned(lse, 4))
+      return ATTN_ERR_ALIGN;
+    if (!any) return ATTN_OK;
+    int cu = 0;
+    if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
+    AnchorPlans a;
+    if ((st = anchor_plans(desc, cu, &a)) != ATTN_OK) return st;
+    if (a.total > 0 && !workspace) return ATTN_ERR_NULL;
+    if (workspace_bytes < a.total) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+    char *ws = static_cast<char *>(workspace);
+    const PartialLayout anc = carve(ws, a.ap, desc->head_dim);
+    const PartialLayout loc = carve(ws + a.anc_bytes, a.lp, desc->head_dim);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    KvPaging shared = dense_paging(&a.anc);
+    shared.seq_stride = 0;  // every block reads the one anchor
+    (void)hipGetLastError();
+    if (launch_split(&a.anc, a.ap, split_args(&a.anc, a.ap, q, k_anchor, v_anchor, nullptr, shared, anc),
+                     SplitMode::kFull, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if (launch_split(&a.loc, a.lp,
+                     split_args(&a.loc, a.lp, q, k_blocks, v_blocks, nullptr,
+                                dense_paging(&a.loc), loc),
+                     SplitMode::kFull, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    MergeArgs m{};
+    m.map = work_map(&a.loc, a.lp);
+    m.part = loc;
+    m.has_shared = a.ap.work_items > 0;
+    m.shared_same_rows = 1;
+    m.smap = work_map(&a.anc, a.ap);
+    m.shared = anc;
+    m.q_len = desc->block_len;
+    m.Hq = desc->num_q_heads;
+    m.G = desc->num_q_heads / desc->num_kv_heads;
+    m.R = a.lp.rows;
     m.o = o;
     m.lse = lse;
     if (launch_merge(m, desc->head_dim, s) != hipSuccess) return ATTN_ERR_HIP;

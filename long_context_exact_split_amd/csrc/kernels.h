@@ -35,13 +35,15 @@ struct SplitArgs {
 
 // Merge of every record of a row, then normalisation.  Output row r of
 // (b, kvh) merges the records of segment ((b*Hkv + kvh)*row_blocks + r/rows)
-// and, when has_shared, the records of the shared layout for its row
-// b*R + r of KV head kvh (records computed once for all batch entries, e.g.
-// a shared prefix whose query rows are every sample's rows).
+// and, when has_shared, the records a second split call left for it: with
+// shared_same_rows, that call had the same sequences and rows (row r of
+// sequence b); otherwise it was one sequence holding every sequence's rows,
+// row b*R + r of KV head kvh (a shared prefix computed once for all samples).
 struct MergeArgs {
   WorkMap map;
   PartialLayout part;
   int32_t has_shared;
+  int32_t shared_same_rows;
   WorkMap smap;
   PartialLayout shared;
   int32_t q_len, Hq, G, R;

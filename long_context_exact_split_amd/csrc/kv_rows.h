@@ -29,7 +29,7 @@ struct KvRows {
       mask = (1 << a.pg.page_shift) - 1;
     } else {
       bt = nullptr;
-      origin = ((int64_t)b * a.map.Hkv + kvh) * a.map.L_max * D;
+      origin = (int64_t)b * a.pg.seq_stride + (int64_t)kvh * a.map.L_max * D;
       page_stride = token_stride = num_pages = 0;
       shift = mask = 0;
     }

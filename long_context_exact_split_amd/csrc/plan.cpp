@@ -55,9 +55,16 @@ attn_status_t validate_desc(const attn_desc_t *d) {
   return ATTN_OK;
 }
 
+KvPaging dense_paging(const attn_desc_t *d) {
+  KvPaging pg{};
+  pg.seq_stride = (int64_t)d->num_kv_heads * d->max_kv_len * d->head_dim;
+  return pg;
+}
+
 attn_status_t validate_paged(const attn_desc_t *d, const attn_paged_kv_t *paged, KvPaging *pg) {
-  *pg = KvPaging{};
+  *pg = dense_paging(d);
   if (!paged) return ATTN_OK;
+  pg->seq_stride = 0;
   const int64_t P = paged->page_size;
   if (P < 1 || P > (int64_t(1) << kMaxPageShift) || (P & (P - 1)) != 0) return ATTN_ERR_VALUE;
   if (paged->pages_per_seq < 1 || (int64_t)paged->pages_per_seq * P < d->max_kv_len)
@@ -199,6 +206,43 @@ void bifurcated_descs(const attn_bifurcated_desc_t *d, attn_desc_t *prefix, attn
   suffix->batch = d->num_samples;
   suffix->q_len = 1;
   suffix->max_kv_len = d->suffix_len;
+}
+
+}  // namespace attn
+
+namespace attn {
+
+attn_status_t validate_anchor(const attn_anchor_desc_t *d) {
+  if (!d) return ATTN_ERR_NULL;
+  if (d->dtype != ATTN_BF16) return d->dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_DTYPE;
+  if (d->num_blocks < 0 || d->block_len < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
+      d->num_q_heads % d->num_kv_heads != 0 || d->anchor_len < 0 ||
+      d->anchor_len > std::numeric_limits<int32_t>::max() || d->head_dim < 1)
+    return ATTN_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(d->scale)) return ATTN_ERR_VALUE;
+  if ((int64_t)(d->num_q_heads / d->num_kv_heads) * d->block_len > kMaxRows)
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+void anchor_descs(const attn_anchor_desc_t *d, attn_desc_t *anchor, attn_desc_t *local) {
+  attn_desc_t c{};
+  c.batch = d->num_blocks;
+  c.q_len = d->block_len;
+  c.num_q_heads = d->num_q_heads;
+  c.num_kv_heads = d->num_kv_heads;
+  c.head_dim = d->head_dim;
+  c.kv_lens = nullptr;
+  c.scale = d->scale;
+  c.chunk_len = 0;
+  c.dtype = d->dtype;
+  *anchor = c;
+  anchor->causal = 0;               // every anchor key precedes the block
+  anchor->max_kv_len = d->anchor_len;
+  *local = c;
+  local->causal = 1;                // query i sees the block's keys t <= i
+  local->max_kv_len = d->block_len;
 }
 
 }  // namespace attn

@@ -29,10 +29,14 @@ attn_status_t validate_desc(const attn_desc_t *d);
 // dense caches, always valid).  Fills *pg for the kernels.
 constexpr int kMaxPageShift = 20;
 attn_status_t validate_paged(const attn_desc_t *d, const attn_paged_kv_t *paged, KvPaging *pg);
+// Addressing of a dense [B][Hkv][L_max][D] cache.
+KvPaging dense_paging(const attn_desc_t *d);
 attn_status_t make_plan(const attn_desc_t *d, int cu_count, bool mfma_available, attn_plan_t *p);
 size_t partial_bytes(int64_t records, int head_dim);
 WorkMap work_map(const attn_desc_t *d, const attn_plan_t &p);
 attn_status_t validate_bifurcated(const attn_bifurcated_desc_t *d);
 void bifurcated_descs(const attn_bifurcated_desc_t *d, attn_desc_t *prefix, attn_desc_t *suffix);
+attn_status_t validate_anchor(const attn_anchor_desc_t *d);
+void anchor_descs(const attn_anchor_desc_t *d, attn_desc_t *anchor, attn_desc_t *local);
 
 }  // namespace attn

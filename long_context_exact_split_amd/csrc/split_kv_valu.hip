@@ -542,9 +542,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
       where[5] = 0;
       if (a.has_shared) {
         const int RBs = a.shared.rows;
-        const int rs = b * a.R + r;
-        const int64_t ssig = (int64_t)kvh * a.smap.row_blocks + rs / RBs;
-        const SlotRange sr = segment_slots(a.smap, total_units(a.smap), 0, ssig);
+        const int sb = a.shared_same_rows ? b : 0;              // sequence in the shared call
+        const int rs = a.shared_same_rows ? r : b * a.R + r;  // row in that sequence
+        const int64_t ssig = ((int64_t)sb * a.smap.Hkv + kvh) * a.smap.row_blocks + rs / RBs;
+        const SlotRange sr = segment_slots(a.smap, total_units(a.smap), sb, ssig);
         where[3] = sr.count;
         where[4] = sr.first * RBs + rs % RBs;
         where[5] = sr.stride * RBs;

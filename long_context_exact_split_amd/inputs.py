@@ -304,6 +304,38 @@ def bifurcated_prefix(seed: int = 4, S: int = 64, Hq: int = 32, Hkv: int = 8, D:
                               ks=ks, vs=vs)
 
 
+@dataclasses.dataclass
+class AnchorWorkload:
+    """Context encoding with an anchor block: N context blocks of Lb tokens,
+    each processed behind an A-token anchor.  Q [N][Lb][Hq][D]; Ka, Va
+    [Hkv][A][D]; Kb, Vb [N][Hkv][Lb][D]; bf16 bits."""
+
+    name: str
+    seed: int
+    Hq: int
+    Hkv: int
+    D: int
+    A: int
+    scale: float
+    q: np.ndarray
+    ka: np.ndarray
+    va: np.ndarray
+    kb: np.ndarray
+    vb: np.ndarray
+
+
+def anchor_blocks(seed: int = 6, N: int = 2, Lb: int = 8192, A: int = 8192, Hq: int = 32,
+                  Hkv: int = 8, D: int = 128) -> AnchorWorkload:
+    """Anchor-block context encoding: N = 2 blocks of 8192 tokens behind an
+    8192-token anchor, 32 query / 8 KV heads, d = 128, bf16 N(0,1)."""
+    ss = np.random.SeedSequence(seed)
+    streams = [np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(5)]
+    shapes = [(N, Lb, Hq, D), (Hkv, A, D), (Hkv, A, D), (N, Hkv, Lb, D), (N, Hkv, Lb, D)]
+    q, ka, va, kb, vb = (_normal_bits(r, sh, True) for r, sh in zip(streams, shapes))
+    return AnchorWorkload(name="anchor_prefill", seed=seed, Hq=Hq, Hkv=Hkv, D=D, A=A,
+                          scale=1.0 / math.sqrt(D), q=q, ka=ka, va=va, kb=kb, vb=vb)
+
+
 # ----------------------------------------------------------------------------
 # Paged KV caches
 # ----------------------------------------------------------------------------

@@ -172,23 +172,29 @@ def attend_bifurcated(q: np.ndarray, kp: np.ndarray, vp: np.ndarray, ks: np.ndar
 
 
 def attend_anchor_blocks(q: np.ndarray, ka: np.ndarray, va: np.ndarray, kb: np.ndarray,
-                         vb: np.ndarray, scale: float, blocks: Optional[Sequence[int]] = None):
+                         vb: np.ndarray, scale: float, blocks: Optional[Sequence[int]] = None,
+                         rows: Optional[Iterable[Tuple[int, int, int]]] = None):
     """Context encoding with an anchor block, per block of queries.
 
     q [N][Lb][Hq][D] (the queries of N context blocks); ka, va [Hkv][A][D]
     (the anchor block); kb, vb [N][Hkv][Lb][D] (each block's own keys and
     values).  Block b's query token i attends over [anchor ; block b] with
     every anchor key visible and the block's own keys t <= i.
-    Returns (O [N][Lb][Hq][D], lse [N][Lb][Hq]); blocks not listed hold NaN.
+    ``rows`` restricts the work to the listed (block, token, head) rows.
+    Returns (O [N][Lb][Hq][D], lse [N][Lb][Hq]); rows not computed hold NaN.
     """
     N, Lb, Hq, D = q.shape
     Hkv, A, _ = ka.shape
     O = np.full((N, Lb, Hq, D), np.nan)
     lse = np.full((N, Lb, Hq), np.nan)
-    for b in (range(N) if blocks is None else blocks):
+    want = {}
+    if rows is not None:
+        for (b, i, h) in rows:
+            want.setdefault(b, []).append((0, i, h))
+    for b in (range(N) if blocks is None else blocks) if rows is None else sorted(want):
         kc = np.concatenate([_widen(ka), _widen(kb[b])], axis=1)[None]  # [1][Hkv][A+Lb][D]
         vc = np.concatenate([_widen(va), _widen(vb[b])], axis=1)[None]
-        Ob, lb = attend(q[b][None], kc, vc, [A + Lb], scale, causal=True)
+        Ob, lb = attend(q[b][None], kc, vc, [A + Lb], scale, causal=True, rows=want.get(b))
         O[b], lse[b] = Ob[0], lb[0]
     return O, lse
 

@@ -71,6 +71,9 @@ int main(void) {
   F(attn_plan_t, record_slots) F(attn_plan_t, cu_count) F(attn_plan_t, workspace_bytes)
   printf("attn_bifurcated_desc_t %zu\\n", sizeof(attn_bifurcated_desc_t));
   F(attn_bifurcated_desc_t, prefix_len) F(attn_bifurcated_desc_t, scale) F(attn_bifurcated_desc_t, dtype)
+  printf("attn_anchor_desc_t %zu\\n", sizeof(attn_anchor_desc_t));
+  F(attn_anchor_desc_t, head_dim) F(attn_anchor_desc_t, anchor_len) F(attn_anchor_desc_t, scale)
+  F(attn_anchor_desc_t, dtype)
   printf("attn_paged_kv_t %zu\\n", sizeof(attn_paged_kv_t));
   F(attn_paged_kv_t, pages_per_seq) F(attn_paged_kv_t, page_size) F(attn_paged_kv_t, num_pages)
   F(attn_paged_kv_t, page_stride) F(attn_paged_kv_t, head_stride) F(attn_paged_kv_t, token_stride)
@@ -83,7 +86,8 @@ int main(void) {
     got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True,
                                                                text=True, check=True).stdout.split("\n") if line)
     structs = {"attn_desc_t": binding.AttnDesc, "attn_plan_t": binding.AttnPlan,
-               "attn_bifurcated_desc_t": binding.AttnBifDesc, "attn_paged_kv_t": binding.AttnPagedKv}
+               "attn_bifurcated_desc_t": binding.AttnBifDesc, "attn_paged_kv_t": binding.AttnPagedKv,
+               "attn_anchor_desc_t": binding.AttnAnchorDesc}
     for key, val in got.items():
         if "." in key:
             s, f = key.split(".")
@@ -228,6 +232,37 @@ def test_paged_and_zeta_null_checks(lib):
     assert binding.STATUS[lib.attn_decode_energy_zeta(ctypes.byref(d), *z)] == "ATTN_ERR_ALIGN"
     z = list(args); z[2] = 0  # F(zeta) reads V
     assert binding.STATUS[lib.attn_decode_energy_zeta(ctypes.byref(d), *z)] == "ATTN_ERR_NULL"
+
+
+def test_anchor_validation(lib):
+    d = binding.AttnAnchorDesc()
+    d.num_blocks, d.block_len, d.num_q_heads, d.num_kv_heads, d.head_dim = 2, 64, 8, 2, 128
+    d.anchor_len, d.scale, d.dtype = 100, 0.1, binding.ATTN_BF16
+    args = [16] * 7 + [16, 1 << 30, None]
+
+    def st(*a):
+        return binding.STATUS[lib.attn_prefill_anchor(ctypes.byref(d), *(a or args))]
+    d.num_q_heads = 7
+    assert st() == "ATTN_ERR_SHAPE"
+    d.num_q_heads = 8
+    d.block_len = 0
+    assert st() == "ATTN_ERR_SHAPE"
+    d.block_len = 20000  # 4 x 20000 rows per KV head
+    assert st() == "ATTN_ERR_UNSUPPORTED"
+    d.block_len = 64
+    d.dtype = binding.ATTN_F32
+    assert st() == "ATTN_ERR_UNSUPPORTED"
+    d.dtype = binding.ATTN_BF16
+    d.anchor_len = -1
+    assert st() == "ATTN_ERR_SHAPE"
+    d.anchor_len = 100
+    assert st(*([16] * 3 + [0] + [16] * 4 + [1, None])) == "ATTN_ERR_NULL"   # k_blocks
+    assert st(*([16] * 5 + [18] + [16] * 2 + [1, None])) == "ATTN_ERR_ALIGN"  # o not 4-byte aligned
+    assert st(*([16] * 3 + [24] + [16] * 4 + [1, None])) == "ATTN_ERR_ALIGN"  # k_blocks not 16-byte
+    d.anchor_len = 0  # no anchor: its tensors may be null
+    assert st(*([16, 0, 0] + [16] * 5 + [1 << 30, None])) not in ("ATTN_ERR_NULL", "ATTN_ERR_ALIGN")
+    d.num_blocks = 0
+    assert lib.attn_prefill_anchor(ctypes.byref(d), *args) == 0
 
 
 def test_status_strings(lib):
