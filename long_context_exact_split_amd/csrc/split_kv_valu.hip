@@ -494,12 +494,54 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   }
 }
 
-// One workgroup per output row.  The row's records are read in parallel:
-// 16 bytes of o per lane, kMergeThreads / (D/4) records per pass, so a row of
-// ~100 records takes a handful of passes instead of a serial walk.  The max
-// over the records is a block-wide reduction (DPP within waves, LDS across
-// them); each record is then rescaled once and the partial sums of the
-// record groups are added through LDS in a fixed order (deterministic).
+// Where a merge row's records are: P pieces of its own segment (record index
+// prow + c*pstride) and S pieces of the shared call (srow + c*sstride).
+struct RowRecords {
+  int64_t prow, pstride, srow, sstride;
+  int32_t P, S;
+};
+
+// Run by a whole wave (the sums of sequence lengths are wave reductions);
+// every lane gets the result.
+__device__ __forceinline__ RowRecords row_records(const MergeArgs &a, int b, int kvh, int r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t tot = 0, pre = 0;
+  if (a.map.mode != 0) {
+    for (int bb = lane; bb < a.map.B; bb += kWave) {
+      const int64_t L = seq_len(a.map, bb);
+      tot += L;
+      pre += bb < b ? L : 0;
+    }
+    tot = wave_sum_i64(tot);
+    pre = wave_sum_i64(pre);
+  }
+  RowRecords rr{};
+  const int RBp = a.part.rows;
+  const int64_t sigma = ((int64_t)b * a.map.Hkv + kvh) * a.map.row_blocks + r / RBp;
+  const SlotRange pr = segment_slots_at(a.map, tot * segs_per_seq(a.map), pre, b, sigma);
+  rr.P = (int32_t)pr.count;
+  rr.prow = pr.first * RBp + r % RBp;
+  rr.pstride = pr.stride * RBp;
+  if (a.has_shared) {
+    const int RBs = a.shared.rows;
+    const int sb = a.shared_same_rows ? b : 0;              // sequence in the shared call
+    const int rs = a.shared_same_rows ? r : b * a.R + r;  // row in that sequence
+    const int64_t ssig = ((int64_t)sb * a.smap.Hkv + kvh) * a.smap.row_blocks + rs / RBs;
+    const SlotRange sr = segment_slots(a.smap, total_units(a.smap), sb, ssig);
+    rr.S = (int32_t)sr.count;
+    rr.srow = sr.first * RBs + rs % RBs;
+    rr.sstride = sr.stride * RBs;
+  }
+  return rr;
+}
+
+// Rows with many records (a long cache cut into many pieces): one workgroup
+// per output row.  The row's records are read in parallel: 16 bytes of o per
+// lane, kMergeThreads / (D/4) records per pass, so a row of ~100 records
+// takes a handful of passes instead of a serial walk.  The max over the
+// records is a block-wide reduction (DPP within waves, LDS across them); each
+// record is then rescaled once and the partial sums of the record groups are
+// added through LDS in a fixed order (deterministic).
 constexpr int kMergeThreads = 256;
 
 template <int D, bool ENERGY>
@@ -515,46 +557,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   const int b = group / a.map.Hkv;
   const int kvh = group - b * a.map.Hkv;
 
-  // The row's records: its segment's pieces, then (optionally) the shared
-  // ones.  Wave 0 sums the sequence lengths (all, and those before b) in
-  // parallel; lane 0 locates the records; LDS broadcasts them.
-  __shared__ int64_t where[6];
+  __shared__ RowRecords where;
   if (wave == 0) {
-    int64_t tot = 0, pre = 0;
-    if (a.map.mode != 0) {
-      for (int bb = lane; bb < a.map.B; bb += kWave) {
-        const int64_t L = seq_len(a.map, bb);
-        tot += L;
-        pre += bb < b ? L : 0;
-      }
-      tot = wave_sum_i64(tot);
-      pre = wave_sum_i64(pre);
-    }
-    if (lane == 0) {
-      const int RBp = a.part.rows;
-      const int64_t sigma = (int64_t)group * a.map.row_blocks + r / RBp;
-      const SlotRange pr = segment_slots_at(a.map, tot * segs_per_seq(a.map), pre, b, sigma);
-      where[0] = pr.count;
-      where[1] = pr.first * RBp + r % RBp;
-      where[2] = pr.stride * RBp;
-      where[3] = 0;
-      where[4] = 0;
-      where[5] = 0;
-      if (a.has_shared) {
-        const int RBs = a.shared.rows;
-        const int sb = a.shared_same_rows ? b : 0;              // sequence in the shared call
-        const int rs = a.shared_same_rows ? r : b * a.R + r;  // row in that sequence
-        const int64_t ssig = ((int64_t)sb * a.smap.Hkv + kvh) * a.smap.row_blocks + rs / RBs;
-        const SlotRange sr = segment_slots(a.smap, total_units(a.smap), sb, ssig);
-        where[3] = sr.count;
-        where[4] = sr.first * RBs + rs % RBs;
-        where[5] = sr.stride * RBs;
-      }
-    }
+    const RowRecords rr = row_records(a, b, kvh, r);
+    if (lane == 0) where = rr;
   }
   __syncthreads();
-  const int P = (int)where[0], S = (int)where[3];
-  const int64_t prow = where[1], pstride = where[2], srow = where[4], sstride = where[5];
+  const int P = where.P, S = where.S;
+  const int64_t prow = where.prow, pstride = where.pstride, srow = where.srow,
+                sstride = where.sstride;
   auto rec_of = [&](int c) { return c < P ? prow + c * pstride : srow + (c - P) * sstride; };
   auto m_of = [&](int c) { return c < P ? a.part.m[prow + c * pstride] : a.shared.m[srow + (c - P) * sstride]; };
 
@@ -612,6 +623,62 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   }
 }
 
+// Rows with few records (most calls: a handful of pieces per segment): one
+// wave per output row, four rows per workgroup, so that hundreds of
+// thousands of short rows (a prefill's query rows) do not each pay for a
+// whole workgroup.  Records are combined one after another in index order
+// (deterministic); each lane holds D/64 of the row's outputs.
+constexpr int kRowsPerMergeBlock = 4;
+
+template <int D, bool ENERGY>
+__global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeArgs a) {
+  constexpr int EPL = D / kWave;  // output elements per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerMergeBlock + threadIdx.x / kWave;
+  const int64_t rows = (int64_t)a.map.B * a.map.Hkv * a.R;
+  if (row >= rows) return;  // whole waves; no workgroup barrier follows
+  const int r = (int)(row % a.R);
+  const int group = (int)(row / a.R);
+  const int b = group / a.map.Hkv;
+  const int kvh = group - b * a.map.Hkv;
+  const RowRecords rr = row_records(a, b, kvh, r);
+  const int n = rr.P + rr.S;
+  auto rec_of = [&](int c) { return c < rr.P ? rr.prow + c * rr.pstride : rr.srow + (c - rr.P) * rr.sstride; };
+
+  float M = -INFINITY;
+  for (int c = lane; c < n; c += kWave) {
+    const int64_t rec = rec_of(c);
+    M = fmaxf(M, c < rr.P ? a.part.m[rec] : a.shared.m[rec]);
+  }
+  M = wave_max(M);
+  float lsum = 0.0f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+#pragma unroll 4
+  for (int c = 0; c < n; ++c) {
+    const bool sh = c >= rr.P;
+    const int64_t rec = rec_of(c);
+    const float f = rescale_factor(sh ? a.shared.m[rec] : a.part.m[rec], M);
+    lsum += f * (sh ? a.shared.l[rec] : a.part.l[rec]);
+    if constexpr (!ENERGY) {
+      const float *op = (sh ? a.shared.o : a.part.o) + rec * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += f * op[e];
+    }
+  }
+  const int i = r / a.G;
+  const int h = kvh * a.G + (r - i * a.G);
+  const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
+  const bool empty = M == -INFINITY || !(lsum > 0.0f);
+  if (lane == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(lsum)) * kLn2;
+  if constexpr (!ENERGY) {
+    const float inv = empty ? 0.0f : 1.0f / lsum;
+    float *dst = a.o + orow * D + lane * EPL;  // O is only 4-byte aligned
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[e] * inv;
+  }
+}
+
 template <typename T, int D, int RB, SplitMode MODE, bool PAGED>
 hipError_t launch_t(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
   constexpr int KT = RB <= 4 ? ATTN_SPLIT_KT_SMALL : ATTN_SPLIT_KT_LARGE;
@@ -662,17 +729,47 @@ hipError_t launch_split_valu(const attn_plan_t &plan, const SplitArgs &a, attn_d
                         : launch_mode<float, 128>(plan, a, mode, stream);
 }
 
+namespace {
+
+// Rows whose record count exceeds this use the workgroup-per-row merge.
+constexpr int64_t kMergeWideRecords = 8;
+
+// Records per output row, roughly, of a work map: fixed chunks give
+// n_chunks; the balanced layout gives about W / segments + 1.
+int64_t records_per_row(const WorkMap &m) {
+  const int64_t segs = (int64_t)m.B * m.Hkv * m.row_blocks;
+  if (segs <= 0) return 0;
+  if (m.mode == 0) return m.n_chunks;
+  return (int64_t)m.n_wg / segs + 1;
+}
+
+template <int D, bool ENERGY>
+void launch_merge_d(const MergeArgs &a, int64_t rows, bool wide, hipStream_t stream) {
+  if (wide) {
+    hipLaunchKernelGGL((merge_partials<D, ENERGY>), dim3((unsigned)rows), dim3(kMergeThreads), 0,
+                       stream, a);
+  } else {
+    const int64_t blocks = (rows + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock;
+    hipLaunchKernelGGL((merge_rows<D, ENERGY>), dim3((unsigned)blocks),
+                       dim3(kRowsPerMergeBlock * kWave), 0, stream, a);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream) {
   const int64_t rows = (int64_t)a.map.B * a.map.Hkv * a.R;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows), block(kMergeThreads);
+  // Few records per row: a wave per row; many: a workgroup per row.
+  const int64_t per_row = records_per_row(a.map) + (a.has_shared ? records_per_row(a.smap) : 0);
+  const bool wide = per_row > kMergeWideRecords;
   const bool energy = a.o == nullptr;
   if (head_dim == 64) {
-    if (energy) hipLaunchKernelGGL((merge_partials<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((merge_partials<64, false>), grid, block, 0, stream, a);
+    if (energy) launch_merge_d<64, true>(a, rows, wide, stream);
+    else launch_merge_d<64, false>(a, rows, wide, stream);
   } else {
-    if (energy) hipLaunchKernelGGL((merge_partials<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((merge_partials<128, false>), grid, block, 0, stream, a);
+    if (energy) launch_merge_d<128, true>(a, rows, wide, stream);
+    else launch_merge_d<128, false>(a, rows, wide, stream);
   }
   return hipGetLastError();
 }
