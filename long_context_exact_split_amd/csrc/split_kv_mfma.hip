@@ -32,6 +32,13 @@
 namespace attn {
 namespace {
 
+#ifndef ATTN_MFMA_KPAD
+#define ATTN_MFMA_KPAD 8    // K tile row padding in LDS (bf16 elements, multiple of 8)
+#endif
+#ifndef ATTN_MFMA_VPAD
+#define ATTN_MFMA_VPAD 32   // V tile row padding in LDS (bf16 elements, multiple of 8)
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kRows = 32;   // query rows per work item
@@ -55,10 +62,10 @@ struct Tiles {
   static constexpr int NL = kTile / KPI;     // load instructions per tile and tensor
   static constexpr int KS = D / 16;          // MFMA k-steps of Q.K (8 dims per lane half)
   static constexpr int NT = D / 32;          // 32-dim output tiles of O^T
-  static constexpr int KROW = D + 8;         // LDS row pitch of the K tile (bf16 elements)
+  static constexpr int KROW = D + ATTN_MFMA_KPAD;  // LDS row pitch of the K tile (bf16 elements)
   // LDS row pitch of the V tile (bf16 elements): consecutive rows 16 banks
   // apart, so the two 16-lane groups of a transpose-read pass use disjoint banks.
-  static constexpr int VROW = D + 32;
+  static constexpr int VROW = D + ATTN_MFMA_VPAD;
 };
 
 template <int D, bool ENERGY>
@@ -87,6 +94,33 @@ __device__ __forceinline__ void settle(bf16x8_t (&qf)[KS]) {
     asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
     qf[s] = __builtin_bit_cast(bf16x8_t, u32x4{a0, a1, a2, a3});
   }
+}
+
+// max(x[l], x[l ^ 32]) in every lane, by gfx950's lane-half swap (no LDS).
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+// Query fragments and scale such that the scale is positive: a negative scale
+// is moved into Q (negating bf16 is exact), and a zero scale makes every logit
+// zero, as zero queries with scale 1 do.
+template <int KS>
+__device__ __forceinline__ float positive_scale(bf16x8_t (&qf)[KS], float scale_log2) {
+  if (scale_log2 > 0.0f) return scale_log2;
+  const uint32_t flip = scale_log2 < 0.0f ? 0x80008000u : 0u;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 t = __builtin_bit_cast(u32x4, qf[s]);
+    if (scale_log2 < 0.0f) {
+      t.x ^= flip; t.y ^= flip; t.z ^= flip; t.w ^= flip;
+    } else {
+      t = u32x4{0, 0, 0, 0};
+    }
+    qf[s] = __builtin_bit_cast(bf16x8_t, t);
+  }
+  return scale_log2 < 0.0f ? -scale_log2 : 1.0f;
 }
 
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
@@ -121,25 +155,22 @@ __device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs
         bf16x8_t, *reinterpret_cast<const u32x4 *>(ks + j * T::KROW + h * (D / 2) + 8 * s));
     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
   }
-  // Scale, mask, online softmax (lane l: row j, keys 8(e/4) + 4h + e%4).
-  // Tiles wholly visible to every row of the wave skip the mask, and with a
-  // positive scale the max is taken on raw logits and the scale is fused into
-  // the exponent's argument.
-  const bool fast = scale_log2 > 0.0f && !__any(t0 + kTile > lim);
-  float tmax = -INFINITY;
-  if (fast) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
-    tmax *= scale_log2;
-  } else {
+  // Mask, online softmax (lane l: row j, keys 8(e/4) + 4h + e%4).  The scale
+  // is positive here (see positive_scale), so the max is taken on the raw
+  // logits, masked keys become -inf in place (only on tiles that reach past
+  // some row's limit), and the scale is fused into the exponent's argument.
+  if (__any(t0 + kTile > lim)) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
-      sacc[e] = t < lim ? sacc[e] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sacc[e]);
+      sacc[e] = t < lim ? sacc[e] : -INFINITY;
     }
   }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+  for (int e = 3; e < 15; e += 2) tmax = fmaxf(fmaxf(tmax, sacc[e]), sacc[e + 1]);
+  tmax = fmaxf(tmax, sacc[15]) * scale_log2;
+  tmax = pair_max(tmax);  // lanes l and l + 32 hold halves of the row's keys
   if (__any(tmax > m + kLazyRescale)) {
     const float mn = fmaxf(m, tmax);
     const float alpha = rescale_factor(m, mn);
@@ -153,19 +184,15 @@ __device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs
     m = mn;
   }
   const float mref = m == -INFINITY ? 0.0f : m;
-  if (fast) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sacc[e] = fast_exp2(fmaf(sacc[e], scale_log2, -mref));
-      lsum += sacc[e];
-    }
-  } else {
+  for (int e = 0; e < 16; ++e) sacc[e] = fast_exp2(fmaf(sacc[e], scale_log2, -mref));
+  // Row sum as a tree (a chain of 16 dependent adds would stall the wave).
+  float ps[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sacc[e] = fast_exp2(sacc[e] - mref);
-      lsum += sacc[e];
-    }
-  }
+  for (int e = 0; e < 8; ++e) ps[e] = sacc[2 * e] + sacc[2 * e + 1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ps[e] += ps[e + 4];
+  lsum += (ps[0] + ps[2]) + (ps[1] + ps[3]);
   if constexpr (!ENERGY) {
     // P^T fragments (B operand): k-step s holds accumulator entries 8s..8s+7.
     bf16x8_t phi[2], plo[2];
@@ -250,6 +277,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, u32x4{0, 0, 0, 0});
   }
+  const float scale_log2 = positive_scale<KS>(qf, a.scale_log2);
   // Last visible key over the block's rows (row limits grow with the token index).
   int hi;
   {
@@ -324,7 +352,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
       for (int i = 0; i < NL; ++i) pn[i] = pnn[i];
     }
 
-    tile_step<D, ENERGY>(ks, vs, qf, t0, lim, a.scale_log2, m, lsum, oacc);
+    tile_step<D, ENERGY>(ks, vs, qf, t0, lim, scale_log2, m, lsum, oacc);
   }
 
   // Per-wave row statistics: lanes l and l + 32 hold the same m and halves of l.
@@ -439,6 +467,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, u32x4{0, 0, 0, 0});
   }
+  const float scale_log2 = positive_scale<KS>(qf, a.scale_log2);
   int hi;
   {
     const int last = min(a.R, (rb + 1) * kRows * RW) - 1;
@@ -533,7 +562,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
       if (tile >= n_tiles) break;  // uniform across the workgroup
       if constexpr (PAGED) lookup(tile + 2 * NS, pr[k]);  // stage (tile + 2NS) % NS = k
       tile_step<D, ENERGY>(sh.t.k[tile & 1], sh.t.v[tile & 1], qf, c0 + tile * kTile, lim,
-                           a.scale_log2, m, lsum, oacc);
+                           scale_log2, m, lsum, oacc);
       if (tile + 1 < n_tiles) {
         const int kn = (k + 1) % NS;  // stage of tile + 1 (constant once unrolled)
         store((tile + 1) & 1, kr[kn], vr[kn]);

@@ -310,3 +310,19 @@ def test_bifurcated_full_size():
     O, lse = run_bifurcated(w)
     Or, lr = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale)
     check_rows(O[:, None], lse[:, None], Or[:, None], lr[:, None], what="bifurcated_prefix full")
+
+
+# Non-positive scales: the MFMA kernels move a negative scale into Q (negating
+# bf16 is exact) and treat a zero scale as zero logits; the vector-ALU kernel
+# applies the scale as given.  All three kernels, against the oracle.
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+@pytest.mark.parametrize("shape", [(2, 1, 8, 2, 700), (2, 4, 32, 4, 900), (1, 8, 64, 2, 1200)],
+                         ids=["valu", "mfma32", "rows"])
+def test_non_positive_scale(scale, shape):
+    B, q_len, Hq, Hkv, L = shape
+    w = inputs.make_decode("negscale", 900 + L, B=B, q_len=q_len, Hq=Hq, Hkv=Hkv, D=128, L_max=L,
+                           kv_lens=[L, L // 2 + 3][:B], causal=q_len > 1, scale=scale,
+                           nan_pad=True)
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what=f"scale {scale} {shape}")
