@@ -25,6 +25,8 @@
 // merged through LDS at the end of each piece of work (work_map.h), giving
 // one record per (piece, row) in the same layout as the vector-ALU kernel, so
 // the same merge kernel follows.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "kv_rows.h"
@@ -131,35 +133,45 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2v_t));
 }
 
-// One 32-key tile in one wave: S^T = K.Q^T, masked online softmax of the
-// lane's row, O^T += V^T.P^T (P as bf16 hi + lo parts).  ks / vs: the tile in
-// LDS (row pitches KROW / VROW); t0: token of the tile's first key; lim: the
-// lane's row sees keys t < lim.
-template <int D, bool ENERGY>
-__device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs,
-                                          const bf16x8_t (&qf)[D / 16], int t0, int lim,
-                                          float scale_log2, float &m, float &lsum,
-                                          f32x16_t (&oacc)[ENERGY ? 1 : D / 32]) {
+// The three parts of one 32-key tile in one wave.
+//
+// qk_tile: S^T = K.Q^T (raw logits), K read from LDS (row pitch KROW).
+template <int D>
+__device__ __forceinline__ f32x16_t qk_tile(const uint16_t *ks, const bf16x8_t (&qf)[D / 16]) {
   using T = Tiles<D>;
-  constexpr int KS = T::KS, NT = T::NT;
   const int lane = threadIdx.x & (kWave - 1);
   const int h = lane >> 5;
   const int j = lane & 31;
-  // S^T = K . Q^T
   f32x16_t sacc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
+  for (int s = 0; s < T::KS; ++s) {
     const bf16x8_t kf = __builtin_bit_cast(
         bf16x8_t, *reinterpret_cast<const u32x4 *>(ks + j * T::KROW + h * (D / 2) + 8 * s));
     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
   }
-  // Mask, online softmax (lane l: row j, keys 8(e/4) + 4h + e%4).  The scale
-  // is positive here (see positive_scale), so the max is taken on the raw
-  // logits, masked keys become -inf in place (only on tiles that reach past
-  // some row's limit), and the scale is fused into the exponent's argument.
-  if (__any(t0 + kTile > lim)) {
+  return sacc;
+}
+
+// softmax_tile: masked online softmax of the lane's row over the tile
+// (lane l: row l % 32, keys 8(e/4) + 4h + e%4); t0: token of the tile's
+// first key; the row sees keys t < lim.  Updates m and lsum, returns the
+// factor alpha by which the unnormalised output must be rescaled before this
+// tile's P.V is added, and (full decode) P^T as bf16 hi + lo fragments.  The
+// scale is positive (positive_scale), so the max is taken on the raw logits,
+// masked keys become -inf in place (only on tiles that reach past some row's
+// limit), and the scale is fused into the exponent's argument.
+//
+// MASK: 0 = the tile is wholly visible to the wave's rows (no mask), 1 =
+// mask in place, 2 = decide at run time.  With MASK < 2 the function has no
+// branch, so the caller's scheduler can interleave it with matrix work.
+template <bool ENERGY, int MASK = 2>
+__device__ __forceinline__ float softmax_tile(f32x16_t sacc, int t0, int lim, float scale_log2,
+                                              float &m, float &lsum, bf16x8_t (&phi)[2],
+                                              bf16x8_t (&plo)[2]) {
+  const int h = (threadIdx.x & (kWave - 1)) >> 5;
+  if (MASK == 1 || (MASK == 2 && __any(t0 + kTile > lim))) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -171,16 +183,19 @@ __device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs
   for (int e = 3; e < 15; e += 2) tmax = fmaxf(fmaxf(tmax, sacc[e]), sacc[e + 1]);
   tmax = fmaxf(tmax, sacc[15]) * scale_log2;
   tmax = pair_max(tmax);  // lanes l and l + 32 hold halves of the row's keys
-  if (__any(tmax > m + kLazyRescale)) {
-    const float mn = fmaxf(m, tmax);
-    const float alpha = rescale_factor(m, mn);
-    lsum *= alpha;
-    if constexpr (!ENERGY) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[n][e] *= alpha;
+  float alpha = 1.0f;
+  if constexpr (MASK == 2) {
+    if (__any(tmax > m + kLazyRescale)) {
+      const float mn = fmaxf(m, tmax);
+      alpha = rescale_factor(m, mn);
+      lsum *= alpha;
+      m = mn;
     }
+  } else {  // the same decision, as selects
+    const bool need = __any(tmax > m + kLazyRescale);
+    const float mn = need ? fmaxf(m, tmax) : m;
+    alpha = need ? rescale_factor(m, mn) : 1.0f;
+    lsum *= alpha;
     m = mn;
   }
   const float mref = m == -INFINITY ? 0.0f : m;
@@ -195,7 +210,6 @@ __device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs
   lsum += (ps[0] + ps[2]) + (ps[1] + ps[3]);
   if constexpr (!ENERGY) {
     // P^T fragments (B operand): k-step s holds accumulator entries 8s..8s+7.
-    bf16x8_t phi[2], plo[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 wh, wl;
@@ -211,30 +225,62 @@ __device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs
       phi[s] = __builtin_bit_cast(bf16x8_t, wh);
       plo[s] = __builtin_bit_cast(bf16x8_t, wl);
     }
-    // V^T fragments (A operand) by transpose reads: in 16-lane group g,
-    // lane lg points at key k0 + lg/4, column n0 + 4(lg%4); it receives
-    // the four keys k0..k0+3 of column n0 + lg.
-    const int g = lane >> 4, lg = lane & 15;
+  }
+  return alpha;
+}
+
+// pv_tile: O^T += V^T.P^T.  V^T fragments (A operand) by transpose reads: in
+// 16-lane group g, lane lg points at key k0 + lg/4, column n0 + 4(lg%4); it
+// receives the four keys k0..k0+3 of column n0 + lg.
+template <int D>
+__device__ __forceinline__ void pv_tile(const uint16_t *vs, const bf16x8_t (&phi)[2],
+                                        const bf16x8_t (&plo)[2], f32x16_t (&oacc)[D / 32]) {
+  using T = Tiles<D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane >> 4, lg = lane & 15;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        s16x4_t part[2];
+    for (int n = 0; n < T::NT; ++n) {
+      s16x4_t part[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int key = 16 * s + 8 * r + 4 * (g >> 1) + (lg >> 2);
-          const int col = 32 * n + 16 * (g & 1) + 4 * (lg & 3);
-          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t *)(vs + key * T::VROW + col));
-        }
-        const bf16x8_t vf = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, part[0]),
-                                                  __builtin_bit_cast(bf16x4_t, part[1]), 0, 1, 2,
-                                                  3, 4, 5, 6, 7);
-        oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi[s], oacc[n], 0, 0, 0);
-        oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo[s], oacc[n], 0, 0, 0);
+      for (int r = 0; r < 2; ++r) {
+        const int key = 16 * s + 8 * r + 4 * (g >> 1) + (lg >> 2);
+        const int col = 32 * n + 16 * (g & 1) + 4 * (lg & 3);
+        part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t *)(vs + key * T::VROW + col));
       }
+      const bf16x8_t vf = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, part[0]),
+                                                __builtin_bit_cast(bf16x4_t, part[1]), 0, 1, 2,
+                                                3, 4, 5, 6, 7);
+      oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi[s], oacc[n], 0, 0, 0);
+      oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo[s], oacc[n], 0, 0, 0);
     }
   }
+}
+
+template <int D, bool ENERGY>
+__device__ __forceinline__ void rescale_o(f32x16_t (&oacc)[ENERGY ? 1 : D / 32], float alpha) {
+  if constexpr (!ENERGY) {
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[n][e] *= alpha;
+  }
+}
+
+// A whole tile in order (S^T, softmax, O rescale, P.V); ks / vs: the tile in
+// LDS (row pitches KROW / VROW).
+template <int D, bool ENERGY>
+__device__ __forceinline__ void tile_step(const uint16_t *ks, const uint16_t *vs,
+                                          const bf16x8_t (&qf)[D / 16], int t0, int lim,
+                                          float scale_log2, float &m, float &lsum,
+                                          f32x16_t (&oacc)[ENERGY ? 1 : D / 32]) {
+  bf16x8_t phi[2], plo[2];
+  const float alpha = softmax_tile<ENERGY>(qk_tile<D>(ks, qf), t0, lim, scale_log2, m, lsum,
+                                           phi, plo);
+  if (__any(alpha != 1.0f)) rescale_o<D, ENERGY>(oacc, alpha);
+  if constexpr (!ENERGY) pv_tile<D>(vs, phi, plo, oacc);
 }
 
 template <int D, bool ENERGY>
@@ -423,11 +469,13 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
 // instead of once per block of 32 rows.  No cross-wave merge: each wave
 // writes the records of its own 32 rows.
 // ---------------------------------------------------------------------------
+constexpr int kRowsBufs = 4;  // LDS tile buffers of the shared-tile kernel
+
 template <int D, int RW, bool ENERGY>
 union RowsSmem {
   struct {
-    uint16_t k[2][kTile * Tiles<D>::KROW];
-    uint16_t v[2][ENERGY ? 1 : kTile * Tiles<D>::VROW];
+    uint16_t k[kRowsBufs][kTile * Tiles<D>::KROW];
+    uint16_t v[kRowsBufs][ENERGY ? 1 : kTile * Tiles<D>::VROW];
   } t;
   float stage[RW][kRows * 32];  // epilogue: one 32 x 32 float slice per wave
 };
@@ -528,49 +576,99 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
     }
   };
 
-  // Paged caches: the block-table loads of tile x are issued in the
-  // iteration of tile x - 2*NS, NS - 1 iterations before the K/V loads of x,
-  // so that waiting for them never waits for K/V loads still in the ring.
-  // Their results live in a ring of page-id stages (tile x in stage x % NS).
+  // Software pipeline over the tiles.  Iteration t issues, for this wave,
+  //   P.V of tile t and S^T of tile t+2 (matrix cores) and
+  //   the softmax of tile t+1 (vector ALUs),
+  // three independent pieces of work that can overlap; the rescale of O that
+  // the softmax of tile t+1 asks for is applied before the P.V of tile t+1.
+  // LDS holds four tiles: t (V being read), t+1 (V next), t+2 (K being read)
+  // and t+3 (being stored from the register ring); one barrier per
+  // iteration.  Tiles past the last read the last visible row again, and
+  // the S^T of a tile past the last is computed but never used.
+  // Register ring: tile x lives in stage x % NS; paged caches: the
+  // block-table loads of tile x are issued in iteration x - 2 - 2*NS, NS - 1
+  // iterations before the K/V loads of x (iteration x - 3 - NS), so waiting
+  // for them never waits for K/V loads still in the ring; their results live
+  // in a ring of page-id stages (tile x in stage x % NS).
+  auto kbuf = [&](int tile) { return sh.t.k[tile & (kRowsBufs - 1)]; };
+  auto vbuf = [&](int tile) { return sh.t.v[tile & (kRowsBufs - 1)]; };
   int32_t pr[NS][PER];
   for (int s2 = 0; s2 < NS; ++s2)
     for (int i = 0; i < PER; ++i) pr[s2][i] = 0;
-  // Prologue: tile 0 into LDS buffer 0, tiles 1..NS in flight.
+  f32x16_t s1;              // S^T of tile t + 1
+  bf16x8_t phi[2], plo[2];  // P^T of tile t
+  float pend = 1.0f;        // O rescale owed before the next P.V
   if (n_tiles > 0) {
-    int32_t p0[PER];
-    lookup(0, p0);
-    load(0, p0, kr[0], vr[0]);
-    store(0, kr[0], vr[0]);
+    // Tiles 0..2 into LDS, tiles 3..2+NS into the register ring.
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      int32_t p0[PER];
+      lookup(x, p0);
+      load(x, p0, kr[x % NS], vr[x % NS]);
+      store(x & (kRowsBufs - 1), kr[x % NS], vr[x % NS]);
+    }
     settle<KS>(qf);
-    int32_t pk[NS + 1][PER];
 #pragma unroll
-    for (int k = 1; k <= NS; ++k)
-      if (k < n_tiles) lookup(k, pk[k]);
-#pragma unroll
-    for (int k = 1; k <= NS; ++k)
-      if (k < n_tiles) load(k, pk[k], kr[k % NS], vr[k % NS]);
+    for (int x = 3; x < 3 + NS; ++x) {
+      int32_t p0[PER];
+      lookup(x, p0);
+      load(x, p0, kr[x % NS], vr[x % NS]);
+    }
     if constexpr (PAGED) {
 #pragma unroll
-      for (int x = NS + 1; x < 2 * NS; ++x) lookup(x, pr[x % NS]);
+      for (int x = 3 + NS; x <= 1 + 2 * NS; ++x) lookup(x, pr[x % NS]);
     }
+    __syncthreads();
+    pend = softmax_tile<ENERGY>(qk_tile<D>(kbuf(0), qf), c0, lim, scale_log2, m, lsum, phi, plo);
+    s1 = qk_tile<D>(kbuf(1), qf);
   }
-  __syncthreads();
-  for (int base = 0; base < n_tiles; base += NS) {
+  // Tiles [0, full) are wholly visible to every row of this wave (no mask).
+  int wave_lim = lim;
+#pragma unroll
+  for (int off = 1; off < kWave; off *= 2) wave_lim = min(wave_lim, __shfl_xor(wave_lim, off));
+  const int full = (wave_lim - c0) / kTile;
+  // The matrix and vector work of one iteration, interleaved: the LDS reads
+  // of both products first, then each MFMA followed by a few VALU
+  // instructions of the softmax (the sched_group_barrier sequence fixes this
+  // order within the iteration's basic block).
+  auto body = [&](int tile, auto mask) {
+    constexpr int MASK = decltype(mask)::value;
+    if constexpr (!ENERGY) pv_tile<D>(vbuf(tile), phi, plo, oacc);
+    const f32x16_t s2 = qk_tile<D>(kbuf(tile + 2), qf);
+    pend = softmax_tile<ENERGY, MASK>(s1, c0 + (tile + 1) * kTile, lim, scale_log2, m, lsum,
+                                      phi, plo);
+    s1 = s2;
+    constexpr int kMfma = (ENERGY ? 0 : 4 * NT) + KS;
+    __builtin_amdgcn_sched_group_barrier(0x100, ENERGY ? 2 : 4, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an LDS read for a later one
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
+    }
+  };
+  for (int base = 0; base < n_tiles - 1; base += NS) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int tile = base + k;
-      if (tile >= n_tiles) break;  // uniform across the workgroup
-      if constexpr (PAGED) lookup(tile + 2 * NS, pr[k]);  // stage (tile + 2NS) % NS = k
-      tile_step<D, ENERGY>(sh.t.k[tile & 1], sh.t.v[tile & 1], qf, c0 + tile * kTile, lim,
-                           scale_log2, m, lsum, oacc);
-      if (tile + 1 < n_tiles) {
-        const int kn = (k + 1) % NS;  // stage of tile + 1 (constant once unrolled)
-        store((tile + 1) & 1, kr[kn], vr[kn]);
-        if (tile + 1 + NS < n_tiles) load(tile + 1 + NS, pr[kn], kr[kn], vr[kn]);
-      }
+      if (tile >= n_tiles - 1) break;  // uniform across the workgroup
+      if (__any(pend != 1.0f)) rescale_o<D, ENERGY>(oacc, pend);
+      if (tile + 1 < full)
+        body(tile, std::integral_constant<int, 0>{});
+      else
+        body(tile, std::integral_constant<int, 1>{});
+      if constexpr (PAGED) lookup(tile + 2 + 2 * NS, pr[(k + 2) % NS]);
+      const int st = (k + 3) % NS;  // stage of tile + 3 (constant once unrolled)
+      store((tile + 3) & (kRowsBufs - 1), kr[st], vr[st]);
+      load(tile + 3 + NS, pr[st], kr[st], vr[st]);
       __syncthreads();
     }
   }
+  if (n_tiles > 0) {  // the last tile's P.V
+    if (__any(pend != 1.0f)) rescale_o<D, ENERGY>(oacc, pend);
+    if constexpr (!ENERGY) pv_tile<D>(vbuf(n_tiles - 1), phi, plo, oacc);
+  }
+  __syncthreads();  // every wave is done with the tile buffers (the epilogue reuses them)
 
   lsum += __shfl_xor(lsum, 32);
   const int64_t rec0 = slot * (kRows * RW) + wave * kRows;  // this wave's first row
