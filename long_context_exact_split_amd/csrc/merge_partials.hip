@@ -1,0 +1,243 @@
+// Merge of the partial records and normalisation (gfx950): for every output
+// row, the (m, l, o) records its pieces left are combined with the
+// associative rule m = max(m_a, m_b), l = l_a e^(m_a-m) + l_b e^(m_b-m), o
+// likewise (Tree Attention article, an energy view of attention: max and
+// logsumexp are associative; Star Attention's phase 2 aggregates the same
+// statistics at its query host), then O = o / l and lse = (m + log2 l) ln 2.
+// The records of a row are found in closed form from the work map
+// (work_map.h), which the split kernels followed.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+// Where a merge row's records are: P pieces of its own segment (record index
+// prow + c*pstride) and S pieces of the shared call (srow + c*sstride).
+struct RowRecords {
+  int64_t prow, pstride, srow, sstride;
+  int32_t P, S;
+};
+
+// Run by a whole wave (the sums of sequence lengths are wave reductions);
+// every lane gets the result.
+__device__ __forceinline__ RowRecords row_records(const MergeArgs &a, int b, int kvh, int r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t tot = 0, pre = 0;
+  if (a.map.mode != 0) {
+    for (int bb = lane; bb < a.map.B; bb += kWave) {
+      const int64_t L = seq_len(a.map, bb);
+      tot += L;
+      pre += bb < b ? L : 0;
+    }
+    tot = wave_sum_i64(tot);
+    pre = wave_sum_i64(pre);
+  }
+  RowRecords rr{};
+  const int RBp = a.part.rows;
+  const int64_t sigma = ((int64_t)b * a.map.Hkv + kvh) * a.map.row_blocks + r / RBp;
+  const SlotRange pr = segment_slots_at(a.map, tot * segs_per_seq(a.map), pre, b, sigma);
+  rr.P = (int32_t)pr.count;
+  rr.prow = pr.first * RBp + r % RBp;
+  rr.pstride = pr.stride * RBp;
+  if (a.has_shared) {
+    const int RBs = a.shared.rows;
+    const int sb = a.shared_same_rows ? b : 0;              // sequence in the shared call
+    const int rs = a.shared_same_rows ? r : b * a.R + r;  // row in that sequence
+    const int64_t ssig = ((int64_t)sb * a.smap.Hkv + kvh) * a.smap.row_blocks + rs / RBs;
+    const SlotRange sr = segment_slots(a.smap, total_units(a.smap), sb, ssig);
+    rr.S = (int32_t)sr.count;
+    rr.srow = sr.first * RBs + rs % RBs;
+    rr.sstride = sr.stride * RBs;
+  }
+  return rr;
+}
+
+// Rows with many records (a long cache cut into many pieces): one workgroup
+// per output row.  The row's records are read in parallel: 16 bytes of o per
+// lane, kMergeThreads / (D/4) records per pass, so a row of ~100 records
+// takes a handful of passes instead of a serial walk.  The max over the
+// records is a block-wide reduction (DPP within waves, LDS across them); each
+// record is then rescaled once and the partial sums of the record groups are
+// added through LDS in a fixed order (deterministic).
+constexpr int kMergeThreads = 256;
+
+template <int D, bool ENERGY>
+__global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
+  constexpr int LPR = D / 4;                 // lanes per record (float4 each)
+  constexpr int NG = kMergeThreads / LPR;    // records in flight per pass
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t row = blockIdx.x;
+  const int r = (int)(row % a.R);
+  const int group = (int)(row / a.R);
+  const int b = group / a.map.Hkv;
+  const int kvh = group - b * a.map.Hkv;
+
+  __shared__ RowRecords where;
+  if (wave == 0) {
+    const RowRecords rr = row_records(a, b, kvh, r);
+    if (lane == 0) where = rr;
+  }
+  __syncthreads();
+  const int P = where.P, S = where.S;
+  const int64_t prow = where.prow, pstride = where.pstride, srow = where.srow,
+                sstride = where.sstride;
+  auto rec_of = [&](int c) { return c < P ? prow + c * pstride : srow + (c - P) * sstride; };
+  auto m_of = [&](int c) { return c < P ? a.part.m[prow + c * pstride] : a.shared.m[srow + (c - P) * sstride]; };
+
+  __shared__ float red[kMergeThreads / kWave];
+  float M = -INFINITY;
+  for (int c = tid; c < P + S; c += kMergeThreads) M = fmaxf(M, m_of(c));
+  M = wave_max(M);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / kWave; ++w) M = fmaxf(M, red[w]);
+
+  const int cg = tid / LPR;   // record group
+  const int dl = tid % LPR;   // float4 slot within the record
+  float lsum = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = cg; c < P + S; c += NG) {
+    const bool shared = c >= P;
+    const int64_t rec = rec_of(c);
+    const float f = rescale_factor(shared ? a.shared.m[rec] : a.part.m[rec], M);
+    lsum += f * (shared ? a.shared.l[rec] : a.part.l[rec]);
+    if constexpr (!ENERGY) {
+      const float *op = (shared ? a.shared.o : a.part.o) + rec * D + dl * 4;
+      const float4 v = *reinterpret_cast<const float4 *>(op);
+      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+    }
+  }
+  __shared__ float sl[NG];
+  __shared__ float4 so[ENERGY ? 1 : NG][ENERGY ? 1 : LPR];
+  if (dl == 0) sl[cg] = lsum;
+  if constexpr (!ENERGY) so[cg][dl] = acc;
+  __syncthreads();
+
+  const int i = r / a.G;
+  const int h = kvh * a.G + (r - i * a.G);
+  const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
+  float ltot = 0.0f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) ltot += sl[g];
+  const bool empty = M == -INFINITY || !(ltot > 0.0f);
+  if (tid == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(ltot)) * kLn2;
+  if constexpr (!ENERGY) {
+    if (tid < LPR) {
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float4 v = so[g][tid];
+        t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+      }
+      const float inv = empty ? 0.0f : 1.0f / ltot;
+      float *dst = a.o + orow * D + tid * 4;  // O is only 4-byte aligned
+      dst[0] = t.x * inv; dst[1] = t.y * inv; dst[2] = t.z * inv; dst[3] = t.w * inv;
+    }
+  }
+}
+
+// Rows with few records (most calls: a handful of pieces per segment): one
+// wave per output row, four rows per workgroup, so that hundreds of
+// thousands of short rows (a prefill's query rows) do not each pay for a
+// whole workgroup.  Records are combined one after another in index order
+// (deterministic); each lane holds D/64 of the row's outputs.
+constexpr int kRowsPerMergeBlock = 4;
+
+template <int D, bool ENERGY>
+__global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeArgs a) {
+  constexpr int EPL = D / kWave;  // output elements per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerMergeBlock + threadIdx.x / kWave;
+  const int64_t rows = (int64_t)a.map.B * a.map.Hkv * a.R;
+  if (row >= rows) return;  // whole waves; no workgroup barrier follows
+  const int r = (int)(row % a.R);
+  const int group = (int)(row / a.R);
+  const int b = group / a.map.Hkv;
+  const int kvh = group - b * a.map.Hkv;
+  const RowRecords rr = row_records(a, b, kvh, r);
+  const int n = rr.P + rr.S;
+  auto rec_of = [&](int c) { return c < rr.P ? rr.prow + c * rr.pstride : rr.srow + (c - rr.P) * rr.sstride; };
+
+  float M = -INFINITY;
+  for (int c = lane; c < n; c += kWave) {
+    const int64_t rec = rec_of(c);
+    M = fmaxf(M, c < rr.P ? a.part.m[rec] : a.shared.m[rec]);
+  }
+  M = wave_max(M);
+  float lsum = 0.0f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+#pragma unroll 4
+  for (int c = 0; c < n; ++c) {
+    const bool sh = c >= rr.P;
+    const int64_t rec = rec_of(c);
+    const float f = rescale_factor(sh ? a.shared.m[rec] : a.part.m[rec], M);
+    lsum += f * (sh ? a.shared.l[rec] : a.part.l[rec]);
+    if constexpr (!ENERGY) {
+      const float *op = (sh ? a.shared.o : a.part.o) + rec * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += f * op[e];
+    }
+  }
+  const int i = r / a.G;
+  const int h = kvh * a.G + (r - i * a.G);
+  const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
+  const bool empty = M == -INFINITY || !(lsum > 0.0f);
+  if (lane == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(lsum)) * kLn2;
+  if constexpr (!ENERGY) {
+    const float inv = empty ? 0.0f : 1.0f / lsum;
+    float *dst = a.o + orow * D + lane * EPL;  // O is only 4-byte aligned
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[e] * inv;
+  }
+}
+
+// Rows whose record count exceeds this use the workgroup-per-row merge.
+constexpr int64_t kMergeWideRecords = 8;
+
+// Records per output row, roughly, of a work map: fixed chunks give
+// n_chunks; the balanced layout gives about W / segments + 1.
+int64_t records_per_row(const WorkMap &m) {
+  const int64_t segs = (int64_t)m.B * m.Hkv * m.row_blocks;
+  if (segs <= 0) return 0;
+  if (m.mode == 0) return m.n_chunks;
+  return (int64_t)m.n_wg / segs + 1;
+}
+
+template <int D, bool ENERGY>
+void launch_merge_d(const MergeArgs &a, int64_t rows, bool wide, hipStream_t stream) {
+  if (wide) {
+    hipLaunchKernelGGL((merge_partials<D, ENERGY>), dim3((unsigned)rows), dim3(kMergeThreads), 0,
+                       stream, a);
+  } else {
+    const int64_t blocks = (rows + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock;
+    hipLaunchKernelGGL((merge_rows<D, ENERGY>), dim3((unsigned)blocks),
+                       dim3(kRowsPerMergeBlock * kWave), 0, stream, a);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.map.B * a.map.Hkv * a.R;
+  if (rows == 0) return hipSuccess;
+  // Few records per row: a wave per row; many: a workgroup per row.
+  const int64_t per_row = records_per_row(a.map) + (a.has_shared ? records_per_row(a.smap) : 0);
+  const bool wide = per_row > kMergeWideRecords;
+  const bool energy = a.o == nullptr;
+  if (head_dim == 64) {
+    if (energy) launch_merge_d<64, true>(a, rows, wide, stream);
+    else launch_merge_d<64, false>(a, rows, wide, stream);
+  } else {
+    if (energy) launch_merge_d<128, true>(a, rows, wide, stream);
+    else launch_merge_d<128, false>(a, rows, wide, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn
