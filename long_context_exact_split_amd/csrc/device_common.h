@@ -25,6 +25,41 @@ __device__ __forceinline__ float dpp_f32(float x) {
                                                                0xF, 0xF, true));
 }
 
+// The values of lanes l and l ^ OFF (OFF in {8, 16, 32}) as (a, b), with
+// lane-crossing VALU operations: a row rotation by 8 (DPP) within a row of 16,
+// v_permlane16_swap across row pairs, v_permlane32_swap across wave halves.
+// For OFF = 16 and 32 both lanes of a pair get the same (a, b); for OFF = 8,
+// a is the lane's own value.  A commutative combination of a and b is
+// therefore identical in both lanes of the pair.
+//
+// The swap builtins return a two-element vector; each element is copied to a
+// scalar before the bit cast to float, because a bit cast applied to the
+// element expression itself reads element 0 with this compiler.
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8
+
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float &a, float &b) {
+  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "lane distance");
+  if constexpr (OFF == 8) {
+    a = x;
+    b = dpp_f32<kDppRowRor8>(x);
+  } else {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    uint32_t r0, r1;
+    if constexpr (OFF == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      r0 = r[0];
+      r1 = r[1];
+    } else {
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      r0 = r[0];
+      r1 = r[1];
+    }
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+  }
+}
+
 // All-reduce (sum) over aligned groups of N lanes, N in {1, 2, 4, 8, 16, 32, 64}.
 // Within a row of 16 lanes the butterfly uses DPP: after the two quad steps
 // every lane holds its quad's sum, the half-row mirror pairs quad 0 with
@@ -35,8 +70,15 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp_f32<kDppQuadXor2>(x);
   if constexpr (N >= 8) x += dpp_f32<kDppRowHalfMirror>(x);
   if constexpr (N >= 16) x += dpp_f32<kDppRowMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  float a, b;
+  if constexpr (N >= 32) {
+    lane_pair<16>(x, a, b);
+    x = a + b;
+  }
+  if constexpr (N >= 64) {
+    lane_pair<32>(x, a, b);
+    x = a + b;
+  }
   return x;
 }
 
@@ -45,12 +87,16 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
   x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
   x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  float a, b;
+  lane_pair<16>(x, a, b);
+  x = fmaxf(a, b);
+  lane_pair<32>(x, a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+
+
 
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
 #pragma unroll

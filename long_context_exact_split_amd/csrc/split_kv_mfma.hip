@@ -100,9 +100,9 @@ __device__ __forceinline__ void settle(bf16x8_t (&qf)[KS]) {
 
 // max(x[l], x[l ^ 32]) in every lane, by gfx950's lane-half swap (no LDS).
 __device__ __forceinline__ float pair_max(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  float a, b;
+  lane_pair<32>(x, a, b);
+  return fmaxf(a, b);
 }
 
 // Query fragments and scale such that the scale is positive: a negative scale

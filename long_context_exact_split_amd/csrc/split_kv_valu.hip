@@ -22,6 +22,8 @@
 // Logits are kept in log2 units (scale * log2 e folded into one fp32
 // multiply after the fp32 dot product), so exponentials are v_exp_f32.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "kv_rows.h"
@@ -43,6 +45,15 @@ namespace {
 #endif
 
 constexpr int kWaves = ATTN_SPLIT_WAVES;
+
+// Calls f(integral_constant<int, OFF>) for OFF, 2*OFF, 4*OFF, ... < 64.
+template <int OFF, typename F>
+__device__ __forceinline__ void for_lane_offsets(F &&f) {
+  if constexpr (OFF < kWave) {
+    f(std::integral_constant<int, OFF>{});
+    for_lane_offsets<2 * OFF>(f);
+  }
+}
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLazyRescale = 8.0f;  // log2 units: rescale only past a 256x growth
 
@@ -95,8 +106,8 @@ __device__ __forceinline__ float slice_dot(const uint4 &q, const uint4 &k) {
 // key row: afterwards the lane holds the full sum of one row only
 // (scatter_row gives which), so the softmax steps that follow run once per
 // (key, row) on RB-times fewer lanes than after an all-reduce.  The steps are
-// the DPP butterfly of group_sum (quad xor 1, quad xor 2, half-row mirror,
-// row mirror, then xor 16), each step keeping half of the lane's rows and
+// the butterfly of group_sum (quad xor 1, quad xor 2, half-row mirror, row
+// mirror, then lanes 16 apart), each step keeping half of the lane's rows and
 // pulling the partner's partials for them.  The partners of the two mirror
 // steps sit at the reflected quad position, so the rows a lane keeps are
 // chosen from its quad position XOR 3 in odd quads; with that choice every
@@ -156,8 +167,15 @@ __device__ __forceinline__ float row_scatter_sum(const float (&x)[RB], int kl) {
   }
   // Steps 4 and 5: all-reduce over the rest of the key row.
   if constexpr (LPK >= 16) v[0] += dpp_f32<kDppRowMirror>(v[0]);
-  if constexpr (LPK >= 32) v[0] += __shfl_xor(v[0], 16);
-  if constexpr (LPK >= 64) v[0] += __shfl_xor(v[0], 32);
+  float pa, pb;
+  if constexpr (LPK >= 32) {
+    lane_pair<16>(v[0], pa, pb);
+    v[0] = pa + pb;
+  }
+  if constexpr (LPK >= 64) {
+    lane_pair<32>(v[0], pa, pb);
+    v[0] = pa + pb;
+  }
   return v[0];
 }
 
@@ -403,26 +421,31 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
   }
 
   // Merge the KPW key slots of the wave (lanes with equal kl, hence the same
-  // rows).
+  // rows): pairs of lanes l, l ^ off for off = LPK .. 32, exchanged without
+  // LDS (lane_pair); both lanes of a pair merge the same two records.
+  for_lane_offsets<LPK>([&](auto off_c) {
+    constexpr int OFF = decltype(off_c)::value;
+    {
 #pragma unroll
-  for (int off = LPK; off < kWave; off *= 2) {
+      for (int r = 0; r < NS_ROWS; ++r) {
+        float ma, mb, la, lb;
+        lane_pair<OFF>(m[r], ma, mb);
+        lane_pair<OFF>(l[r], la, lb);
+        const float M = fmaxf(ma, mb);
+        const float fa = rescale_factor(ma, M), fb = rescale_factor(mb, M);
+        l[r] = la * fa + lb * fb;
+        if constexpr (!ENERGY) {
 #pragma unroll
-    for (int r = 0; r < NS_ROWS; ++r) {
-      const float mo = __shfl_xor(m[r], off);
-      const float lo = __shfl_xor(l[r], off);
-      const float M = fmaxf(m[r], mo);
-      const float fa = rescale_factor(m[r], M), fb = rescale_factor(mo, M);
-      l[r] = l[r] * fa + lo * fb;
-      if constexpr (!ENERGY) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float oo = __shfl_xor(o[r][e], off);
-          o[r][e] = o[r][e] * fa + oo * fb;
+          for (int e = 0; e < EPL; ++e) {
+            float oa, ob;
+            lane_pair<OFF>(o[r][e], oa, ob);
+            o[r][e] = oa * fa + ob * fb;
+          }
         }
+        m[r] = M;
       }
-      m[r] = M;
     }
-  }
+  });
 
   // Merge the waves through LDS and write the piece's record (the barrier
   // keeps the previous piece's readers of the buffers ahead of these writes).

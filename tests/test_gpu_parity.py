@@ -178,6 +178,44 @@ def test_huge_logits_are_stable():
     check_rows(O, lse, Or, lr, what="huge logits")
 
 
+SPIKES = [
+    # B, q_len, Hq, Hkv, causal: vector-ALU rows, matrix-core kernel 1, shared-tile kernel 2
+    (2, 1, 8, 2, False),
+    (1, 4, 32, 4, True),
+    (1, 6, 16, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", SPIKES, ids=[f"B{c[0]}_ql{c[1]}_Hq{c[2]}_Hkv{c[3]}" for c in SPIKES])
+def test_isolated_huge_logits_at_every_lane_position(case):
+    """One key per 65-token stride aimed at one row with a logit of 200 + j
+    (natural units, j = 0..63), so that across the cache the dominating key
+    sits at every position modulo 64: whichever lanes or key slots hold it,
+    every partial maximum that combines with it must see it, or its
+    exponential overflows (2^288 and more)."""
+    B, q_len, Hq, Hkv, causal = case
+    L = 4500
+    w = inputs.make_decode("spikes", 41 + Hq, B=B, q_len=q_len, Hq=Hq, Hkv=Hkv, D=128,
+                           L_max=L, causal=causal)
+    qf = w.values("q").astype(np.float64)
+    G = Hq // Hkv
+    for b in range(B):
+        for kvh in range(Hkv):
+            for j in range(64):
+                i, h = j % q_len, kvh * G + (j // q_len) % G
+                qv = qf[b, i, h]
+                c = (200.0 + j) / (w.scale * float(np.dot(qv, qv)))
+                w.k[b, kvh, 65 * j, :] = inputs.f32_to_bf16((c * qv).astype(np.float32))
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    assert lr.max() > 200
+    check_rows(O, lse, Or, lr, what=f"spikes {case}")
+    q, k, v, lens_t = workload_tensors(w)
+    lse_e = binding.decode_energy(q, k, lens_t, causal=causal)
+    torch.cuda.synchronize()
+    check_rows(None, lse_e.cpu().numpy(), None, lr, what=f"spikes energy {case}")
+
+
 # ----------------------------------------------------------------------------
 # Properties of the path
 # ----------------------------------------------------------------------------
