@@ -10,7 +10,11 @@ Other workload shapes are selectable with --workload.
 Prints one JSON line: KV tokens/s (value), whole-path HBM GB/s against the
 8 TB/s peak, the roofline record of the dominant kernel (its per-launch time
 from HIP events recorded on the stream it runs on), and the fp64 CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload.  Whole-call times are also
+given as median / 10th / 90th percentile, for the back-to-back timed calls
+(call_ms) and for calls that each follow a 1 GiB write evicting L2 and the
+Infinity Cache (call_ms_cold_cache; the bifurcated batch, ~203 MB, would
+otherwise stay cache-resident between calls).
 """
 import argparse
 import json
@@ -73,6 +77,9 @@ def parse():
                     help="skip the HBM read-stream reference measurement")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged workloads: tokens per page (0: the workload's own, 16)")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="extra calls after the timed steps, each behind a 1 GiB write that "
+                         "evicts L2 and the Infinity Cache (0: skip)")
     return ap.parse_args()
 
 
@@ -397,6 +404,38 @@ def cpu_baseline(run, n_rows, O_gpu, lse_gpu):
             "seconds": dt, "parity_max_abs_dO": dO, "parity_max_rel_dlse": dl}
 
 
+FLUSH_BYTES = 1 << 30  # > 8 x 4 MB L2 + 256 MB Infinity Cache
+
+
+def spread(ms):
+    """Median, 10th and 90th percentile of a list of call times (ms)."""
+    xs = sorted(ms)
+
+    def pct(p):
+        return xs[min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))]
+    return {"median": statistics.median(xs), "p10": pct(10), "p90": pct(90), "calls": len(xs)}
+
+
+def cold_calls(torch, run, n):
+    """Whole-call times (HIP events around every launch of the call) with the
+    caches cleared before each call by a 1 GiB write, outside the events."""
+    stream = torch.cuda.current_stream()
+    junk = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i in range(n):
+        junk.fill_(i)
+        ev[i][0].record(stream)
+        run.first()
+        run.second()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    del junk
+    out = spread([a.elapsed_time(b) for a, b in ev])
+    out["flush_bytes"] = FLUSH_BYTES
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -451,6 +490,7 @@ def main():
     wall = time.perf_counter() - t0
     first_ms = [e[0].elapsed_time(e[1]) for e in ev]
     second_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    call_ms = [e[0].elapsed_time(e[2]) for e in ev]
 
     step_ms = wall * 1e3 / K
     first_avg = statistics.mean(first_ms)
@@ -477,6 +517,7 @@ def main():
         "dominant_kernel_ms": first_avg,
         "dominant_kernel_ms_median": statistics.median(first_ms),
         "second_launch_ms": statistics.mean(second_ms),
+        "call_ms": spread(call_ms),
         "tflops": run.flops / (first_avg * 1e-3) / 1e12,
         "roofline": {"bound": "hbm", "achieved": dom_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": dom_gbps / PEAK_GBPS, "traffic": counter_traffic(args.workload),
@@ -491,6 +532,8 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
                               "kernel": run.kernel, "algorithmic_flops_per_launch": run.flops}
+    if args.cold_calls > 0:
+        result["call_ms_cold_cache"] = cold_calls(torch, run, args.cold_calls)
     if not args.no_ceiling:
         ceil = read_ceiling(torch)
         result["hbm_read_ceiling_gbps"] = ceil

@@ -198,7 +198,10 @@ __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeAr
 }
 
 // Rows whose record count exceeds this use the workgroup-per-row merge.
-constexpr int64_t kMergeWideRecords = 8;
+#ifndef ATTN_MERGE_WIDE_RECORDS
+#define ATTN_MERGE_WIDE_RECORDS 8
+#endif
+constexpr int64_t kMergeWideRecords = ATTN_MERGE_WIDE_RECORDS;
 
 // Records per output row, roughly, of a work map: fixed chunks give
 // n_chunks; the balanced layout gives about W / segments + 1.
