@@ -19,24 +19,32 @@ struct RowRecords {
   int32_t P, S;
 };
 
-// Run by a whole wave (the sums of sequence lengths are wave reductions);
+// Run by a whole wave (the sums of sequence units are wave reductions);
 // every lane gets the result.
+// CAUSAL_ROWS = false: neither map has causal segment lengths (the launcher
+// checked), and the copies below say so at compile time.
+template <bool CAUSAL_ROWS>
 __device__ __forceinline__ RowRecords row_records(const MergeArgs &a, int b, int kvh, int r) {
+  WorkMap map = a.map, smap = a.smap;
+  if constexpr (!CAUSAL_ROWS) {
+    map.causal_rows = 0;
+    smap.causal_rows = 0;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   int64_t tot = 0, pre = 0;
-  if (a.map.mode != 0) {
-    for (int bb = lane; bb < a.map.B; bb += kWave) {
-      const int64_t L = seq_len(a.map, bb);
-      tot += L;
-      pre += bb < b ? L : 0;
+  if (map.mode != 0) {
+    for (int bb = lane; bb < map.B; bb += kWave) {
+      const int64_t u = seq_units(map, seq_len(map, bb));
+      tot += u;
+      pre += bb < b ? u : 0;
     }
     tot = wave_sum_i64(tot);
     pre = wave_sum_i64(pre);
   }
   RowRecords rr{};
   const int RBp = a.part.rows;
-  const int64_t sigma = ((int64_t)b * a.map.Hkv + kvh) * a.map.row_blocks + r / RBp;
-  const SlotRange pr = segment_slots_at(a.map, tot * segs_per_seq(a.map), pre, b, sigma);
+  const int64_t sigma = ((int64_t)b * map.Hkv + kvh) * map.row_blocks + r / RBp;
+  const SlotRange pr = segment_slots_at(map, tot, pre, b, sigma);
   rr.P = (int32_t)pr.count;
   rr.prow = pr.first * RBp + r % RBp;
   rr.pstride = pr.stride * RBp;
@@ -44,8 +52,8 @@ __device__ __forceinline__ RowRecords row_records(const MergeArgs &a, int b, int
     const int RBs = a.shared.rows;
     const int sb = a.shared_same_rows ? b : 0;              // sequence in the shared call
     const int rs = a.shared_same_rows ? r : b * a.R + r;  // row in that sequence
-    const int64_t ssig = ((int64_t)sb * a.smap.Hkv + kvh) * a.smap.row_blocks + rs / RBs;
-    const SlotRange sr = segment_slots(a.smap, total_units(a.smap), sb, ssig);
+    const int64_t ssig = ((int64_t)sb * smap.Hkv + kvh) * smap.row_blocks + rs / RBs;
+    const SlotRange sr = segment_slots(smap, total_units(smap), sb, ssig);
     rr.S = (int32_t)sr.count;
     rr.srow = sr.first * RBs + rs % RBs;
     rr.sstride = sr.stride * RBs;
@@ -62,7 +70,7 @@ __device__ __forceinline__ RowRecords row_records(const MergeArgs &a, int b, int
 // added through LDS in a fixed order (deterministic).
 constexpr int kMergeThreads = 256;
 
-template <int D, bool ENERGY>
+template <int D, bool ENERGY, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   constexpr int LPR = D / 4;                 // lanes per record (float4 each)
   constexpr int NG = kMergeThreads / LPR;    // records in flight per pass
@@ -77,7 +85,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
 
   __shared__ RowRecords where;
   if (wave == 0) {
-    const RowRecords rr = row_records(a, b, kvh, r);
+    const RowRecords rr = row_records<CAUSAL_ROWS>(a, b, kvh, r);
     if (lane == 0) where = rr;
   }
   __syncthreads();
@@ -141,61 +149,87 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   }
 }
 
-// Rows with few records (most calls: a handful of pieces per segment): one
-// wave per output row, four rows per workgroup, so that hundreds of
-// thousands of short rows (a prefill's query rows) do not each pay for a
-// whole workgroup.  Records are combined one after another in index order
+// Rows with few records (most calls: a handful of pieces per segment): a
+// wave per output row, or per run of rows_per_wave consecutive rows when
+// there are hundreds of thousands of them (a prefill's query rows), four
+// waves per workgroup.  Rows of one row block have their records in the same
+// slots, one record row apart, so a run works out where they are once per
+// block.  Records are combined one after another in index order
 // (deterministic); each lane holds D/64 of the row's outputs.
 constexpr int kRowsPerMergeBlock = 4;
 
-template <int D, bool ENERGY>
-__global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeArgs a) {
+template <int D, bool ENERGY, bool CAUSAL_ROWS>
+__global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeArgs a,
+                                                                          int rows_per_wave) {
   constexpr int EPL = D / kWave;  // output elements per lane
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerMergeBlock + threadIdx.x / kWave;
   const int64_t rows = (int64_t)a.map.B * a.map.Hkv * a.R;
-  if (row >= rows) return;  // whole waves; no workgroup barrier follows
-  const int r = (int)(row % a.R);
-  const int group = (int)(row / a.R);
-  const int b = group / a.map.Hkv;
-  const int kvh = group - b * a.map.Hkv;
-  const RowRecords rr = row_records(a, b, kvh, r);
-  const int n = rr.P + rr.S;
-  auto rec_of = [&](int c) { return c < rr.P ? rr.prow + c * rr.pstride : rr.srow + (c - rr.P) * rr.sstride; };
+  const int64_t row0 =
+      ((int64_t)blockIdx.x * kRowsPerMergeBlock + threadIdx.x / kWave) * rows_per_wave;
+  if (row0 >= rows) return;  // whole waves; no workgroup barrier follows
+  const int64_t row1 = row0 + rows_per_wave < rows ? row0 + rows_per_wave : rows;
+  RowRecords rr{};
+  int key_group = -1, key_p = -1, key_s = -1;  // the row blocks rr was worked out for
+  for (int64_t row = row0; row < row1; ++row) {
+    const int r = (int)(row % a.R);
+    const int group = (int)(row / a.R);
+    const int b = group / a.map.Hkv;
+    const int kvh = group - b * a.map.Hkv;
+    const int kp = r / a.part.rows;
+    const int ks = a.has_shared ? (a.shared_same_rows ? r : b * a.R + r) / a.shared.rows : 0;
+    if (group == key_group && kp == key_p && ks == key_s) {
+      rr.prow += 1;  // the next row of the same blocks: the next record row
+      rr.srow += 1;
+    } else {
+      rr = row_records<CAUSAL_ROWS>(a, b, kvh, r);
+      key_group = group;
+      key_p = kp;
+      key_s = ks;
+    }
+    const int n = rr.P + rr.S;
+    auto rec_of = [&](int c) {
+      return c < rr.P ? rr.prow + c * rr.pstride : rr.srow + (c - rr.P) * rr.sstride;
+    };
 
-  float M = -INFINITY;
-  for (int c = lane; c < n; c += kWave) {
-    const int64_t rec = rec_of(c);
-    M = fmaxf(M, c < rr.P ? a.part.m[rec] : a.shared.m[rec]);
-  }
-  M = wave_max(M);
-  float lsum = 0.0f, acc[EPL];
+    float M = -INFINITY;
+    for (int c = lane; c < n; c += kWave) {
+      const int64_t rec = rec_of(c);
+      M = fmaxf(M, c < rr.P ? a.part.m[rec] : a.shared.m[rec]);
+    }
+    M = wave_max(M);
+    float lsum = 0.0f, acc[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
 #pragma unroll 4
-  for (int c = 0; c < n; ++c) {
-    const bool sh = c >= rr.P;
-    const int64_t rec = rec_of(c);
-    const float f = rescale_factor(sh ? a.shared.m[rec] : a.part.m[rec], M);
-    lsum += f * (sh ? a.shared.l[rec] : a.part.l[rec]);
-    if constexpr (!ENERGY) {
-      const float *op = (sh ? a.shared.o : a.part.o) + rec * D + lane * EPL;
+    for (int c = 0; c < n; ++c) {
+      const bool sh = c >= rr.P;
+      const int64_t rec = rec_of(c);
+      const float f = rescale_factor(sh ? a.shared.m[rec] : a.part.m[rec], M);
+      lsum += f * (sh ? a.shared.l[rec] : a.part.l[rec]);
+      if constexpr (!ENERGY) {
+        const float *op = (sh ? a.shared.o : a.part.o) + rec * D + lane * EPL;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += f * op[e];
+        for (int e = 0; e < EPL; ++e) acc[e] += f * op[e];
+      }
+    }
+    const int i = r / a.G;
+    const int h = kvh * a.G + (r - i * a.G);
+    const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
+    const bool empty = M == -INFINITY || !(lsum > 0.0f);
+    if (lane == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(lsum)) * kLn2;
+    if constexpr (!ENERGY) {
+      const float inv = empty ? 0.0f : 1.0f / lsum;
+      float *dst = a.o + orow * D + lane * EPL;  // O is only 4-byte aligned
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dst[e] = acc[e] * inv;
     }
   }
-  const int i = r / a.G;
-  const int h = kvh * a.G + (r - i * a.G);
-  const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
-  const bool empty = M == -INFINITY || !(lsum > 0.0f);
-  if (lane == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(lsum)) * kLn2;
-  if constexpr (!ENERGY) {
-    const float inv = empty ? 0.0f : 1.0f / lsum;
-    float *dst = a.o + orow * D + lane * EPL;  // O is only 4-byte aligned
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) dst[e] = acc[e] * inv;
-  }
 }
+
+// Waves that keep the whole GPU busy (256 CUs x 32): row runs get longer only
+// beyond that many rows.
+constexpr int64_t kMergeWavesWanted = 8192;
+constexpr int kMaxRowsPerWave = 16;
 
 // Rows whose record count exceeds this use the workgroup-per-row merge.
 #ifndef ATTN_MERGE_WIDE_RECORDS
@@ -212,16 +246,27 @@ int64_t records_per_row(const WorkMap &m) {
   return (int64_t)m.n_wg / segs + 1;
 }
 
+template <int D, bool ENERGY, bool CAUSAL_ROWS>
+void launch_merge_dc(const MergeArgs &a, int64_t rows, bool wide, hipStream_t stream) {
+  if (wide) {
+    hipLaunchKernelGGL((merge_partials<D, ENERGY, CAUSAL_ROWS>), dim3((unsigned)rows),
+                       dim3(kMergeThreads), 0, stream, a);
+  } else {
+    int rpw = 1;
+    while (rpw < kMaxRowsPerWave && rows / (2 * rpw) >= kMergeWavesWanted) rpw *= 2;
+    const int64_t waves = (rows + rpw - 1) / rpw;
+    const int64_t blocks = (waves + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock;
+    hipLaunchKernelGGL((merge_rows<D, ENERGY, CAUSAL_ROWS>), dim3((unsigned)blocks),
+                       dim3(kRowsPerMergeBlock * kWave), 0, stream, a, rpw);
+  }
+}
+
 template <int D, bool ENERGY>
 void launch_merge_d(const MergeArgs &a, int64_t rows, bool wide, hipStream_t stream) {
-  if (wide) {
-    hipLaunchKernelGGL((merge_partials<D, ENERGY>), dim3((unsigned)rows), dim3(kMergeThreads), 0,
-                       stream, a);
-  } else {
-    const int64_t blocks = (rows + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock;
-    hipLaunchKernelGGL((merge_rows<D, ENERGY>), dim3((unsigned)blocks),
-                       dim3(kRowsPerMergeBlock * kWave), 0, stream, a);
-  }
+  if (a.map.causal_rows || (a.has_shared && a.smap.causal_rows))
+    launch_merge_dc<D, ENERGY, true>(a, rows, wide, stream);
+  else
+    launch_merge_dc<D, ENERGY, false>(a, rows, wide, stream);
 }
 
 }  // namespace

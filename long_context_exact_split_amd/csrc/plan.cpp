@@ -135,7 +135,10 @@ attn_status_t make_plan(const attn_desc_t *d, int cu_count, bool mfma_available,
   } else {
     p->balanced = 1;
     p->chunks_per_seq = 0;
-    const int64_t units = segs * L;  // upper bound (all sequences full)
+    // Upper bound (all sequences full); causal row blocks count the keys
+    // they see.
+    const WorkMap shape = work_map(d, *p);
+    const int64_t units = (int64_t)d->batch * seq_units(shape, L);
     int64_t W = (int64_t)cu_count * items_per_cu(p->kernel, units, cu_count);
     if (W > 65535) W = 65535;
     const int64_t by_size = (units + kMinPiece - 1) / kMinPiece;
@@ -163,6 +166,13 @@ WorkMap work_map(const attn_desc_t *d, const attn_plan_t &p) {
   m.chunk_len = p.balanced ? 0 : p.chunk_len;
   m.n_chunks = p.chunks_per_seq;
   m.n_wg = p.balanced ? (int32_t)p.work_items : 0;
+  // Only the shared-tile kernel's row blocks (up to 256 rows, prefill-sized
+  // query blocks) differ enough in visible keys to matter.
+  m.causal_rows = (p.balanced && d->causal && p.row_blocks > 1 && p.kernel == 2) ? 1 : 0;
+  m.q_len = d->q_len;
+  m.G = d->num_q_heads / d->num_kv_heads;
+  m.R = p.rows;
+  m.rpb = p.rows_per_block;
   return m;
 }
 

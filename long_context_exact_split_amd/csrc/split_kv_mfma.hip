@@ -442,7 +442,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
 template <int D, bool ENERGY, bool PAGED>
 __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   __shared__ MfmaSmem<D, ENERGY> sh;
-  const WorkMap &m = a.map;
+  WorkMap m = a.map;
+  m.causal_rows = 0;  // one row block: never set for this kernel's maps
   if (m.mode == 0) {
     const int w = blockIdx.x;
     const int sigma = w / m.n_chunks, c = w - sigma * m.n_chunks;
@@ -708,10 +709,11 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   }
 }
 
-template <int D, int RW, bool ENERGY, bool PAGED>
+template <int D, int RW, bool ENERGY, bool PAGED, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
   __shared__ RowsSmem<D, RW, ENERGY> sh;
-  const WorkMap &m = a.map;
+  WorkMap m = a.map;
+  if constexpr (!CAUSAL_ROWS) m.causal_rows = 0;  // the launcher checked it is 0
   if (m.mode == 0) {
     const int w = blockIdx.x;
     const int sigma = w / m.n_chunks, c = w - sigma * m.n_chunks;
@@ -732,8 +734,12 @@ __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
 
 template <int D, int RW, bool ENERGY, bool PAGED>
 hipError_t launch_rows(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, ENERGY, PAGED>), dim3((unsigned)plan.work_items),
-                     dim3(RW * kWave), 0, stream, a);
+  if (a.map.causal_rows)
+    hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, ENERGY, PAGED, true>),
+                       dim3((unsigned)plan.work_items), dim3(RW * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, ENERGY, PAGED, false>),
+                       dim3((unsigned)plan.work_items), dim3(RW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -750,7 +756,7 @@ hipError_t launch_rows_rw(const attn_plan_t &plan, const SplitArgs &a, hipStream
 template <int D, bool ENERGY, bool PAGED>
 hipError_t launch_kernel(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
   if (plan.kernel == 2) return launch_rows_rw<D, ENERGY, PAGED>(plan, a, stream);
-  if (plan.rows_per_block != kRows) return hipErrorInvalidValue;
+  if (plan.rows_per_block != kRows || a.map.causal_rows) return hipErrorInvalidValue;
   hipLaunchKernelGGL((split_kv_mfma<D, ENERGY, PAGED>), dim3((unsigned)plan.work_items),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -498,7 +498,8 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
 template <typename T, int D, int RB, int KT, SplitMode MODE, bool PAGED>
 __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   __shared__ ValuSmem<D, RB, MODE != SplitMode::kFull> sh;
-  const WorkMap &m = a.map;
+  WorkMap m = a.map;
+  m.causal_rows = 0;  // never set for this kernel's maps (the launcher checks)
   if (m.mode == 0) {
     const int w = blockIdx.x;
     const int sigma = w / m.n_chunks, c = w - sigma * m.n_chunks;
@@ -521,6 +522,7 @@ template <typename T, int D, int RB, SplitMode MODE, bool PAGED>
 hipError_t launch_t(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
   constexpr int KT = RB <= 4 ? ATTN_SPLIT_KT_SMALL : ATTN_SPLIT_KT_LARGE;
   if (plan.work_items <= 0) return hipSuccess;
+  if (a.map.causal_rows) return hipErrorInvalidValue;
   hipLaunchKernelGGL((split_kv_valu<T, D, RB, KT, MODE, PAGED>), dim3((unsigned)plan.work_items),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();

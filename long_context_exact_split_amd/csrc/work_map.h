@@ -11,7 +11,11 @@
 //
 // * balanced (mode 1): the segments are laid end to end (offset of sigma =
 //   sum of the lengths before it) into U token units, and workgroup w takes
-//   units [floor(w*U/W), floor((w+1)*U/W)).  Every workgroup then streams the
+//   units [floor(w*U/W), floor((w+1)*U/W)).  A segment is as long as the keys
+//   its rows can see: L_b, or under a causal mask with several row blocks the
+//   keys visible to the block's last row (block_keys), so that a prefill's
+//   early row blocks, which see few keys, are not given as much work as the
+//   late ones.  Every workgroup then streams the
 //   same number of tokens whatever the lengths are (they are read from
 //   kv_lens on the device, so the host never needs them).  A workgroup's range
 //   may start or end inside a segment and may cover several short segments;
@@ -41,6 +45,14 @@ struct WorkMap {
   int32_t chunk_len;  // mode 0
   int32_t n_chunks;   // mode 0
   int32_t n_wg;       // mode 1: number of workgroups W
+  // Mode 1 under a causal mask with several row blocks of the shared-tile
+  // kernel: row block rb holds query rows [rb*rpb, min(R, (rb+1)*rpb)); row r
+  // is query token r / G, which sees keys t <= L_b - q_len + r / G.
+  // causal_rows = 0: every segment is L_b long.  Kernels instantiated for
+  // maps without it clear the field in their copy of the map, so that the
+  // causal arithmetic folds away.
+  int32_t causal_rows;
+  int32_t q_len, G, R, rpb;
 };
 
 ATTN_HD int64_t seq_len(const WorkMap &m, int b) {
@@ -50,11 +62,93 @@ ATTN_HD int64_t seq_len(const WorkMap &m, int b) {
 
 ATTN_HD int64_t segs_per_seq(const WorkMap &m) { return (int64_t)m.Hkv * m.row_blocks; }
 
+// sum over i in [0, n) of floor((a*i + b) / c), for n, a, b >= 0 and c >= 1.
+// The lattice points under the line y = (a*x + b) / c are counted column by
+// column; after reducing a and b below c, the same points are counted row by
+// row, which is the sum with a and c exchanged: the Euclidean algorithm on
+// (a, c), so O(log c) steps.
+ATTN_HD int64_t floor_sum(int64_t n, int64_t c, int64_t a, int64_t b) {
+  int64_t s = 0;
+  while (n > 0) {
+    if (a >= c) {
+      s += (a / c) * (n * (n - 1) / 2);
+      a %= c;
+    }
+    if (b >= c) {
+      s += (b / c) * n;
+      b %= c;
+    }
+    const int64_t top = a * n + b;  // the line's height at x = n
+    if (top < c) break;
+    n = top / c;
+    b = top % c;
+    const int64_t t = c;
+    c = a;
+    a = t;
+  }
+  return s;
+}
+
+// Keys row block rb sees in a sequence of L keys (its segment length).
+ATTN_HD int64_t block_keys(const WorkMap &m, int64_t L, int64_t rb) {
+  if (!m.causal_rows) return L;
+  const int64_t end = (rb + 1) * m.rpb;
+  const int64_t last = (end < m.R ? end : m.R) - 1;  // the block's last row
+  const int64_t v = L - m.q_len + last / m.G + 1;
+  return v < 0 ? 0 : (v > L ? L : v);
+}
+
+// Keys of row blocks 0 .. n-1 together (0 <= n <= row_blocks), in closed form:
+// a block r below the last one is full, so it sees max(0, c + floor((rpb*r +
+// rpb - 1) / G)) keys with c = L - q_len + 1 (never more than L, as its last
+// row's token is below q_len).  The terms grow with r; they are positive from
+// r0 on.
+ATTN_HD int64_t keys_before(const WorkMap &m, int64_t L, int64_t n) {
+  if (!m.causal_rows) return L * n;
+  int64_t last_block = 0;
+  if (n == m.row_blocks && n > 0) {
+    last_block = block_keys(m, L, n - 1);
+    n -= 1;
+  }
+  const int64_t c = L - m.q_len + 1;
+  int64_t r0 = 0;
+  if (c < 1) {
+    const int64_t need = (int64_t)m.G * (1 - c) - (m.rpb - 1);  // positive from rpb*r >= need
+    r0 = need <= 0 ? 0 : (need + m.rpb - 1) / m.rpb;
+  }
+  if (n <= r0) return last_block;
+  if (m.rpb % m.G == 0) {
+    // Whole tokens per block (tpb of them): block r sees c - 1 + tpb*(r+1)
+    // keys, an arithmetic series.
+    const int64_t tpb = m.rpb / m.G;
+    return last_block + (n - r0) * (c - 1) + tpb * ((n * (n + 1) - r0 * (r0 + 1)) / 2);
+  }
+  return last_block + (n - r0) * c + floor_sum(n, m.G, m.rpb, m.rpb - 1) -
+         floor_sum(r0, m.G, m.rpb, m.rpb - 1);
+}
+
+// Units of one KV head of a sequence of L keys, and of the whole sequence.
+ATTN_HD int64_t head_units(const WorkMap &m, int64_t L) { return keys_before(m, L, m.row_blocks); }
+ATTN_HD int64_t seq_units(const WorkMap &m, int64_t L) { return m.Hkv * head_units(m, L); }
+
+// The row block whose segment holds unit rem of a KV head's units
+// (0 <= rem < head_units): the last block starting at or before rem.
+ATTN_HD int64_t block_of(const WorkMap &m, int64_t L, int64_t rem) {
+  if (!m.causal_rows) return rem / L;
+  int64_t lo = 0, hi = m.row_blocks - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (keys_before(m, L, mid) <= rem) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Total token units U of the balanced layout.
 ATTN_HD int64_t total_units(const WorkMap &m) {
   int64_t u = 0;
-  for (int b = 0; b < m.B; ++b) u += seq_len(m, b);
-  return u * segs_per_seq(m);
+  for (int b = 0; b < m.B; ++b) u += seq_units(m, seq_len(m, b));
+  return u;
 }
 
 // First unit of workgroup w (balanced): floor(w * U / W); wg_start(W) = U.
@@ -97,24 +191,28 @@ ATTN_HD PieceCursor first_piece(const WorkMap &m, int64_t U, int64_t w) {
 // Fills *p with the next piece of workgroup w and advances; false when done.
 ATTN_HD bool next_piece(const WorkMap &m, int64_t w, PieceCursor &c, Piece *p) {
   if (c.x >= c.xe) return false;
-  const int64_t S = segs_per_seq(m);
   int64_t L = seq_len(m, c.b);
-  while (c.PB + L * S <= c.x) {  // skip whole sequences (empty ones included)
-    c.PB += L * S;
+  int64_t Tk = head_units(m, L);
+  while (c.PB + m.Hkv * Tk <= c.x) {  // skip whole sequences (empty ones included)
+    c.PB += m.Hkv * Tk;
     ++c.b;
     L = seq_len(m, c.b);
+    Tk = head_units(m, L);
   }
   const int64_t within = c.x - c.PB;
-  const int64_t s_in_b = within / L;  // L > 0 here
-  const int64_t P = c.PB + s_in_b * L;
-  const int64_t end = P + L < c.xe ? P + L : c.xe;
-  p->sigma = (int64_t)c.b * S + s_in_b;
+  const int64_t kvh = within / Tk;  // Tk > 0 here
+  const int64_t rem = within - kvh * Tk;
+  const int64_t rb = block_of(m, L, rem);
+  const int64_t P = c.PB + kvh * Tk + keys_before(m, L, rb);
+  const int64_t len = block_keys(m, L, rb);
+  const int64_t end = P + len < c.xe ? P + len : c.xe;
+  p->sigma = ((int64_t)c.b * m.Hkv + kvh) * m.row_blocks + rb;
   p->t0 = c.x - P;
   p->t1 = end - P;
   p->slot = w + p->sigma;
   p->b = c.b;
-  p->kvh = (int32_t)(s_in_b / m.row_blocks);
-  p->rb = (int32_t)(s_in_b % m.row_blocks);
+  p->kvh = (int32_t)kvh;
+  p->rb = (int32_t)rb;
   c.x = end;
   return true;
 }
@@ -125,8 +223,8 @@ struct SlotRange {
   int64_t first, stride, count;
 };
 
-// As segment_slots below, with PB = sum of seq_len over sequences before b
-// (and U) already known.
+// As segment_slots below, with PB = the units of the sequences before b (the
+// sum of seq_units over them) and U already known.
 ATTN_HD SlotRange segment_slots_at(const WorkMap &m, int64_t U, int64_t PB, int b, int64_t sigma) {
   SlotRange r{0, 1, 0};
   const int64_t L = seq_len(m, b);
@@ -137,9 +235,12 @@ ATTN_HD SlotRange segment_slots_at(const WorkMap &m, int64_t U, int64_t PB, int 
     if (r.count > m.n_chunks) r.count = m.n_chunks;
     return r;
   }
-  const int64_t S = segs_per_seq(m);
-  const int64_t P = PB * S + (sigma - (int64_t)b * S) * L;
-  const int64_t w0 = wg_of_unit(m, U, P), w1 = wg_of_unit(m, U, P + L - 1);
+  const int64_t s_in_b = sigma - (int64_t)b * segs_per_seq(m);
+  const int64_t kvh = s_in_b / m.row_blocks, rb = s_in_b - kvh * m.row_blocks;
+  const int64_t len = block_keys(m, L, rb);
+  if (len == 0) return r;  // the block's rows see no key: no piece, no record
+  const int64_t P = PB + kvh * head_units(m, L) + keys_before(m, L, rb);
+  const int64_t w0 = wg_of_unit(m, U, P), w1 = wg_of_unit(m, U, P + len - 1);
   r.first = w0 + sigma;
   r.count = w1 - w0 + 1;
   return r;
@@ -148,7 +249,7 @@ ATTN_HD SlotRange segment_slots_at(const WorkMap &m, int64_t U, int64_t PB, int 
 ATTN_HD SlotRange segment_slots(const WorkMap &m, int64_t U, int b, int64_t sigma) {
   int64_t PB = 0;
   if (m.mode != 0)
-    for (int bb = 0; bb < b; ++bb) PB += seq_len(m, bb);
+    for (int bb = 0; bb < b; ++bb) PB += seq_units(m, seq_len(m, bb));
   return segment_slots_at(m, U, PB, b, sigma);
 }
 

@@ -169,6 +169,37 @@ def test_identical_keys_give_mean_of_v():
     check_rows(O, lse, Or, lr, what="identical keys")
 
 
+CAUSAL_BLOCKS = [
+    # B, q_len, Hq, Hkv, D, L, dtype, lens: causal calls over several row blocks
+    (1, 96, 8, 2, 128, 700, "bf16", None),         # 384 rows: two blocks of 256
+    (2, 300, 4, 1, 128, 1000, "bf16", [200, 1000]),  # q_len > L_b: early blocks see nothing
+    (2, 7, 6, 2, 128, 500, "f32", [500, 5]),      # vector ALUs, 3 blocks of 8 rows
+    (3, 40, 16, 2, 64, 333, "bf16", [333, 0, 41]),   # 320 rows, an empty sequence
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL_BLOCKS, ids=[f"B{c[0]}_ql{c[1]}_Hq{c[2]}_Hkv{c[3]}_D{c[4]}_L{c[5]}_{c[6]}" for c in CAUSAL_BLOCKS])
+def test_causal_query_blocks_over_several_row_blocks(case):
+    """Each row block of a causal call is given only the keys its rows can
+    see; every row still matches the oracle, and rows that see no key give
+    lse = -inf and O = 0."""
+    B, q_len, Hq, Hkv, D, L, dt, lens = case
+    say(f"causal row blocks {case}")
+    w = inputs.make_decode("causal_blocks", 900 + L, B=B, q_len=q_len, Hq=Hq, Hkv=Hkv, D=D,
+                           L_max=L, kv_lens=lens, dtype=dt, causal=True, nan_pad=True)
+    desc = binding.make_desc(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                             max_kv_len=L, causal=True,
+                             dtype=binding.ATTN_BF16 if dt == "bf16" else binding.ATTN_F32)
+    assert binding.plan(desc, 256)["row_blocks"] > 1
+    O, lse = run_decode(w)
+    Or, lr = oracle_decode(w)
+    check_rows(O, lse, Or, lr, what=f"causal row blocks {case}")
+    q, k, v, lens_t = workload_tensors(w)
+    lse_e = binding.decode_energy(q, k, lens_t, causal=True)
+    torch.cuda.synchronize()
+    check_rows(None, lse_e.cpu().numpy(), None, lr, what=f"causal row blocks energy {case}")
+
+
 def test_huge_logits_are_stable():
     w = inputs.make_decode("huge", 8, B=1, q_len=1, Hq=4, Hkv=1, D=128, L_max=4000, dtype="f32")
     w.q *= np.float32(40.0)  # logits of several hundred

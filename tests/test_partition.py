@@ -68,12 +68,25 @@ def test_small_calls_use_fewer_workgroups():
     assert p["work_items"] == 0 and p["workspace_bytes"] == 0
 
 
+def segment_keys(d, p, L_b, rb):
+    """Keys a segment of the layout covers: all L_b, or under a causal mask
+    with several row blocks of the shared-tile kernel (balanced layout) the
+    keys the block's last row sees (written out from the visibility rule
+    t <= L_b - q_len + i)."""
+    if not (p["balanced"] and d.causal and p["row_blocks"] > 1 and p["kernel"] == 2):
+        return L_b
+    G = d.num_q_heads // d.num_kv_heads
+    last_row = min(p["rows"], (rb + 1) * p["rows_per_block"]) - 1
+    return min(L_b, max(0, L_b - d.q_len + last_row // G + 1))
+
+
 def check_cover(d, lens, cu):
     p = binding.plan(d, cu)
     B, Hkv = d.batch, d.num_kv_heads
     rbk = p["row_blocks"]
     L = np.full(B, d.max_kv_len) if lens is None else np.minimum(np.maximum(lens, 0), d.max_kv_len)
     segs = B * Hkv * rbk
+    seg_len = [segment_keys(d, p, int(L[s // (Hkv * rbk)]), s % rbk) for s in range(segs)]
     covered = {s: [] for s in range(segs)}
     slots = set()
     per_wg = []
@@ -81,14 +94,14 @@ def check_cover(d, lens, cu):
         pieces = binding.testing_pieces(d, lens, cu, w)
         per_wg.append(sum(t1 - t0 for (_, t0, t1, _) in pieces))
         for (s, t0, t1, slot) in pieces:
-            assert 0 <= t0 < t1 <= L[s // (Hkv * rbk)], (s, t0, t1)
+            assert 0 <= t0 < t1 <= seg_len[s], (s, t0, t1)
             assert 0 <= slot < p["record_slots"], (slot, p["record_slots"])
             assert slot not in slots
             slots.add(slot)
             covered[s].append((t0, t1, slot))
     for s in range(segs):
         iv = sorted(covered[s])
-        Ls = int(L[s // (Hkv * rbk)])
+        Ls = seg_len[s]
         pos = 0
         for (t0, t1, _) in iv:
             assert t0 == pos
@@ -115,6 +128,35 @@ def test_pieces_tile_every_segment_exactly_once(B, Hkv, G, q_len, L, cu, forced,
              max_kv_len=L, chunk_len=forced, kv_lens_ptr=0x1000 if ragged else 0,
              causal=q_len > 1)
     check_cover(d, lens, cu)
+
+
+@settings(max_examples=150, deadline=None)
+@given(B=st.integers(1, 4), Hkv=st.integers(1, 3), G=st.integers(1, 8), q_len=st.integers(1, 160),
+       L=st.integers(0, 3000), cu=st.sampled_from([1, 5, 40, 256]), seed=st.integers(0, 2 ** 31),
+       ragged=st.booleans(), dt=st.sampled_from([binding.ATTN_BF16, binding.ATTN_F32]))
+def test_causal_row_blocks_get_only_visible_keys(B, Hkv, G, q_len, L, cu, seed, ragged, dt):
+    """Causal query blocks spanning several row blocks (prefill-like): each
+    segment covers exactly the keys its last row sees, the pieces still tile
+    every segment once, and workgroups get equal shares of visible keys."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, L + 1, size=B).astype(np.int32) if ragged else None
+    d = desc(batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, q_len=q_len, max_kv_len=L,
+             kv_lens_ptr=0x1000 if ragged else 0, causal=True, dtype=dt)
+    check_cover(d, lens, cu)
+
+
+def test_anchor_prefill_local_part_is_balanced_over_visible_keys():
+    """Causal prefill of 2 blocks of 8192 tokens (Hq=32, Hkv=8): 128 row
+    blocks of 64 tokens per KV head, which see 64, 128, ..., 8192 keys."""
+    d = desc(batch=2, q_len=8192, num_q_heads=32, num_kv_heads=8, max_kv_len=8192, causal=True)
+    p = binding.plan(d, 256)
+    assert p["kernel"] == 2 and p["row_blocks"] == 128
+    units = 2 * 8 * sum(64 * (rb + 1) for rb in range(128))
+    per_wg = []
+    for w in range(p["work_items"]):
+        per_wg.append(sum(t1 - t0 for (_, t0, t1, _) in binding.testing_pieces(d, None, 256, w)))
+    assert sum(per_wg) == units
+    assert max(per_wg) - min(per_wg) <= 1
 
 
 def test_ragged_70b_shape_is_balanced():
