@@ -12,7 +12,7 @@ Prints one JSON line: KV tokens/s (value), whole-path HBM GB/s against the
 from HIP events recorded on the stream it runs on), and the fp64 CPU oracle
 timed on a bounded sample of the same workload.  Whole-call times are also
 given as median / 10th / 90th percentile, for the back-to-back timed calls
-(call_ms) and for calls that each follow a 1 GiB write evicting L2 and the
+(call_ms) and for calls that each follow a 1 GiB read evicting L2 and the
 Infinity Cache (call_ms_cold_cache; the bifurcated batch, ~203 MB, would
 otherwise stay cache-resident between calls).
 """
@@ -78,7 +78,7 @@ def parse():
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged workloads: tokens per page (0: the workload's own, 16)")
     ap.add_argument("--cold-calls", type=int, default=20,
-                    help="extra calls after the timed steps, each behind a 1 GiB write that "
+                    help="extra calls after the timed steps, each behind a 1 GiB read that "
                          "evicts L2 and the Infinity Cache (0: skip)")
     return ap.parse_args()
 
@@ -418,13 +418,16 @@ def spread(ms):
 
 def cold_calls(torch, run, n):
     """Whole-call times (HIP events around every launch of the call) with the
-    caches cleared before each call by a 1 GiB write, outside the events."""
+    caches cleared before each call by a 1 GiB read, outside the events.  A
+    read rather than a write: evicted dirty lines would otherwise be written
+    back to HBM while the timed call runs."""
     stream = torch.cuda.current_stream()
-    junk = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    junk = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     for i in range(n):
-        junk.fill_(i)
+        torch.amax(junk)
         ev[i][0].record(stream)
         run.first()
         run.second()
