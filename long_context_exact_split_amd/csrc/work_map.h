@@ -9,21 +9,22 @@
 // * fixed chunks (mode 0): workgroup w = sigma * n_chunks + c covers tokens
 //   [c*C, min((c+1)*C, L_b)) of segment sigma; record slot = w.
 //
-// * balanced (mode 1): the segments are laid end to end (offset of sigma =
-//   sum of the lengths before it) into U token units, and workgroup w takes
-//   units [floor(w*U/W), floor((w+1)*U/W)).  A segment is as long as the keys
-//   its rows can see: L_b, or under a causal mask with several row blocks the
-//   keys visible to the block's last row (block_keys), so that a prefill's
-//   early row blocks, which see few keys, are not given as much work as the
-//   late ones.  Every workgroup then streams the
-//   same number of tokens whatever the lengths are (they are read from
-//   kv_lens on the device, so the host never needs them).  A workgroup's range
-//   may start or end inside a segment and may cover several short segments;
-//   each (w, sigma) piece gives one record, stored at slot w + sigma.  The
-//   pieces form a monotone staircase in the (w, sigma) grid, so distinct
-//   pieces never share a slot, and W + #segments slots suffice.  (LeanAttention,
-//   among the related work on the Bifurcated Attention page, balances decode
-//   work across the GPU in the same spirit.)
+// * balanced (mode 1): the segments are laid end to end into U token units
+//   (sequence by sequence, KV head by KV head, and within a KV head the row
+//   blocks in layout order, see block_at), and workgroup w takes units
+//   [floor(w*U/W), floor((w+1)*U/W)).  A segment is as long as the keys its
+//   rows can see: L_b, or under a causal mask with several row blocks of the
+//   shared-tile kernel the keys visible to the block's last row (block_keys),
+//   so that a prefill's early row blocks, which see few keys, are not given
+//   as much work as the late ones.  Every workgroup then streams the same
+//   number of keys whatever the lengths are (they are read from kv_lens on
+//   the device, so the host never needs them).  A workgroup's range may start
+//   or end inside a segment and may cover several short segments; each piece
+//   gives one record, stored at slot w + (the segment's index in layout
+//   order).  The pieces form a monotone staircase in the (w, layout index)
+//   grid, so distinct pieces never share a slot, and W + #segments slots
+//   suffice.  (LeanAttention, among the related work on the Bifurcated
+//   Attention page, balances decode work across the GPU in the same spirit.)
 #pragma once
 
 #include <stdint.h>
@@ -131,14 +132,42 @@ ATTN_HD int64_t keys_before(const WorkMap &m, int64_t L, int64_t n) {
 ATTN_HD int64_t head_units(const WorkMap &m, int64_t L) { return keys_before(m, L, m.row_blocks); }
 ATTN_HD int64_t seq_units(const WorkMap &m, int64_t L) { return m.Hkv * head_units(m, L); }
 
-// The row block whose segment holds unit rem of a KV head's units
-// (0 <= rem < head_units): the last block starting at or before rem.
-ATTN_HD int64_t block_of(const WorkMap &m, int64_t L, int64_t rem) {
+// Order of the row blocks of one KV head in the layout.  Causal row blocks
+// go in zigzag order 0, n-1, 1, n-2, ... (n = row_blocks): block j and block
+// n-1-j together see about as many keys as any other such pair, so every
+// stretch of the layout mixes short and long segments and workgroups end up
+// with similar numbers of pieces, each of which costs a pipeline start and a
+// record write.  Otherwise the natural order.
+ATTN_HD int64_t block_at(const WorkMap &m, int64_t pos) {
+  if (!m.causal_rows) return pos;
+  const int64_t j = pos / 2;
+  return (pos & 1) ? m.row_blocks - 1 - j : j;
+}
+
+ATTN_HD int64_t pos_of(const WorkMap &m, int64_t rb) {
+  if (!m.causal_rows) return rb;
+  const int64_t mirror = m.row_blocks - 1 - rb;
+  return rb <= mirror ? 2 * rb : 2 * mirror + 1;
+}
+
+// Units of the layout positions before pos (0 <= pos <= row_blocks) of one
+// KV head: for pos = 2j the pairs (i, n-1-i), i < j, which are the first j
+// blocks and the last j; for pos = 2j+1 also block j.
+ATTN_HD int64_t units_before(const WorkMap &m, int64_t L, int64_t pos) {
+  if (!m.causal_rows) return L * pos;
+  const int64_t j = pos / 2;
+  const int64_t even = keys_before(m, L, j) + head_units(m, L) - keys_before(m, L, m.row_blocks - j);
+  return (pos & 1) ? even + block_keys(m, L, j) : even;
+}
+
+// The layout position whose segment holds unit rem of a KV head's units
+// (0 <= rem < head_units): the last position starting at or before rem.
+ATTN_HD int64_t position_of(const WorkMap &m, int64_t L, int64_t rem) {
   if (!m.causal_rows) return rem / L;
   int64_t lo = 0, hi = m.row_blocks - 1;
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) / 2;
-    if (keys_before(m, L, mid) <= rem) lo = mid;
+    if (units_before(m, L, mid) <= rem) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -164,7 +193,11 @@ ATTN_HD int64_t wg_of_unit(const WorkMap &m, int64_t U, int64_t x) {
   return ((x + 1) * (int64_t)m.n_wg - 1) / U;
 }
 
-// One piece of work: tokens [t0, t1) of segment sigma, record slot `slot`.
+// One piece of work: tokens [t0, t1) of segment sigma (numbered
+// (b * Hkv + kvh) * row_blocks + rb), record slot `slot`.  Slots number the
+// segments in layout order: slot = w + (b * Hkv + kvh) * row_blocks + the
+// segment's layout position, which grows along the layout as w does, so
+// distinct pieces never share a slot.
 struct Piece {
   int64_t sigma;
   int64_t t0, t1;
@@ -202,14 +235,16 @@ ATTN_HD bool next_piece(const WorkMap &m, int64_t w, PieceCursor &c, Piece *p) {
   const int64_t within = c.x - c.PB;
   const int64_t kvh = within / Tk;  // Tk > 0 here
   const int64_t rem = within - kvh * Tk;
-  const int64_t rb = block_of(m, L, rem);
-  const int64_t P = c.PB + kvh * Tk + keys_before(m, L, rb);
+  const int64_t pos = position_of(m, L, rem);
+  const int64_t rb = block_at(m, pos);
+  const int64_t P = c.PB + kvh * Tk + units_before(m, L, pos);
   const int64_t len = block_keys(m, L, rb);
   const int64_t end = P + len < c.xe ? P + len : c.xe;
-  p->sigma = ((int64_t)c.b * m.Hkv + kvh) * m.row_blocks + rb;
+  const int64_t group = (int64_t)c.b * m.Hkv + kvh;
+  p->sigma = group * m.row_blocks + rb;
   p->t0 = c.x - P;
   p->t1 = end - P;
-  p->slot = w + p->sigma;
+  p->slot = w + group * m.row_blocks + pos;
   p->b = c.b;
   p->kvh = (int32_t)kvh;
   p->rb = (int32_t)rb;
@@ -239,9 +274,10 @@ ATTN_HD SlotRange segment_slots_at(const WorkMap &m, int64_t U, int64_t PB, int 
   const int64_t kvh = s_in_b / m.row_blocks, rb = s_in_b - kvh * m.row_blocks;
   const int64_t len = block_keys(m, L, rb);
   if (len == 0) return r;  // the block's rows see no key: no piece, no record
-  const int64_t P = PB + kvh * head_units(m, L) + keys_before(m, L, rb);
+  const int64_t pos = pos_of(m, rb);
+  const int64_t P = PB + kvh * head_units(m, L) + units_before(m, L, pos);
   const int64_t w0 = wg_of_unit(m, U, P), w1 = wg_of_unit(m, U, P + len - 1);
-  r.first = w0 + sigma;
+  r.first = w0 + (sigma - rb + pos);
   r.count = w1 - w0 + 1;
   return r;
 }

@@ -157,6 +157,10 @@ def test_anchor_prefill_local_part_is_balanced_over_visible_keys():
         per_wg.append(sum(t1 - t0 for (_, t0, t1, _) in binding.testing_pieces(d, None, 256, w)))
     assert sum(per_wg) == units
     assert max(per_wg) - min(per_wg) <= 1
+    # Zigzag order of the row blocks: every workgroup gets as many pieces
+    # (each costs a pipeline start and a record write), not 4 here and 30 there.
+    pieces = [len(binding.testing_pieces(d, None, 256, w)) for w in range(p["work_items"])]
+    assert max(pieces) - min(pieces) <= 1
 
 
 def test_ragged_70b_shape_is_balanced():
