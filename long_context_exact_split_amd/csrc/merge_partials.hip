@@ -63,75 +63,71 @@ __device__ __forceinline__ RowRecords row_records(const MergeArgs &a, int b, int
 
 // Rows with many records (a long cache cut into many pieces): one workgroup
 // per output row.  The row's records are read in parallel: 16 bytes of o per
-// lane, kMergeThreads / (D/4) records per pass, so a row of ~100 records
-// takes a handful of passes instead of a serial walk.  The max over the
-// records is a block-wide reduction (DPP within waves, LDS across them); each
-// record is then rescaled once and the partial sums of the record groups are
-// added through LDS in a fixed order (deterministic).
+// lane, kMergeThreads / (D/4) record groups, each combining its records in
+// one pass with the rule itself (running max, earlier sums rescaled when it
+// grows), so no separate pass over the records' maxima has to come first.
+// The groups' results are then combined through LDS in a fixed order
+// (deterministic).  Every wave works out where the row's records are by
+// itself, so no barrier comes before the first record load.
 constexpr int kMergeThreads = 256;
 
 template <int D, bool ENERGY, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   constexpr int LPR = D / 4;                 // lanes per record (float4 each)
-  constexpr int NG = kMergeThreads / LPR;    // records in flight per pass
+  constexpr int NG = kMergeThreads / LPR;    // record groups
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const int64_t row = blockIdx.x;
   const int r = (int)(row % a.R);
   const int group = (int)(row / a.R);
   const int b = group / a.map.Hkv;
   const int kvh = group - b * a.map.Hkv;
 
-  __shared__ RowRecords where;
-  if (wave == 0) {
-    const RowRecords rr = row_records<CAUSAL_ROWS>(a, b, kvh, r);
-    if (lane == 0) where = rr;
-  }
-  __syncthreads();
-  const int P = where.P, S = where.S;
-  const int64_t prow = where.prow, pstride = where.pstride, srow = where.srow,
-                sstride = where.sstride;
-  auto rec_of = [&](int c) { return c < P ? prow + c * pstride : srow + (c - P) * sstride; };
-  auto m_of = [&](int c) { return c < P ? a.part.m[prow + c * pstride] : a.shared.m[srow + (c - P) * sstride]; };
-
-  __shared__ float red[kMergeThreads / kWave];
-  float M = -INFINITY;
-  for (int c = tid; c < P + S; c += kMergeThreads) M = fmaxf(M, m_of(c));
-  M = wave_max(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / kWave; ++w) M = fmaxf(M, red[w]);
-
+  const RowRecords rr = row_records<CAUSAL_ROWS>(a, b, kvh, r);
+  const int n = rr.P + rr.S;
   const int cg = tid / LPR;   // record group
   const int dl = tid % LPR;   // float4 slot within the record
-  float lsum = 0.0f;
+  float Mg = -INFINITY, lg = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = cg; c < P + S; c += NG) {
-    const bool shared = c >= P;
-    const int64_t rec = rec_of(c);
-    const float f = rescale_factor(shared ? a.shared.m[rec] : a.part.m[rec], M);
-    lsum += f * (shared ? a.shared.l[rec] : a.part.l[rec]);
+#pragma unroll 2
+  for (int c = cg; c < n; c += NG) {
+    const bool shared = c >= rr.P;
+    const int64_t rec = shared ? rr.srow + (c - rr.P) * rr.sstride : rr.prow + c * rr.pstride;
+    const PartialLayout &pl = shared ? a.shared : a.part;
+    const float mc = pl.m[rec], lc = pl.l[rec];
+    const float Mn = fmaxf(Mg, mc);
+    const float fa = rescale_factor(Mg, Mn), fb = rescale_factor(mc, Mn);
+    lg = lg * fa + lc * fb;
     if constexpr (!ENERGY) {
-      const float *op = (shared ? a.shared.o : a.part.o) + rec * D + dl * 4;
-      const float4 v = *reinterpret_cast<const float4 *>(op);
-      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+      const float4 v = *reinterpret_cast<const float4 *>(pl.o + rec * D + dl * 4);
+      acc.x = acc.x * fa + v.x * fb;
+      acc.y = acc.y * fa + v.y * fb;
+      acc.z = acc.z * fa + v.z * fb;
+      acc.w = acc.w * fa + v.w * fb;
     }
+    Mg = Mn;
   }
-  __shared__ float sl[NG];
+  __shared__ float sm[NG], sl[NG];
   __shared__ float4 so[ENERGY ? 1 : NG][ENERGY ? 1 : LPR];
-  if (dl == 0) sl[cg] = lsum;
+  if (dl == 0) {
+    sm[cg] = Mg;
+    sl[cg] = lg;
+  }
   if constexpr (!ENERGY) so[cg][dl] = acc;
   __syncthreads();
 
   const int i = r / a.G;
   const int h = kvh * a.G + (r - i * a.G);
   const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
+  float M = sm[0];
+#pragma unroll
+  for (int g = 1; g < NG; ++g) M = fmaxf(M, sm[g]);
+  float f[NG];
   float ltot = 0.0f;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) ltot += sl[g];
+  for (int g = 0; g < NG; ++g) {
+    f[g] = rescale_factor(sm[g], M);
+    ltot += sl[g] * f[g];
+  }
   const bool empty = M == -INFINITY || !(ltot > 0.0f);
   if (tid == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(ltot)) * kLn2;
   if constexpr (!ENERGY) {
@@ -140,7 +136,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const float4 v = so[g][tid];
-        t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+        t.x += v.x * f[g]; t.y += v.y * f[g]; t.z += v.z * f[g]; t.w += v.w * f[g];
       }
       const float inv = empty ? 0.0f : 1.0f / ltot;
       float *dst = a.o + orow * D + tid * 4;  // O is only 4-byte aligned
