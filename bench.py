@@ -442,8 +442,8 @@ def cold_calls(torch, run, n):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(the multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1 "
+                                   "(sharding the KV cache across GPUs is not implemented)"}))
         sys.exit(2)
     import torch
 
