@@ -150,9 +150,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
 // there are hundreds of thousands of them (a prefill's query rows), four
 // waves per workgroup.  Rows of one row block have their records in the same
 // slots, one record row apart, so a run works out where they are once per
-// block.  Records are combined one after another in index order
-// (deterministic); each lane holds D/64 of the row's outputs.
+// block.  A row's records are loaded together and combined one after another
+// in index order with the merge rule (deterministic); each lane holds D/64 of
+// the row's outputs.
 constexpr int kRowsPerMergeBlock = 4;
+constexpr int kRowBatch = 4;  // records of one row loaded together
 
 template <int D, bool ENERGY, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeArgs a,
@@ -183,29 +185,42 @@ __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeAr
       key_s = ks;
     }
     const int n = rr.P + rr.S;
-    auto rec_of = [&](int c) {
-      return c < rr.P ? rr.prow + c * rr.pstride : rr.srow + (c - rr.P) * rr.sstride;
-    };
-
-    float M = -INFINITY;
-    for (int c = lane; c < n; c += kWave) {
-      const int64_t rec = rec_of(c);
-      M = fmaxf(M, c < rr.P ? a.part.m[rec] : a.shared.m[rec]);
-    }
-    M = wave_max(M);
-    float lsum = 0.0f, acc[EPL];
+    // Up to kRowBatch records are loaded at once (one memory round trip for
+    // a row of that many), then combined in index order with the rule itself.
+    float M = -INFINITY, lsum = 0.0f, acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-#pragma unroll 4
-    for (int c = 0; c < n; ++c) {
-      const bool sh = c >= rr.P;
-      const int64_t rec = rec_of(c);
-      const float f = rescale_factor(sh ? a.shared.m[rec] : a.part.m[rec], M);
-      lsum += f * (sh ? a.shared.l[rec] : a.part.l[rec]);
-      if constexpr (!ENERGY) {
-        const float *op = (sh ? a.shared.o : a.part.o) + rec * D + lane * EPL;
+    for (int c0 = 0; c0 < n; c0 += kRowBatch) {
+      float mc[kRowBatch], lc[kRowBatch], oc[ENERGY ? 1 : kRowBatch][EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += f * op[e];
+      for (int k = 0; k < kRowBatch; ++k) {
+        const int c = c0 + k;
+        mc[k] = -INFINITY;
+        lc[k] = 0.0f;
+        if constexpr (!ENERGY)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) oc[k][e] = 0.0f;
+        if (c < n) {
+          const bool sh = c >= rr.P;
+          const int64_t rec = sh ? rr.srow + (c - rr.P) * rr.sstride : rr.prow + c * rr.pstride;
+          const PartialLayout &pl = sh ? a.shared : a.part;
+          mc[k] = pl.m[rec];
+          lc[k] = pl.l[rec];
+          if constexpr (!ENERGY)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) oc[k][e] = pl.o[rec * D + lane * EPL + e];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kRowBatch; ++k) {
+        if (c0 + k >= n) break;
+        const float Mn = fmaxf(M, mc[k]);
+        const float fa = rescale_factor(M, Mn), fb = rescale_factor(mc[k], Mn);
+        lsum = lsum * fa + lc[k] * fb;
+        if constexpr (!ENERGY)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * fa + oc[k][e] * fb;
+        M = Mn;
       }
     }
     const int i = r / a.G;
