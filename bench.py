@@ -466,6 +466,12 @@ def main():
         run = DecodeRunner(torch, w, mode, paging)
     print(f"# plan {run.plan}", file=sys.stderr, flush=True)
 
+    K = args.steps
+    # Events are created before the warm-up: creating them afterwards would
+    # leave the GPU idle long enough for its clocks to drop again.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    stream = torch.cuda.current_stream()
+
     # Untimed warm-up: at least --warmup steps and --min-warmup-s seconds.  From
     # idle the GPU needs ~30-40 back-to-back steps (~25 ms) to reach its
     # steady clocks; the timed region measures the steady state.
@@ -476,11 +482,6 @@ def main():
         warm += 1
         if warm % 16 == 0:
             torch.cuda.synchronize()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()  # barrier (one rank)
     t0 = time.perf_counter()
     for i in range(K):
