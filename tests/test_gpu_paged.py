@@ -52,6 +52,9 @@ PAGED = [
     (1, 2, 8, 1, 64, 1000, "bf16", True, None, 8, "token_major", 0, 0),
     (2, 4, 16, 2, 128, 1500, "bf16", True, [1500, 1100], 1024, "head_major", 1024, 0),
     (2, 6, 16, 1, 128, 2000, "bf16", True, [2000, 900], 32, "token_major", 512, 2),
+    # causal query blocks over several row blocks of 256 (each sees only its keys)
+    (1, 96, 8, 2, 128, 700, "bf16", True, None, 16, "head_major", 0, 1),
+    (2, 130, 16, 4, 64, 900, "bf16", True, [900, 300], 32, "token_major", 0, 2),
 ]
 
 
