@@ -374,6 +374,26 @@ def test_bifurcated_degenerate_parts():
         check_rows(O[:, None], lse[:, None], Or[:, None], lr[:, None], what=f"bifurcated Lp={Lp} Ls={Ls}")
 
 
+BIF_MANY = [
+    # S, Hq, Hkv, D, Lp, Ls: many samples (at least one sample x KV head per CU)
+    (32, 32, 8, 128, 1000, 77),
+    (64, 8, 4, 64, 0, 50),       # no prefix: the suffix alone
+    (32, 16, 8, 128, 300, 1),    # one suffix token
+    (32, 32, 8, 128, 700, 0),    # no suffix
+    (32, 128, 8, 128, 500, 100),  # 16 rows per KV head: the suffix runs on the matrix cores
+]
+
+
+@pytest.mark.parametrize("case", BIF_MANY, ids=[f"S{c[0]}_Hq{c[1]}_Hkv{c[2]}_D{c[3]}_Lp{c[4]}_Ls{c[5]}" for c in BIF_MANY])
+def test_bifurcated_many_samples(case):
+    S, Hq, Hkv, D, Lp, Ls = case
+    say(f"bifurcated {case}")
+    w = inputs.bifurcated_prefix(seed=43 + Ls, S=S, Hq=Hq, Hkv=Hkv, D=D, Lp=Lp, Ls=Ls)
+    O, lse = run_bifurcated(w)
+    Or, lr = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale)
+    check_rows(O[:, None], lse[:, None], Or[:, None], lr[:, None], what=f"bifurcated {case}")
+
+
 def test_bifurcated_full_size():
     w = inputs.bifurcated_prefix(seed=4)
     O, lse = run_bifurcated(w)
