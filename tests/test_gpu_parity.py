@@ -200,6 +200,38 @@ def test_causal_query_blocks_over_several_row_blocks(case):
     check_rows(None, lse_e.cpu().numpy(), None, lr, what=f"causal row blocks energy {case}")
 
 
+TWO_PHASE = [
+    # B, q_len, Hq, Hkv, D, L, causal, lens, energy
+    (2, 1, 32, 8, 128, 3000, False, [3000, 1234], False),   # vector ALUs
+    (2, 4, 64, 8, 128, 4500, True, [4500, 4096], False),    # 32-row matrix-core kernel
+    (1, 96, 8, 2, 128, 700, True, None, False),             # shared-tile, causal row blocks
+    (2, 130, 16, 4, 64, 900, True, [900, 300], True),       # the same, energy only
+]
+
+
+@pytest.mark.parametrize("case", TWO_PHASE, ids=[f"B{c[0]}_ql{c[1]}_Hq{c[2]}_Hkv{c[3]}_D{c[4]}{'_energy' if c[8] else ''}" for c in TWO_PHASE])
+def test_two_phases_give_the_one_call_result(case):
+    """attn_decode_partials then attn_decode_merge (each planning the call by
+    itself) reproduce attn_decode / attn_decode_energy bit for bit."""
+    B, q_len, Hq, Hkv, D, L, causal, lens, energy = case
+    w = inputs.make_decode("phases", 950 + L, B=B, q_len=q_len, Hq=Hq, Hkv=Hkv, D=D, L_max=L,
+                           kv_lens=lens, causal=causal, nan_pad=True)
+    q, k, v, lens_t = workload_tensors(w)
+    ph = binding.Phases(q, k, None if energy else v, lens_t, scale=w.scale, causal=causal)
+    ph.partials()
+    ph.merge()
+    if energy:
+        lse1 = binding.decode_energy(q, k, lens_t, scale=w.scale, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(ph.lse, lse1)
+    else:
+        O1, lse1 = binding.decode(q, k, v, lens_t, scale=w.scale, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(ph.out, O1) and torch.equal(ph.lse, lse1)
+    _, lr = oracle.attend(w.q, w.k, None, w.kv_lens, w.scale, causal)
+    check_rows(None, ph.lse.cpu().numpy(), None, lr, what=f"two phases {case}")
+
+
 def test_huge_logits_are_stable():
     w = inputs.make_decode("huge", 8, B=1, q_len=1, Hq=4, Hkv=1, D=128, L_max=4000, dtype="f32")
     w.q *= np.float32(40.0)  # logits of several hundred
