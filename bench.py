@@ -286,19 +286,12 @@ class BifurcatedRunner:
     """The shared-prefix call, timed as one unit (three launches)."""
 
     def __init__(self, torch, w):
-        import ctypes
         from long_context_exact_split_amd import binding
         self.w, self.binding = w, binding
         self.t = [dev(torch, x) for x in (w.q, w.kp, w.vp, w.ks, w.vs)]
-        self.out = torch.empty((w.S, w.Hq, w.D), dtype=torch.float32, device="cuda")
-        self.lse = torch.empty((w.S, w.Hq), dtype=torch.float32, device="cuda")
-        d = binding.bifurcated_desc(self.t[0], self.t[1], self.t[3], w.scale)
-        n = ctypes.c_size_t(0)
-        st = binding.load_library().attn_bifurcated_workspace_bytes(ctypes.byref(d),
-                                                                      ctypes.byref(n))
-        assert st == 0, st
-        self.ws = torch.empty(max(1, n.value), dtype=torch.uint8, device="cuda")
-        self.plan = {"prefix_rows": w.S * w.G, "workspace_bytes": n.value}
+        self.call = binding.BifurcatedCall(*self.t, scale=w.scale)
+        self.out, self.lse = self.call.out, self.call.lse
+        self.plan = {"prefix_rows": w.S * w.G, "workspace_bytes": self.call.nbytes}
         self.kv_tokens = w.S * (w.Lp + w.Ls)             # logical tokens attended
         self.kv_bytes = 2 * (w.Lp + w.S * w.Ls) * w.Hkv * w.D * 2   # physical bytes read
         self.q_bytes = w.S * w.Hq * w.D * 2
@@ -307,9 +300,7 @@ class BifurcatedRunner:
         self.kernel = "bifurcated (prefix split kernel + suffix split kernel + merge)"
 
     def first(self):
-        q, kp, vp, ks, vs = self.t
-        self.binding.decode_bifurcated(q, kp, vp, ks, vs, scale=self.w.scale, out=self.out,
-                                       lse=self.lse, workspace=self.ws)
+        self.call.run()
 
     def second(self):
         pass

@@ -498,6 +498,38 @@ def decode_bifurcated(q, k_prefix, v_prefix, k_suffix, v_suffix, *, scale: Optio
     return out, lse
 
 
+class BifurcatedCall:
+    """attn_decode_bifurcated prepared once for fixed tensors: descriptor,
+    outputs and workspace are set up here, and ``run()`` is only the C call
+    (for repeated calls, where the per-call Python work would otherwise be
+    comparable to the GPU time of a small batch)."""
+
+    def __init__(self, q, k_prefix, v_prefix, k_suffix, v_suffix, *, scale=None):
+        torch = _torch()
+        self.lib = load_library()
+        _check_tensors(q, k_prefix, v_prefix, k_suffix, v_suffix)
+        if v_prefix.shape != k_prefix.shape or v_suffix.shape != k_suffix.shape:
+            raise ValueError("v tensors must match k tensors")
+        self.desc = bifurcated_desc(q, k_prefix, k_suffix, scale)
+        S, Hq, D = q.shape
+        with torch.cuda.device(q.device):
+            self.out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+            self.lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+            n = ctypes.c_size_t(0)
+            _check(self.lib.attn_bifurcated_workspace_bytes(ctypes.byref(self.desc), ctypes.byref(n)),
+                   "attn_bifurcated_workspace_bytes")
+            self.ws = _workspace(n.value, q.device, None)
+            self.stream = _stream_ptr(q.device)
+        self.nbytes = 0 if self.ws is None else self.ws.numel()
+        self.args = [ctypes.byref(self.desc)] + [_ptr(t) for t in (q, k_prefix, v_prefix, k_suffix,
+                                                                   v_suffix, self.out, self.lse)]
+        self.args += [_ptr(self.ws), self.nbytes, self.stream]
+
+    def run(self):
+        _check(self.lib.attn_decode_bifurcated(*self.args), "attn_decode_bifurcated")
+        return self.out, self.lse
+
+
 def anchor_desc(q, k_anchor, k_blocks, scale=None) -> AttnAnchorDesc:
     if q.dim() != 4 or k_anchor.dim() != 3 or k_blocks.dim() != 4:
         raise ValueError("q [N,Lb,Hq,D], k_anchor [Hkv,A,D], k_blocks [N,Hkv,Lb,D]")

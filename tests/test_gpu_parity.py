@@ -426,6 +426,19 @@ def test_bifurcated_many_samples(case):
     check_rows(O[:, None], lse[:, None], Or[:, None], lr[:, None], what=f"bifurcated {case}")
 
 
+def test_prepared_bifurcated_call_matches_the_plain_call():
+    """BifurcatedCall (set up once, run repeatedly) gives decode_bifurcated's
+    result bit for bit, on every run."""
+    w = inputs.bifurcated_prefix(seed=44, S=32, Lp=2000, Ls=300)
+    t = [dev(x) for x in (w.q, w.kp, w.vp, w.ks, w.vs)]
+    O0, lse0 = binding.decode_bifurcated(*t, scale=w.scale)
+    call = binding.BifurcatedCall(*t, scale=w.scale)
+    for _ in range(2):
+        O1, lse1 = call.run()
+        torch.cuda.synchronize()
+        assert torch.equal(O0, O1) and torch.equal(lse0, lse1)
+
+
 def test_bifurcated_full_size():
     w = inputs.bifurcated_prefix(seed=4)
     O, lse = run_bifurcated(w)
