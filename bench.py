@@ -14,7 +14,8 @@ timed on a bounded sample of the same workload.  Whole-call times are also
 given as median / 10th / 90th percentile, for the back-to-back timed calls
 (call_ms) and for calls that each follow a 1 GiB read evicting L2 and the
 Infinity Cache (call_ms_cold_cache; the bifurcated batch, ~203 MB, would
-otherwise stay cache-resident between calls).
+otherwise stay cache-resident between calls), and for the call captured once
+into a HIP graph and replayed (call_ms_graph, with the wall time per replay).
 """
 import argparse
 import json
@@ -77,6 +78,8 @@ def parse():
                     help="skip the HBM read-stream reference measurement")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged workloads: tokens per page (0: the workload's own, 16)")
+    ap.add_argument("--graph-calls", type=int, default=100,
+                    help="extra calls replayed from a captured HIP graph (0: skip)")
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="extra calls after the timed steps, each behind a 1 GiB read that "
                          "evicts L2 and the Infinity Cache (0: skip)")
@@ -224,8 +227,9 @@ class DecodeRunner:
             self.plan = binding.plan(desc)
             self.plan["kernel"] = 0  # F(zeta) always runs on the vector-ALU kernel
         else:
-            self.ph = binding.Phases(q, k, None if mode == "energy" else v, lens, scale=w.scale,
-                                     causal=w.causal, chunk_len=w.chunk_len, paged=paged)
+            self.ph_args = ((q, k, None if mode == "energy" else v, lens),
+                            dict(scale=w.scale, causal=w.causal, chunk_len=w.chunk_len, paged=paged))
+            self.ph = binding.Phases(*self.ph_args[0], **self.ph_args[1])
             self.plan = self.ph.plan
         esz = 2 if w.dtype == "bf16" else 4
         self.kv_tokens = int(w.kv_lens.sum())
@@ -253,6 +257,18 @@ class DecodeRunner:
     def second(self):
         if self.mode != "zeta":
             self.ph.merge()
+
+    def make_graph_call(self):
+        """The call on buffers of its own, bound to the current stream (for
+        capture into a HIP graph); None when not capturable as is."""
+        if self.mode == "zeta":
+            return None
+        ph = self.binding.Phases(*self.ph_args[0], **self.ph_args[1])
+
+        def call():
+            ph.partials()
+            ph.merge()
+        return call
 
     def outputs(self):
         if self.mode == "zeta":
@@ -301,6 +317,10 @@ class BifurcatedRunner:
 
     def first(self):
         self.call.run()
+
+    def make_graph_call(self):
+        call = self.binding.BifurcatedCall(*self.t, scale=self.w.scale)
+        return call.run
 
     def second(self):
         pass
@@ -430,6 +450,46 @@ def cold_calls(torch, run, n):
     return out
 
 
+def graph_calls(torch, run, n):
+    """Whole-call times when the call is captured once into a HIP graph and
+    replayed (no per-call host work: what a serving loop would do).  The call
+    gets buffers of its own, bound to a side stream that is captured."""
+    make = getattr(run, "make_graph_call", None)
+    if make is None:
+        return None
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        call = make()
+        if call is None:
+            return None
+        for _ in range(3):
+            call()
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 0.3:  # clocks up again
+        g.replay()
+    for i in range(n):
+        ev[i][0].record(stream)
+        g.replay()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        g.replay()
+    torch.cuda.synchronize()
+    out = spread([a.elapsed_time(b) for a, b in ev])
+    out["wall_ms_per_call"] = (time.perf_counter() - t0) * 1e3 / n
+    del g
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -529,6 +589,8 @@ def main():
                               "kernel": run.kernel, "algorithmic_flops_per_launch": run.flops}
     if args.cold_calls > 0:
         result["call_ms_cold_cache"] = cold_calls(torch, run, args.cold_calls)
+    if args.graph_calls > 0:
+        result["call_ms_graph"] = graph_calls(torch, run, args.graph_calls)
     if not args.no_ceiling:
         ceil = read_ceiling(torch)
         result["hbm_read_ceiling_gbps"] = ceil

@@ -439,6 +439,45 @@ def test_prepared_bifurcated_call_matches_the_plain_call():
         assert torch.equal(O0, O1) and torch.equal(lse0, lse1)
 
 
+def test_graph_replays_match_eager_calls():
+    """A decode (split + merge) and a bifurcated call captured into one HIP
+    graph (prepared calls bound to the capturing stream; the library launches
+    kernels only, no memset, no allocation) and replayed three times, with
+    eager work and synchronisation between the replays: every replay gives
+    the eager results bit for bit."""
+    w = inputs.make_decode("graph", 77, B=2, q_len=1, Hq=32, Hkv=8, D=128, L_max=3000,
+                           kv_lens=[3000, 1500], nan_pad=True)
+    q, k, v, lens = workload_tensors(w)
+    O0, lse0 = binding.decode(q, k, v, lens, scale=w.scale)
+    wb = inputs.bifurcated_prefix(seed=45, S=8, Lp=700, Ls=90)
+    tb = [dev(x) for x in (wb.q, wb.kp, wb.vp, wb.ks, wb.vs)]
+    Ob0, lseb0 = binding.decode_bifurcated(*tb, scale=wb.scale)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        ph = binding.Phases(q, k, v, lens, scale=w.scale)
+        bc = binding.BifurcatedCall(*tb, scale=wb.scale)
+        ph.partials()
+        ph.merge()
+        bc.run()
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        ph.partials()
+        ph.merge()
+        bc.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (ph.out, ph.lse, bc.out, bc.lse):
+            t.fill_(float("nan"))
+        binding.decode(q, k, v, lens, scale=w.scale)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ph.out, O0) and torch.equal(ph.lse, lse0), f"decode, replay {rep}"
+        assert torch.equal(bc.out, Ob0) and torch.equal(bc.lse, lseb0), f"bifurcated, replay {rep}"
+
+
 def test_bifurcated_full_size():
     w = inputs.bifurcated_prefix(seed=4)
     O, lse = run_bifurcated(w)
