@@ -36,6 +36,9 @@
  * on the stream completes.  The library allocates nothing, keeps no device
  * state, never synchronises, and caches only the CU count per device.  All
  * work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ * The calls enqueue kernel launches only (no memset, copy or allocation), so
+ * a call may be captured into a HIP graph on a capturing stream and the
+ * graph replayed, as long as every buffer it names stays alive.
  *
  * Null tensors are accepted where they would hold no element (K and V when
  * max_kv_len == 0, every tensor when B == 0).
