@@ -713,7 +713,7 @@ template <int D, int RW, bool ENERGY, bool PAGED, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
   __shared__ RowsSmem<D, RW, ENERGY> sh;
   WorkMap m = a.map;
-  if constexpr (!CAUSAL_ROWS) m.causal_rows = 0;  // the launcher checked it is 0
+  m.causal_rows = CAUSAL_ROWS ? 1 : 0;  // as the launcher checked; known at compile time
   if (m.mode == 0) {
     const int w = blockIdx.x;
     const int sigma = w / m.n_chunks, c = w - sigma * m.n_chunks;
@@ -723,6 +723,41 @@ __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
     const int c0 = c * m.chunk_len;
     if (c0 >= L) return;
     rows_piece<D, RW, ENERGY, PAGED>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
+  } else if constexpr (CAUSAL_ROWS) {
+    // The causal layout's arithmetic (closed-form sums, a binary search per
+    // piece) runs on one lane, a batch of pieces at a time, into LDS; the
+    // tile loop then runs with none of its state held in registers (inlined
+    // next to the loop it cost SGPR spills and ~5% more VALU per tile).
+    constexpr int kBatch = 16;
+    __shared__ PieceCursor cur_s;
+    __shared__ Piece list[kBatch];
+    __shared__ int count;
+    if (threadIdx.x == 0) cur_s = first_piece(m, total_units(m), blockIdx.x);
+    for (;;) {
+      __syncthreads();  // every wave is done with the previous batch
+      if (threadIdx.x == 0) {
+        PieceCursor c = cur_s;
+        int n = 0;
+        Piece p;
+        while (n < kBatch && next_piece(m, blockIdx.x, c, &p)) list[n++] = p;
+        cur_s = c;
+        count = n;
+      }
+      __syncthreads();
+      const int n = __builtin_amdgcn_readfirstlane(count);
+      if (n == 0) break;
+      for (int k = 0; k < n; ++k) {
+        const Piece &p = list[k];
+        const int b = __builtin_amdgcn_readfirstlane(p.b);
+        const int kvh = __builtin_amdgcn_readfirstlane(p.kvh);
+        const int rb = __builtin_amdgcn_readfirstlane(p.rb);
+        const int t0 = __builtin_amdgcn_readfirstlane((int)p.t0);
+        const int t1 = __builtin_amdgcn_readfirstlane((int)p.t1);
+        const int64_t slot = ((int64_t)__builtin_amdgcn_readfirstlane((int)(p.slot >> 32)) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(p.slot & 0xffffffff));
+        rows_piece<D, RW, ENERGY, PAGED>(a, b, kvh, rb, t0, t1, slot, sh);
+      }
+    }
   } else {
     const int64_t U = total_units(m);
     PieceCursor cur = first_piece(m, U, blockIdx.x);

@@ -67,23 +67,24 @@ ATTN_HD int64_t segs_per_seq(const WorkMap &m) { return (int64_t)m.Hkv * m.row_b
 // The lattice points under the line y = (a*x + b) / c are counted column by
 // column; after reducing a and b below c, the same points are counted row by
 // row, which is the sum with a and c exchanged: the Euclidean algorithm on
-// (a, c), so O(log c) steps.
-ATTN_HD int64_t floor_sum(int64_t n, int64_t c, int64_t a, int64_t b) {
+// (a, c), so O(log c) steps.  The callers' arguments are row counts (a*n + b
+// stays below 2^31, as R <= 2^16), so the divisions are 32-bit.
+ATTN_HD int64_t floor_sum(int32_t n, int32_t c, int32_t a, int32_t b) {
   int64_t s = 0;
   while (n > 0) {
     if (a >= c) {
-      s += (a / c) * (n * (n - 1) / 2);
+      s += (int64_t)(a / c) * ((int64_t)n * (n - 1) / 2);
       a %= c;
     }
     if (b >= c) {
-      s += (b / c) * n;
+      s += (int64_t)(b / c) * n;
       b %= c;
     }
-    const int64_t top = a * n + b;  // the line's height at x = n
+    const int32_t top = a * n + b;  // the line's height at x = n
     if (top < c) break;
     n = top / c;
     b = top % c;
-    const int64_t t = c;
+    const int32_t t = c;
     c = a;
     a = t;
   }
@@ -93,8 +94,8 @@ ATTN_HD int64_t floor_sum(int64_t n, int64_t c, int64_t a, int64_t b) {
 // Keys row block rb sees in a sequence of L keys (its segment length).
 ATTN_HD int64_t block_keys(const WorkMap &m, int64_t L, int64_t rb) {
   if (!m.causal_rows) return L;
-  const int64_t end = (rb + 1) * m.rpb;
-  const int64_t last = (end < m.R ? end : m.R) - 1;  // the block's last row
+  const int32_t end = ((int32_t)rb + 1) * m.rpb;
+  const int32_t last = (end < m.R ? end : m.R) - 1;  // the block's last row (< 2^16)
   const int64_t v = L - m.q_len + last / m.G + 1;
   return v < 0 ? 0 : (v > L ? L : v);
 }
@@ -112,19 +113,22 @@ ATTN_HD int64_t keys_before(const WorkMap &m, int64_t L, int64_t n) {
     n -= 1;
   }
   const int64_t c = L - m.q_len + 1;
-  int64_t r0 = 0;
+  int32_t r0 = 0;
   if (c < 1) {
-    const int64_t need = (int64_t)m.G * (1 - c) - (m.rpb - 1);  // positive from rpb*r >= need
+    // Positive from rpb*r >= need; need <= G*q_len = R, so 32-bit.
+    const int32_t need = (int32_t)((int64_t)m.G * (1 - c)) - (m.rpb - 1);
     r0 = need <= 0 ? 0 : (need + m.rpb - 1) / m.rpb;
   }
-  if (n <= r0) return last_block;
+  const int32_t n32 = (int32_t)n;  // n <= row_blocks <= 2^16
+  if (n32 <= r0) return last_block;
   if (m.rpb % m.G == 0) {
     // Whole tokens per block (tpb of them): block r sees c - 1 + tpb*(r+1)
     // keys, an arithmetic series.
     const int64_t tpb = m.rpb / m.G;
-    return last_block + (n - r0) * (c - 1) + tpb * ((n * (n + 1) - r0 * (r0 + 1)) / 2);
+    return last_block + (int64_t)(n32 - r0) * (c - 1) +
+           tpb * (((int64_t)n32 * (n32 + 1) - (int64_t)r0 * (r0 + 1)) / 2);
   }
-  return last_block + (n - r0) * c + floor_sum(n, m.G, m.rpb, m.rpb - 1) -
+  return last_block + (int64_t)(n32 - r0) * c + floor_sum(n32, m.G, m.rpb, m.rpb - 1) -
          floor_sum(r0, m.G, m.rpb, m.rpb - 1);
 }
 

@@ -28,6 +28,7 @@ ANCHOR = [
     (2, 300, 32, 8, 128, 777),   # 1200 rows, ragged tiles
     (2, 64, 4, 4, 128, 0),       # no anchor: causal within each block
     (1, 257, 16, 2, 128, 1000),  # 2056 rows
+    (2, 10, 32, 4, 128, 500),    # 80 rows: one row block
 ]
 
 
