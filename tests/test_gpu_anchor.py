@@ -72,3 +72,23 @@ def test_anchor_blocks_bench_shape_sampled():
     rows = [(b, i, h) for b in range(N) for i in (0, 1, Lb // 2, Lb - 1) for h in range(Hq)]
     Or, lr = oracle.attend_anchor_blocks(q, ka, va, kb, vb, scale, rows=rows)
     check_rows(O.cpu().numpy(), lse.cpu().numpy(), Or, lr, rows=rows, what="anchor bench shape")
+
+
+def test_anchor_too_small_workspace_is_refused():
+    """A workspace one byte short: ATTN_ERR_WORKSPACE and untouched outputs."""
+    import ctypes
+    lib = binding.load_library()
+    q, ka, va, kb, vb = make(2, 100, 8, 2, 128, 300, seed=3)
+    t = [dev(x) for x in (q, ka, va, kb, vb)]
+    d = binding.anchor_desc(t[0], t[1], t[3], 1.0 / np.sqrt(128))
+    n = ctypes.c_size_t(0)
+    assert lib.attn_anchor_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0 and n.value > 0
+    ws = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+    O = torch.full((2, 100, 8, 128), 7.0, device="cuda")
+    lse = torch.full((2, 100, 8), 7.0, device="cuda")
+    st = lib.attn_prefill_anchor(ctypes.byref(d), *[x.data_ptr() for x in t], O.data_ptr(),
+                                 lse.data_ptr(), ws.data_ptr(), n.value - 1,
+                                 torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert binding.STATUS[st] == "ATTN_ERR_WORKSPACE"
+    assert (O == 7.0).all() and (lse == 7.0).all()

@@ -232,6 +232,41 @@ def test_two_phases_give_the_one_call_result(case):
     check_rows(None, ph.lse.cpu().numpy(), None, lr, what=f"two phases {case}")
 
 
+def test_too_small_workspace_is_refused_and_nothing_is_written():
+    """A workspace below the size query's answer: ATTN_ERR_WORKSPACE, and the
+    outputs keep their contents (nothing was launched)."""
+    import ctypes
+    lib = binding.load_library()
+    w = inputs.make_decode("ws", 12, B=2, q_len=1, Hq=8, Hkv=2, D=128, L_max=3000)
+    q, k, v, _ = workload_tensors(w)
+    d = binding.make_desc(batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                          max_kv_len=3000, scale=w.scale)
+    need = binding.workspace_bytes(d)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    O = torch.full((2, 1, 8, 128), 7.0, device="cuda")
+    lse = torch.full((2, 1, 8), 7.0, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    st = lib.attn_decode(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(),
+                         lse.data_ptr(), ws.data_ptr(), need - 1, stream)
+    torch.cuda.synchronize()
+    assert binding.STATUS[st] == "ATTN_ERR_WORKSPACE"
+    assert (O == 7.0).all() and (lse == 7.0).all()
+    wb = inputs.bifurcated_prefix(seed=46, S=4, Lp=300, Ls=40)
+    tb = [dev(x) for x in (wb.q, wb.kp, wb.vp, wb.ks, wb.vs)]
+    bd = binding.bifurcated_desc(tb[0], tb[1], tb[3], wb.scale)
+    n = ctypes.c_size_t(0)
+    assert lib.attn_bifurcated_workspace_bytes(ctypes.byref(bd), ctypes.byref(n)) == 0 and n.value > 0
+    wsb = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+    Ob = torch.full((4, wb.Hq, wb.D), 7.0, device="cuda")
+    lseb = torch.full((4, wb.Hq), 7.0, device="cuda")
+    st = lib.attn_decode_bifurcated(ctypes.byref(bd), *[t.data_ptr() for t in tb], Ob.data_ptr(),
+                                    lseb.data_ptr(), wsb.data_ptr(), n.value - 1, stream)
+    torch.cuda.synchronize()
+    assert binding.STATUS[st] == "ATTN_ERR_WORKSPACE"
+    assert (Ob == 7.0).all() and (lseb == 7.0).all()
+
+
 def test_huge_logits_are_stable():
     w = inputs.make_decode("huge", 8, B=1, q_len=1, Hq=4, Hkv=1, D=128, L_max=4000, dtype="f32")
     w.q *= np.float32(40.0)  # logits of several hundred
