@@ -19,7 +19,7 @@ from long_context_exact_split_amd import binding, inputs
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n=40, seed=2024):
+def _cases(n=120, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for k in range(n):
