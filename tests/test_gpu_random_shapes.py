@@ -6,7 +6,8 @@ both merges at once: batch sizes, query blocks (causal or not, up to several
 row blocks of the shared-tile kernel, GQA ratios that do and do not divide a
 row block), head sizes, element types, ragged and empty sequences, forced
 chunk lengths, paged pools of several page sizes and both layouts, and
-energy-only calls.
+energy-only calls; and random bifurcated batches (empty prefix or suffix
+included) and anchor-block prefills (empty anchor included).
 """
 import numpy as np
 import pytest
@@ -82,3 +83,59 @@ def test_random_shape(case):
     Or, lr = oracle.attend(w.q, w.k, None if energy else w.v, w.kv_lens, w.scale, causal)
     check_rows(None if O is None else O.cpu().numpy(), lse.cpu().numpy(), Or, lr,
                what=f"random {_id(case)}")
+
+
+def _bif_cases(n=24, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        Hkv = int(rng.integers(1, 5))
+        G = int(rng.integers(1, 10))
+        out.append((k, int(rng.integers(1, 80)), G * Hkv, Hkv, int(rng.choice([64, 128])),
+                    int(rng.integers(0, 3000)), int(rng.integers(0, 700))))
+    return out
+
+
+BIF = _bif_cases()
+
+
+@pytest.mark.parametrize("case", BIF, ids=[f"{c[0]:02d}_S{c[1]}_Hq{c[2]}_Hkv{c[3]}_D{c[4]}_Lp{c[5]}_Ls{c[6]}" for c in BIF])
+def test_random_bifurcated(case):
+    k, S, Hq, Hkv, D, Lp, Ls = case
+    say(f"random bifurcated {case}")
+    w = inputs.bifurcated_prefix(seed=500 + k, S=S, Hq=Hq, Hkv=Hkv, D=D, Lp=Lp, Ls=Ls)
+    O, lse = binding.decode_bifurcated(*[dev(x) for x in (w.q, w.kp, w.vp, w.ks, w.vs)],
+                                       scale=w.scale)
+    torch.cuda.synchronize()
+    Or, lr = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale)
+    check_rows(O.cpu().numpy()[:, None], lse.cpu().numpy()[:, None], Or[:, None], lr[:, None],
+               what=f"random bifurcated {case}")
+
+
+def _anchor_cases(n=24, seed=99):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.integers(1, 9))
+        out.append((k, int(rng.integers(1, 4)), int(rng.integers(1, 260)), G * Hkv, Hkv,
+                    int(rng.choice([64, 128])), int(rng.integers(0, 1200))))
+    return out
+
+
+ANCHOR = _anchor_cases()
+
+
+@pytest.mark.parametrize("case", ANCHOR, ids=[f"{c[0]:02d}_N{c[1]}_Lb{c[2]}_Hq{c[3]}_Hkv{c[4]}_D{c[5]}_A{c[6]}" for c in ANCHOR])
+def test_random_anchor_blocks(case):
+    k, N, Lb, Hq, Hkv, D, A = case
+    say(f"random anchor {case}")
+    rng = np.random.default_rng(900 + k)
+    bits = lambda *s: inputs.f32_to_bf16(rng.standard_normal(s, dtype=np.float32))
+    q, ka, va, kb, vb = (bits(N, Lb, Hq, D), bits(Hkv, A, D), bits(Hkv, A, D),
+                         bits(N, Hkv, Lb, D), bits(N, Hkv, Lb, D))
+    scale = 1.0 / np.sqrt(D)
+    O, lse = binding.prefill_anchor(dev(q), dev(ka), dev(va), dev(kb), dev(vb), scale=scale)
+    torch.cuda.synchronize()
+    Or, lr = oracle.attend_anchor_blocks(q, ka, va, kb, vb, scale)
+    check_rows(O.cpu().numpy(), lse.cpu().numpy(), Or, lr, what=f"random anchor {case}")
