@@ -19,8 +19,14 @@ struct RowRecords {
   int32_t P, S;
 };
 
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(x & 0xffffffff));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+  return ((int64_t)hi << 32) | (uint32_t)lo;
+}
+
 // Run by a whole wave (the sums of sequence units are wave reductions);
-// every lane gets the result.
+// every lane gets the result, marked wave-uniform for the compiler.
 // CAUSAL_ROWS = false: neither map has causal segment lengths (the launcher
 // checked), and the copies below say so at compile time.
 template <bool CAUSAL_ROWS>
@@ -58,6 +64,12 @@ __device__ __forceinline__ RowRecords row_records(const MergeArgs &a, int b, int
     rr.srow = sr.first * RBs + rs % RBs;
     rr.sstride = sr.stride * RBs;
   }
+  rr.prow = uniform_i64(rr.prow);
+  rr.pstride = uniform_i64(rr.pstride);
+  rr.srow = uniform_i64(rr.srow);
+  rr.sstride = uniform_i64(rr.sstride);
+  rr.P = __builtin_amdgcn_readfirstlane(rr.P);
+  rr.S = __builtin_amdgcn_readfirstlane(rr.S);
   return rr;
 }
 
@@ -92,13 +104,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   for (int c = cg; c < n; c += NG) {
     const bool shared = c >= rr.P;
     const int64_t rec = shared ? rr.srow + (c - rr.P) * rr.sstride : rr.prow + c * rr.pstride;
-    const PartialLayout &pl = shared ? a.shared : a.part;
-    const float mc = pl.m[rec], lc = pl.l[rec];
+    // Pointers chosen as values: a reference to either argument struct would
+    // be read back from argument memory before every record.
+    const float mc = (shared ? a.shared.m : a.part.m)[rec];
+    const float lc = (shared ? a.shared.l : a.part.l)[rec];
     const float Mn = fmaxf(Mg, mc);
     const float fa = rescale_factor(Mg, Mn), fb = rescale_factor(mc, Mn);
     lg = lg * fa + lc * fb;
     if constexpr (!ENERGY) {
-      const float4 v = *reinterpret_cast<const float4 *>(pl.o + rec * D + dl * 4);
+      const float4 v =
+          *reinterpret_cast<const float4 *>((shared ? a.shared.o : a.part.o) + rec * D + dl * 4);
       acc.x = acc.x * fa + v.x * fb;
       acc.y = acc.y * fa + v.y * fb;
       acc.z = acc.z * fa + v.z * fb;
@@ -203,12 +218,13 @@ __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeAr
         if (c < n) {
           const bool sh = c >= rr.P;
           const int64_t rec = sh ? rr.srow + (c - rr.P) * rr.sstride : rr.prow + c * rr.pstride;
-          const PartialLayout &pl = sh ? a.shared : a.part;
-          mc[k] = pl.m[rec];
-          lc[k] = pl.l[rec];
-          if constexpr (!ENERGY)
+          mc[k] = (sh ? a.shared.m : a.part.m)[rec];  // pointers as values, as above
+          lc[k] = (sh ? a.shared.l : a.part.l)[rec];
+          if constexpr (!ENERGY) {
+            const float *po = (sh ? a.shared.o : a.part.o) + rec * D + lane * EPL;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) oc[k][e] = pl.o[rec * D + lane * EPL + e];
+            for (int e = 0; e < EPL; ++e) oc[k][e] = po[e];
+          }
         }
       }
 #pragma unroll
