@@ -470,7 +470,10 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
 // instead of once per block of 32 rows.  No cross-wave merge: each wave
 // writes the records of its own 32 rows.
 // ---------------------------------------------------------------------------
-constexpr int kRowsBufs = 4;  // LDS tile buffers of the shared-tile kernel
+// LDS tile buffers of the shared-tile kernel, and how many iterations ahead
+// of its first use a tile is stored into them (one barrier per two tiles).
+constexpr int kRowsBufs = 6;
+constexpr int kStoreAhead = 4;
 
 template <int D, int RW, bool ENERGY>
 union RowsSmem {
@@ -541,6 +544,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   // t % NS) feeding two LDS buffers.  Stage indices are compile-time inside
   // the unrolled inner loop, so the ring stays in registers.
   constexpr int NS = RW >= 8 ? 3 : (RW >= 4 ? 2 : 1);
+  constexpr int SA = kStoreAhead;
   u32x4 kr[NS][PER], vr[NS][ENERGY ? 1 : PER];
   // Token of this thread's copy piece i of a tile (clamped to a valid row).
   auto token = [&](int tile, int i) {
@@ -582,17 +586,22 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   //   the softmax of tile t+1 (vector ALUs),
   // three independent pieces of work that can overlap; the rescale of O that
   // the softmax of tile t+1 asks for is applied before the P.V of tile t+1.
-  // LDS holds four tiles: t (V being read), t+1 (V next), t+2 (K being read)
-  // and t+3 (being stored from the register ring); one barrier per
-  // iteration.  Tiles past the last read the last visible row again, and
-  // the S^T of a tile past the last is computed but never used.
+  // LDS holds six tiles, tile x in buffer x % 6; iteration t stores tile t+4
+  // from the register ring, and a workgroup barrier follows odd iterations
+  // only.  Both hazards still cross a barrier: the K of tile t+2 read in
+  // iteration t was stored in iteration t-2, and the buffer that iteration t
+  // overwrites last held tile t-2, whose V was read in iteration t-2; a
+  // barrier follows iteration t-2 or t-1, whichever is odd.  (A barrier per
+  // iteration with four buffers ran 3% slower on long pieces.)  Tiles past
+  // the last read the last visible row again, and the S^T of a tile past the
+  // last is computed but never used.
   // Register ring: tile x lives in stage x % NS; paged caches: the
-  // block-table loads of tile x are issued in iteration x - 2 - 2*NS, NS - 1
-  // iterations before the K/V loads of x (iteration x - 3 - NS), so waiting
+  // block-table loads of tile x are issued in iteration x - 3 - 2*NS, NS - 1
+  // iterations before the K/V loads of x (iteration x - 4 - NS), so waiting
   // for them never waits for K/V loads still in the ring; their results live
   // in a ring of page-id stages (tile x in stage x % NS).
-  auto kbuf = [&](int tile) { return sh.t.k[tile & (kRowsBufs - 1)]; };
-  auto vbuf = [&](int tile) { return sh.t.v[tile & (kRowsBufs - 1)]; };
+  auto kbuf = [&](int tile) { return sh.t.k[(unsigned)tile % kRowsBufs]; };
+  auto vbuf = [&](int tile) { return sh.t.v[(unsigned)tile % kRowsBufs]; };
   int32_t pr[NS][PER];
   for (int s2 = 0; s2 < NS; ++s2)
     for (int i = 0; i < PER; ++i) pr[s2][i] = 0;
@@ -600,24 +609,24 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   bf16x8_t phi[2], plo[2];  // P^T of tile t
   float pend = 1.0f;        // O rescale owed before the next P.V
   if (n_tiles > 0) {
-    // Tiles 0..2 into LDS, tiles 3..2+NS into the register ring.
+    // Tiles 0..SA-1 into LDS, tiles SA..SA-1+NS into the register ring.
 #pragma unroll
-    for (int x = 0; x < 3; ++x) {
+    for (int x = 0; x < SA; ++x) {
       int32_t p0[PER];
       lookup(x, p0);
       load(x, p0, kr[x % NS], vr[x % NS]);
-      store(x & (kRowsBufs - 1), kr[x % NS], vr[x % NS]);
+      store(x % kRowsBufs, kr[x % NS], vr[x % NS]);
     }
     settle<KS>(qf);
 #pragma unroll
-    for (int x = 3; x < 3 + NS; ++x) {
+    for (int x = SA; x < SA + NS; ++x) {
       int32_t p0[PER];
       lookup(x, p0);
       load(x, p0, kr[x % NS], vr[x % NS]);
     }
     if constexpr (PAGED) {
 #pragma unroll
-      for (int x = 3 + NS; x <= 1 + 2 * NS; ++x) lookup(x, pr[x % NS]);
+      for (int x = SA + NS; x <= SA - 2 + 2 * NS; ++x) lookup(x, pr[x % NS]);
     }
     __syncthreads();
     pend = softmax_tile<ENERGY>(qk_tile<D>(kbuf(0), qf), c0, lim, scale_log2, m, lsum, phi, plo);
@@ -648,9 +657,13 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
     }
   };
-  for (int base = 0; base < n_tiles - 1; base += NS) {
+  // U iterations per unrolled round: a multiple of NS (ring stages), of the
+  // buffer count and of 2, so stages and barrier parity are constants.
+  constexpr int U = 6;
+  static_assert(U % NS == 0 && U % kRowsBufs == 0, "ring stages and buffers cycle within U");
+  for (int base = 0; base < n_tiles - 1; base += U) {
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
+    for (int k = 0; k < U; ++k) {
       const int tile = base + k;
       if (tile >= n_tiles - 1) break;  // uniform across the workgroup
       if (__any(pend != 1.0f)) rescale_o<D, ENERGY>(oacc, pend);
@@ -658,11 +671,11 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
         body(tile, std::integral_constant<int, 0>{});
       else
         body(tile, std::integral_constant<int, 1>{});
-      if constexpr (PAGED) lookup(tile + 2 + 2 * NS, pr[(k + 2) % NS]);
-      const int st = (k + 3) % NS;  // stage of tile + 3 (constant once unrolled)
-      store((tile + 3) & (kRowsBufs - 1), kr[st], vr[st]);
-      load(tile + 3 + NS, pr[st], kr[st], vr[st]);
-      __syncthreads();
+      if constexpr (PAGED) lookup(tile + SA - 1 + 2 * NS, pr[(k + SA - 1) % NS]);
+      const int st = (k + SA) % NS;  // stage of tile + SA (constant once unrolled)
+      store((unsigned)(tile + SA) % kRowsBufs, kr[st], vr[st]);
+      load(tile + SA + NS, pr[st], kr[st], vr[st]);
+      if (k & 1) __syncthreads();  // after odd tiles only
     }
   }
   if (n_tiles > 0) {  // the last tile's P.V
