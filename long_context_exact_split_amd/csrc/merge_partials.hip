@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   const int dl = tid % LPR;   // float4 slot within the record
   float Mg = -INFINITY, lg = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 2
+#pragma unroll 4  // four records of a group in flight (unroll 2: 2-8% slower, 8: 18%)
   for (int c = cg; c < n; c += NG) {
     const bool shared = c >= rr.P;
     const int64_t rec = shared ? rr.srow + (c - rr.P) * rr.sstride : rr.prow + c * rr.pstride;
