@@ -10,28 +10,16 @@
 #include "plan.h"
 
 #include <cmath>
-#include <cstdlib>
 #include <limits>
 
 namespace attn {
 namespace {
-
-int env_int(const char *name, int fallback, int lo, int hi) {
-  const char *s = std::getenv(name);
-  if (!s || !*s) return fallback;
-  char *end = nullptr;
-  long v = std::strtol(s, &end, 10);
-  if (end == s || v < lo || v > hi) return fallback;
-  return (int)v;
-}
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
 int items_per_cu(int kernel, int64_t units, int cu_count) {
-  static const int forced = env_int("ATTN_DECODE_ITEMS_PER_CU", 0, 1, 1024);
-  if (forced > 0) return forced;
   // Short shares on the vector-ALU kernel: each workgroup's load pipeline
   // starts and drains once per piece, and two workgroups per CU overlap one
   // another's start-up (measured: 512-token segments, 9% faster).

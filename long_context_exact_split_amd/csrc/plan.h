@@ -18,7 +18,7 @@ constexpr int kMaxRows = 1 << 16;        // G * q_len limit
 constexpr int64_t kMaxUnits = int64_t(1) << 46;  // B * Hkv * row_blocks * max_kv_len limit
 // Workgroups per CU in the balanced layout: one contiguous share of the
 // tokens per CU, which measured fastest on MI355X (each CU streams one long
-// run of K/V).  Overridable with ATTN_DECODE_ITEMS_PER_CU for experiments.
+// run of K/V).
 constexpr int kItemsPerCu = 1;
 // Tokens per CU below which the vector-ALU kernel gets twice the workgroups.
 constexpr int64_t kShortShare = 2048;
