@@ -722,6 +722,22 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   }
 }
 
+// Workgroups are dealt to the eight XCDs in turn (workgroup w runs on XCD
+// w % 8), and each XCD has its own L2.  When a KV head's tiles are read by
+// several row blocks (a prefill's query blocks), neighbouring pieces of the
+// balanced layout share them, so the logical index is permuted to give each
+// XCD one contiguous stretch of the layout (a bijection of [0, n)).  With
+// one row block per KV head (a shared prefix) no piece shares tiles with
+// another and the identity is kept: there the permutation measured 4%
+// slower, against 3% faster on the anchor-block prefill.
+__device__ __forceinline__ int xcd_local_index(int w, int n, bool shared_tiles) {
+  if (!shared_tiles) return w;
+  constexpr int kXcds = 8;
+  const int x = w % kXcds, j = w / kXcds;
+  const int q = n / kXcds, r = n % kXcds;
+  return x * q + min(x, r) + j;
+}
+
 template <int D, int RW, bool ENERGY, bool PAGED, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
   __shared__ RowsSmem<D, RW, ENERGY> sh;
@@ -745,14 +761,15 @@ __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
     __shared__ PieceCursor cur_s;
     __shared__ Piece list[kBatch];
     __shared__ int count;
-    if (threadIdx.x == 0) cur_s = first_piece(m, total_units(m), blockIdx.x);
+    const int wl = xcd_local_index(blockIdx.x, m.n_wg, m.row_blocks > 1);
+    if (threadIdx.x == 0) cur_s = first_piece(m, total_units(m), wl);
     for (;;) {
       __syncthreads();  // every wave is done with the previous batch
       if (threadIdx.x == 0) {
         PieceCursor c = cur_s;
         int n = 0;
         Piece p;
-        while (n < kBatch && next_piece(m, blockIdx.x, c, &p)) list[n++] = p;
+        while (n < kBatch && next_piece(m, wl, c, &p)) list[n++] = p;
         cur_s = c;
         count = n;
       }
@@ -773,9 +790,10 @@ __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
     }
   } else {
     const int64_t U = total_units(m);
-    PieceCursor cur = first_piece(m, U, blockIdx.x);
+    const int wl = xcd_local_index(blockIdx.x, m.n_wg, m.row_blocks > 1);
+    PieceCursor cur = first_piece(m, U, wl);
     Piece p;
-    while (next_piece(m, blockIdx.x, cur, &p))
+    while (next_piece(m, wl, cur, &p))
       rows_piece<D, RW, ENERGY, PAGED>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
   }
 }
