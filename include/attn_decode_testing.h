@@ -29,6 +29,18 @@ int64_t attn_testing_pieces(const attn_desc_t *desc, const int32_t *host_lens, i
 attn_status_t attn_testing_segment_slots(const attn_desc_t *desc, const int32_t *host_lens,
                                          int32_t cu_count, int64_t segment, int64_t out[3]);
 
+/* Whether attn_prefill_anchor takes its finalising path for this shape on
+ * cu_count CUs: 1 when every segment of both the anchor part and the local
+ * part is a single piece (the local split then merges each row's two
+ * records itself and no merge launch follows), 0 otherwise, or a negative
+ * attn_status_t on invalid arguments. */
+int32_t attn_testing_anchor_fuses(const attn_anchor_desc_t *desc, int32_t cu_count);
+
+/* enabled = 0 makes attn_prefill_anchor always take the unfused path
+ * (anchor split, local split, merge), 1 restores the default.  Process-wide;
+ * for comparing the two paths in tests. */
+void attn_testing_set_anchor_fusion(int32_t enabled);
+
 #ifdef __cplusplus
 }
 #endif

@@ -133,6 +133,10 @@ def load_library():
         lib.attn_testing_segment_slots.argtypes = [P(AttnDesc), c.c_void_p, c.c_int32, c.c_int64,
                                                    c.c_void_p]
         lib.attn_testing_segment_slots.restype = c.c_int
+        lib.attn_testing_anchor_fuses.argtypes = [P(AttnAnchorDesc), c.c_int32]
+        lib.attn_testing_anchor_fuses.restype = c.c_int32
+        lib.attn_testing_set_anchor_fusion.argtypes = [c.c_int32]
+        lib.attn_testing_set_anchor_fusion.restype = None
         _lib = lib
         return lib
 
@@ -176,6 +180,19 @@ def testing_pieces(desc: AttnDesc, lens, cu_count: int, w: int):
         if n <= cap:
             return [tuple(int(x) for x in out[4 * i:4 * i + 4]) for i in range(n)]
         cap = int(n)
+
+
+def testing_anchor_fuses(desc: "AttnAnchorDesc", cu_count: int) -> bool:
+    """Whether attn_prefill_anchor finalises rows in its local split for this shape."""
+    r = load_library().attn_testing_anchor_fuses(ctypes.byref(desc), cu_count)
+    if r < 0:
+        raise AttnError(int(-r), "attn_testing_anchor_fuses")
+    return bool(r)
+
+
+def testing_set_anchor_fusion(enabled: bool) -> None:
+    """Process-wide: False forces attn_prefill_anchor's unfused path (tests only)."""
+    load_library().attn_testing_set_anchor_fusion(1 if enabled else 0)
 
 
 def testing_segment_slots(desc: AttnDesc, lens, cu_count: int, segment: int):

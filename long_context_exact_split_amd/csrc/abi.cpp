@@ -224,7 +224,24 @@ struct AnchorPlans {
   attn_desc_t anc, loc;
   attn_plan_t ap, lp;
   size_t anc_bytes, total;
+  bool fuse;  // the local split merges each row's two records and writes O, lse
 };
+
+// True when every segment of a balanced layout is a single piece: each
+// workgroup's share then starts at a segment's first unit (its first piece
+// starts at token 0), so no workgroup boundary falls inside a segment.
+bool whole_segment_pieces(const WorkMap &m) {
+  if (m.mode != 1 || m.n_wg <= 0) return false;
+  const int64_t U = total_units(m);
+  for (int64_t w = 0; w < m.n_wg; ++w) {
+    PieceCursor c = first_piece(m, U, w);
+    Piece p;
+    if (next_piece(m, w, c, &p) && p.t0 != 0) return false;
+  }
+  return true;
+}
+
+std::atomic<int> g_anchor_fusion{1};
 
 attn_status_t anchor_plans(const attn_anchor_desc_t *d, int cu, AnchorPlans *a) {
   anchor_descs(d, &a->anc, &a->loc);
@@ -233,6 +250,14 @@ attn_status_t anchor_plans(const attn_anchor_desc_t *d, int cu, AnchorPlans *a) 
   if ((st = make_plan(&a->loc, cu, kMfma, &a->lp)) != ATTN_OK) return st;
   a->anc_bytes = (size_t)round_up((int64_t)a->ap.workspace_bytes, 256);
   a->total = a->anc_bytes + a->lp.workspace_bytes;
+  // The local split can finalise the rows itself when both parts run on the
+  // shared-tile kernel with the same row blocks and every segment of both is
+  // one piece: each row then has exactly one record of each part.
+  a->fuse = g_anchor_fusion.load(std::memory_order_relaxed) != 0 && a->ap.work_items > 0 &&
+            a->lp.work_items > 0 && a->ap.kernel == 2 && a->lp.kernel == 2 &&
+            a->ap.rows_per_block == a->lp.rows_per_block &&
+            whole_segment_pieces(work_map(&a->anc, a->ap)) &&
+            whole_segment_pieces(work_map(&a->loc, a->lp));
   return ATTN_OK;
 }
 
@@ -491,11 +516,17 @@ attn_status_t attn_prefill_anchor(const attn_anchor_desc_t *desc, const void *q,
     if (launch_split(&a.anc, a.ap, split_args(&a.anc, a.ap, q, k_anchor, v_anchor, nullptr, shared, anc),
                      SplitMode::kFull, s) != hipSuccess)
       return ATTN_ERR_HIP;
-    if (launch_split(&a.loc, a.lp,
-                     split_args(&a.loc, a.lp, q, k_blocks, v_blocks, nullptr,
-                                dense_paging(&a.loc), loc),
-                     SplitMode::kFull, s) != hipSuccess)
-      return ATTN_ERR_HIP;
+    SplitArgs la = split_args(&a.loc, a.lp, q, k_blocks, v_blocks, nullptr,
+                              dense_paging(&a.loc), loc);
+    if (a.fuse) {
+      la.fin = 1;
+      la.fin_map = work_map(&a.anc, a.ap);
+      la.fin_part = anc;
+      la.fin_o = o;
+      la.fin_lse = lse;
+    }
+    if (launch_split(&a.loc, a.lp, la, SplitMode::kFull, s) != hipSuccess) return ATTN_ERR_HIP;
+    if (a.fuse) return ATTN_OK;
     MergeArgs m{};
     m.map = work_map(&a.loc, a.lp);
     m.part = loc;
@@ -572,6 +603,24 @@ attn_status_t attn_testing_segment_slots(const attn_desc_t *desc, const int32_t 
   } catch (...) {
     return ATTN_ERR_HIP;
   }
+}
+
+int32_t attn_testing_anchor_fuses(const attn_anchor_desc_t *desc, int32_t cu_count) {
+  try {
+    attn_status_t st = validate_anchor(desc);
+    if (st != ATTN_OK) return -(int32_t)st;
+    if (cu_count < 1) return -(int32_t)ATTN_ERR_VALUE;
+    if (desc->num_blocks == 0) return 0;
+    AnchorPlans a;
+    if ((st = anchor_plans(desc, cu_count, &a)) != ATTN_OK) return -(int32_t)st;
+    return a.fuse ? 1 : 0;
+  } catch (...) {
+    return -(int32_t)ATTN_ERR_HIP;
+  }
+}
+
+void attn_testing_set_anchor_fusion(int32_t enabled) {
+  g_anchor_fusion.store(enabled ? 1 : 0, std::memory_order_relaxed);
 }
 
 const char *attn_status_string(attn_status_t status) {

@@ -31,6 +31,15 @@ struct SplitArgs {
   int32_t q_len, Hq, G, R;
   int32_t causal;
   float scale_log2;  // scale * log2(e)
+  // Finalising split (shared-tile kernel, balanced layout only): every piece
+  // of this call and of fin_map is a whole segment, fin_map has the same
+  // sequences, rows and row blocks, and its one record per row (fin_part) is
+  // merged with the piece's own before O and lse are written (fin_o,
+  // fin_lse); no record is written and no merge launch follows.
+  int32_t fin;
+  WorkMap fin_map;
+  PartialLayout fin_part;
+  float *fin_o, *fin_lse;
 };
 
 // Merge of every record of a row, then normalisation.  Output row r of

@@ -481,10 +481,102 @@ union RowsSmem {
     uint16_t k[kRowsBufs][kTile * Tiles<D>::KROW];
     uint16_t v[kRowsBufs][ENERGY ? 1 : kTile * Tiles<D>::VROW];
   } t;
-  float stage[RW][kRows * 32];  // epilogue: one 32 x 32 float slice per wave
+  struct {
+    float stage[RW][kRows * 32];  // epilogue: one 32 x 32 float slice per wave
+    float coef[RW][5][kRows];     // finalising epilogue: per-row merge factors
+  } ep;
 };
 
-template <int D, int RW, bool ENERGY, bool PAGED>
+// Finalising epilogue of a piece that is its segment's only piece, when
+// the other call of the same rows (a.fin_map) also left one record per row:
+// the two records are merged by the rule and in the order the merge kernel
+// uses (this call's record first), and O and lse are written directly.
+// m, lsum: the wave's row statistics (lane l: row l % 32); oacc: O^T.
+template <int D, int RW>
+__device__ __forceinline__ void finalize_rows(const SplitArgs &a, int b, int kvh, int rb, float m,
+                                              float lsum, const f32x16_t (&oacc)[D / 32],
+                                              RowsSmem<D, RW, false> &sh) {
+  constexpr int NT = D / 32;
+  constexpr int OP = 32;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int h = lane >> 5, j = lane & 31;
+  const WorkMap &fm = a.fin_map;
+  int64_t PB = 0;
+  for (int bb = 0; bb < b; ++bb) PB += seq_units(fm, seq_len(fm, bb));
+  const int64_t sigma = ((int64_t)b * fm.Hkv + kvh) * fm.row_blocks + rb;
+  const SlotRange sr = segment_slots_at(fm, total_units(fm), PB, b, sigma);
+  const int64_t frec0 = sr.first * a.fin_part.rows + wave * kRows;  // the wave's first row
+  const int row0 = rb * kRows * RW + wave * kRows;                  // ... in the call's rows
+  float *coef = &sh.ep.coef[wave][0][0];
+  if (h == 0) {
+    const float ma = a.fin_part.m[frec0 + j], la = a.fin_part.l[frec0 + j];
+    float M = -INFINITY, L = 0.0f;
+    const float M1 = fmaxf(M, m);
+    const float fa0 = rescale_factor(M, M1), fb0 = rescale_factor(m, M1);
+    L = L * fa0 + lsum * fb0;
+    M = M1;
+    const float M2 = fmaxf(M, ma);
+    const float fa1 = rescale_factor(M, M2), fb1 = rescale_factor(ma, M2);
+    L = L * fa1 + la * fb1;
+    M = M2;
+    const bool empty = M == -INFINITY || !(L > 0.0f);
+    coef[0 * kRows + j] = fa0;
+    coef[1 * kRows + j] = fb0;
+    coef[2 * kRows + j] = fa1;
+    coef[3 * kRows + j] = fb1;
+    coef[4 * kRows + j] = empty ? 0.0f : 1.0f / L;
+    const int r = row0 + j;
+    if (r < a.R) {
+      const int i = r / a.G;
+      const int hq = kvh * a.G + (r - i * a.G);
+      a.fin_lse[((int64_t)b * a.q_len + i) * a.Hq + hq] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // O^T tiles to rows through the wave's LDS slice, as for the records;
+  // lane l finishes rows 8q + l/8 (q = 0..3), four dims at a time.
+  float *stage = sh.ep.stage[wave];
+  const int swz_w = (j & 7) * 4;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      stage[j * OP + ((8 * (e >> 2) + 4 * h) ^ swz_w) + (e & 3)] = oacc[n][e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = q * kWave + lane;
+      const int rr = idx >> 3, c4 = (idx & 7) * 4;
+      const float4 v = *reinterpret_cast<const float4 *>(stage + rr * OP + (c4 ^ ((rr & 7) * 4)));
+      const float4 va =
+          *reinterpret_cast<const float4 *>(a.fin_part.o + (frec0 + rr) * D + 32 * n + c4);
+      const int r = row0 + rr;
+      if (r < a.R) {
+        const int i = r / a.G;
+        const int hq = kvh * a.G + (r - i * a.G);
+        const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + hq;
+        const float fa0 = coef[0 * kRows + rr], fb0 = coef[1 * kRows + rr];
+        const float fa1 = coef[2 * kRows + rr], fb1 = coef[3 * kRows + rr];
+        const float inv = coef[4 * kRows + rr];
+        float *dst = a.fin_o + orow * D + 32 * n + c4;  // O is only 4-byte aligned
+        dst[0] = ((0.0f * fa0 + v.x * fb0) * fa1 + va.x * fb1) * inv;
+        dst[1] = ((0.0f * fa0 + v.y * fb0) * fa1 + va.y * fb1) * inv;
+        dst[2] = ((0.0f * fa0 + v.z * fb0) * fa1 + va.z * fb1) * inv;
+        dst[3] = ((0.0f * fa0 + v.w * fb0) * fa1 + va.w * fb1) * inv;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+template <int D, int RW, bool ENERGY, bool PAGED, bool FIN = false>
 __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, int rb, int c0,
                                            int c1, int64_t slot, RowsSmem<D, RW, ENERGY> &sh) {
   using T = Tiles<D>;
@@ -685,6 +777,10 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   __syncthreads();  // every wave is done with the tile buffers (the epilogue reuses them)
 
   lsum += __shfl_xor(lsum, 32);
+  if constexpr (FIN) {
+    finalize_rows<D, RW>(a, b, kvh, rb, m, lsum, oacc, sh);
+    return;
+  }
   const int64_t rec0 = slot * (kRows * RW) + wave * kRows;  // this wave's first row
   if (h == 0) {
     a.part.m[rec0 + j] = m;
@@ -698,7 +794,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
     // Slice row pitch 32 floats; 4-float column groups are XOR-swizzled by
     // row (keeps float4 alignment, spreads the column writes over banks).
     constexpr int OP = 32;
-    float *stage = sh.stage[wave];
+    float *stage = sh.ep.stage[wave];
     const int swz_w = (j & 7) * 4;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -738,7 +834,8 @@ __device__ __forceinline__ int xcd_local_index(int w, int n, bool shared_tiles) 
   return x * q + min(x, r) + j;
 }
 
-template <int D, int RW, bool ENERGY, bool PAGED, bool CAUSAL_ROWS>
+// FIN: the finalising epilogue (a.fin set; full mode, dense caches only).
+template <int D, int RW, bool ENERGY, bool PAGED, bool CAUSAL_ROWS, bool FIN = false>
 __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
   __shared__ RowsSmem<D, RW, ENERGY> sh;
   WorkMap m = a.map;
@@ -751,7 +848,7 @@ __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
     const int L = (int)seq_len(m, b);
     const int c0 = c * m.chunk_len;
     if (c0 >= L) return;
-    rows_piece<D, RW, ENERGY, PAGED>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
+    rows_piece<D, RW, ENERGY, PAGED, FIN>(a, b, kvh, rb, c0, min(c0 + m.chunk_len, L), w, sh);
   } else if constexpr (CAUSAL_ROWS) {
     // The causal layout's arithmetic (closed-form sums, a binary search per
     // piece) runs on one lane, a batch of pieces at a time, into LDS; the
@@ -785,7 +882,7 @@ __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
         const int t1 = __builtin_amdgcn_readfirstlane((int)p.t1);
         const int64_t slot = ((int64_t)__builtin_amdgcn_readfirstlane((int)(p.slot >> 32)) << 32) |
                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(p.slot & 0xffffffff));
-        rows_piece<D, RW, ENERGY, PAGED>(a, b, kvh, rb, t0, t1, slot, sh);
+        rows_piece<D, RW, ENERGY, PAGED, FIN>(a, b, kvh, rb, t0, t1, slot, sh);
       }
     }
   } else {
@@ -794,12 +891,24 @@ __global__ __launch_bounds__(RW * kWave) void split_kv_mfma_rows(SplitArgs a) {
     PieceCursor cur = first_piece(m, U, wl);
     Piece p;
     while (next_piece(m, wl, cur, &p))
-      rows_piece<D, RW, ENERGY, PAGED>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
+      rows_piece<D, RW, ENERGY, PAGED, FIN>(a, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1, p.slot, sh);
   }
 }
 
 template <int D, int RW, bool ENERGY, bool PAGED>
 hipError_t launch_rows(const attn_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+  if (a.fin) {
+    if constexpr (!ENERGY && !PAGED) {
+      if (a.map.causal_rows)
+        hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, false, false, true, true>),
+                           dim3((unsigned)plan.work_items), dim3(RW * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, false, false, false, true>),
+                           dim3((unsigned)plan.work_items), dim3(RW * kWave), 0, stream, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.map.causal_rows)
     hipLaunchKernelGGL((split_kv_mfma_rows<D, RW, ENERGY, PAGED, true>),
                        dim3((unsigned)plan.work_items), dim3(RW * kWave), 0, stream, a);
