@@ -219,7 +219,9 @@ attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans
 
 // Anchor-block context encoding: the anchor part as one call over a cache
 // shared by every block (sequence stride 0), the local part as a causal call
-// over each block's own cache; both leave records for the same rows.
+// over each block's own cache; both leave records for the same rows, merged
+// by the merge kernel, or by the local call itself when every segment of
+// both parts is one piece (fuse).
 struct AnchorPlans {
   attn_desc_t anc, loc;
   attn_plan_t ap, lp;

@@ -465,10 +465,12 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
 // ---------------------------------------------------------------------------
 // Shared-tile variant for many query rows per KV head (R > 32): a workgroup of
 // RW waves owns 32*RW rows, all waves walk the same keys, and each 32-key K/V
-// tile is loaded into LDS once (cooperatively, double-buffered) and used by
-// every wave.  For a shared prefix this reads the prefix once for all samples
-// instead of once per block of 32 rows.  No cross-wave merge: each wave
-// writes the records of its own 32 rows.
+// tile is loaded into LDS once (cooperatively, six tile buffers, see the
+// pipeline below) and used by every wave.  For a shared prefix this reads
+// the prefix once for all samples instead of once per block of 32 rows.  No
+// cross-wave merge: each wave writes the records of its own 32 rows (or, in
+// the finalising form, merges them with another call's records and writes
+// O and lse).
 // ---------------------------------------------------------------------------
 // LDS tile buffers of the shared-tile kernel, and how many iterations ahead
 // of its first use a tile is stored into them (one barrier per two tiles).
@@ -633,8 +635,8 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   const int n_tiles = (hi - c0 + kTile - 1) / kTile;
 
   // Tiles in flight: a ring of NS register stages (tile t lives in stage
-  // t % NS) feeding two LDS buffers.  Stage indices are compile-time inside
-  // the unrolled inner loop, so the ring stays in registers.
+  // t % NS) feeding the LDS tile buffers.  Stage indices are compile-time
+  // inside the unrolled inner loop, so the ring stays in registers.
   constexpr int NS = RW >= 8 ? 3 : (RW >= 4 ? 2 : 1);
   constexpr int SA = kStoreAhead;
   u32x4 kr[NS][PER], vr[NS][ENERGY ? 1 : PER];
