@@ -57,6 +57,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Exported symbols: the library is built with hidden default visibility and
+ * exports exactly the functions declared with ATTN_API. */
+#if defined(__GNUC__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -77,7 +85,7 @@ typedef enum {
 typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype_t;
 
 /* One decode call.  B = batch >= 0, q_len >= 1, Hq % Hkv == 0, D in {64, 128},
- * 0 <= max_kv_len < 2^31.  kv_lens: device int32[B], or NULL for "every
+ * 0 <= max_kv_len <= 2^31 - 2^16.  kv_lens: device int32[B], or NULL for "every
  * sequence holds max_kv_len tokens".  scale: logit multiplier, normally
  * 1/sqrt(D).  chunk_len: 0 lets the partitioner choose the chunk length; a
  * positive multiple of 64 forces it. */
@@ -120,23 +128,23 @@ typedef struct {
  * the work items fill the GPU (Tree Attention's per-device local energies and
  * Star Attention's per-host context blocks, placed on CUs).  Pure host code
  * when cu_count > 0. */
-attn_status_t attn_decode_plan(const attn_desc_t *desc, int32_t cu_count, attn_plan_t *plan);
+ATTN_API attn_status_t attn_decode_plan(const attn_desc_t *desc, int32_t cu_count, attn_plan_t *plan);
 
 /* Bytes of device workspace that attn_decode, attn_decode_energy,
  * attn_decode_energy_zeta and the paged variants need for `desc` on the
  * current device (0 is possible for an empty call). */
-attn_status_t attn_workspace_bytes(const attn_desc_t *desc, size_t *bytes);
+ATTN_API attn_status_t attn_workspace_bytes(const attn_desc_t *desc, size_t *bytes);
 
 /* lse only: the energy F at zeta = 0, i.e. the logsumexp of every row, read
  * from K alone (Tree Attention article, "an energy view of attention": the
  * local energies are computed in parallel and combined by an associative
  * reduction).  lse: float32 [B][q_len][Hq]. */
-attn_status_t attn_decode_energy(const attn_desc_t *desc, const void *q, const void *k,
+ATTN_API attn_status_t attn_decode_energy(const attn_desc_t *desc, const void *q, const void *k,
                                  float *lse, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
 /* O and lse (definition above).  v has the layout of k. */
-attn_status_t attn_decode(const attn_desc_t *desc, const void *q, const void *k, const void *v,
+ATTN_API attn_status_t attn_decode(const attn_desc_t *desc, const void *q, const void *k, const void *v,
                           float *o, float *lse, void *workspace, size_t workspace_bytes,
                           void *stream);
 
@@ -164,10 +172,10 @@ attn_status_t attn_decode(const attn_desc_t *desc, const void *q, const void *k,
  * O = o / l and lse = (m + log2 l) * ln 2.  o == NULL gives lse only; o !=
  * NULL requires records produced with v != NULL.  Same desc and workspace as
  * the attn_decode_partials call that filled it; errors as above. */
-attn_status_t attn_decode_partials(const attn_desc_t *desc, const void *q, const void *k,
+ATTN_API attn_status_t attn_decode_partials(const attn_desc_t *desc, const void *q, const void *k,
                                    const void *v, void *workspace, size_t workspace_bytes,
                                    void *stream);
-attn_status_t attn_decode_merge(const attn_desc_t *desc, float *o, float *lse, void *workspace,
+ATTN_API attn_status_t attn_decode_merge(const attn_desc_t *desc, float *o, float *lse, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
 /* Energy at a given zeta (Tree Attention article, "an energy view of
@@ -178,7 +186,7 @@ attn_status_t attn_decode_merge(const attn_desc_t *desc, float *o, float *lse, v
  * this call reproduce attn_decode's O.  zeta: [B][q_len][Hq][D], element
  * type and alignment of q.  lse receives F(zeta), float32 [B][q_len][Hq].
  * Runs on the vector-ALU kernel for every row count; dense caches only. */
-attn_status_t attn_decode_energy_zeta(const attn_desc_t *desc, const void *q, const void *k,
+ATTN_API attn_status_t attn_decode_energy_zeta(const attn_desc_t *desc, const void *q, const void *k,
                                       const void *v, const void *zeta, float *lse,
                                       void *workspace, size_t workspace_bytes, void *stream);
 
@@ -217,15 +225,15 @@ typedef struct {
   int64_t token_stride;
 } attn_paged_kv_t;
 
-attn_status_t attn_decode_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+ATTN_API attn_status_t attn_decode_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
                                 const void *q, const void *k_pool, const void *v_pool, float *o,
                                 float *lse, void *workspace, size_t workspace_bytes, void *stream);
-attn_status_t attn_decode_energy_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+ATTN_API attn_status_t attn_decode_energy_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
                                        const void *q, const void *k_pool, float *lse,
                                        void *workspace, size_t workspace_bytes, void *stream);
 /* The split phase alone on a paged cache (records as attn_decode_partials;
  * attn_decode_merge then finishes the call). */
-attn_status_t attn_decode_partials_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
+ATTN_API attn_status_t attn_decode_partials_paged(const attn_desc_t *desc, const attn_paged_kv_t *paged,
                                          const void *q, const void *k_pool, const void *v_pool,
                                          void *workspace, size_t workspace_bytes, void *stream);
 
@@ -248,9 +256,9 @@ typedef struct {
   attn_dtype_t dtype;
 } attn_bifurcated_desc_t;
 
-attn_status_t attn_bifurcated_workspace_bytes(const attn_bifurcated_desc_t *desc, size_t *bytes);
+ATTN_API attn_status_t attn_bifurcated_workspace_bytes(const attn_bifurcated_desc_t *desc, size_t *bytes);
 
-attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const void *q,
+ATTN_API attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const void *q,
                                      const void *k_prefix, const void *v_prefix,
                                      const void *k_suffix, const void *v_suffix, float *o,
                                      float *lse, void *workspace, size_t workspace_bytes,
@@ -278,16 +286,16 @@ typedef struct {
   attn_dtype_t dtype;
 } attn_anchor_desc_t;
 
-attn_status_t attn_anchor_workspace_bytes(const attn_anchor_desc_t *desc, size_t *bytes);
+ATTN_API attn_status_t attn_anchor_workspace_bytes(const attn_anchor_desc_t *desc, size_t *bytes);
 
-attn_status_t attn_prefill_anchor(const attn_anchor_desc_t *desc, const void *q,
+ATTN_API attn_status_t attn_prefill_anchor(const attn_anchor_desc_t *desc, const void *q,
                                   const void *k_anchor, const void *v_anchor,
                                   const void *k_blocks, const void *v_blocks, float *o,
                                   float *lse, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
 /* Static text for a status code. */
-const char *attn_status_string(attn_status_t status);
+ATTN_API const char *attn_status_string(attn_status_t status);
 
 #ifdef __cplusplus
 }

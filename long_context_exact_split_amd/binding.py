@@ -16,6 +16,9 @@ from typing import Optional, Tuple
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libattn_decode.so"
+# Test build: the same library plus the hooks of include/attn_decode_testing.h.
+# ATTN_TESTING_LIB names another build of those hooks (the host sanitizer test).
+TESTING_LIB_NAME = "libattn_decode_testing.so"
 
 ATTN_BF16, ATTN_F32 = 0, 1
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
@@ -80,6 +83,7 @@ class AttnPagedKv(ctypes.Structure):
 
 
 _lib = None
+_testing_lib = None
 _lock = threading.Lock()
 
 
@@ -127,6 +131,21 @@ def load_library():
             getattr(lib, name).restype = c.c_int
         lib.attn_status_string.argtypes = [c.c_int]
         lib.attn_status_string.restype = c.c_char_p
+        _lib = lib
+        return lib
+
+
+def load_testing_library():
+    """Load the test build (partition and check hooks; never used by the product path)."""
+    global _testing_lib
+    with _lock:
+        if _testing_lib is not None:
+            return _testing_lib
+        path = os.environ.get("ATTN_TESTING_LIB") or os.path.join(PKG, TESTING_LIB_NAME)
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        P, c = ctypes.POINTER, ctypes
         lib.attn_testing_pieces.argtypes = [P(AttnDesc), c.c_void_p, c.c_int32, c.c_int64,
                                             c.c_void_p, c.c_int64]
         lib.attn_testing_pieces.restype = c.c_int64
@@ -135,9 +154,18 @@ def load_library():
         lib.attn_testing_segment_slots.restype = c.c_int
         lib.attn_testing_anchor_fuses.argtypes = [P(AttnAnchorDesc), c.c_int32]
         lib.attn_testing_anchor_fuses.restype = c.c_int32
-        lib.attn_testing_set_anchor_fusion.argtypes = [c.c_int32]
-        lib.attn_testing_set_anchor_fusion.restype = None
-        _lib = lib
+        lib.attn_testing_plan.argtypes = [P(AttnDesc), c.c_int32, P(AttnPlan)]
+        lib.attn_testing_plan.restype = c.c_int
+        lib.attn_testing_check_decode.argtypes = [P(AttnDesc), P(AttnPagedKv)] + [
+            c.c_void_p] * 5 + [c.c_int32, c.c_int32]
+        lib.attn_testing_check_decode.restype = c.c_int
+        lib.attn_testing_check_bifurcated.argtypes = [P(AttnBifDesc), c.c_int32, P(c.c_size_t)]
+        lib.attn_testing_check_bifurcated.restype = c.c_int
+        if hasattr(lib, "attn_testing_prefill_anchor_unfused"):  # absent in host-only builds
+            lib.attn_testing_prefill_anchor_unfused.argtypes = [P(AttnAnchorDesc)] + [
+                c.c_void_p] * 8 + [c.c_size_t, c.c_void_p]
+            lib.attn_testing_prefill_anchor_unfused.restype = c.c_int
+        _testing_lib = lib
         return lib
 
 
@@ -165,10 +193,18 @@ def plan(desc: AttnDesc, cu_count: int = 0) -> dict:
     return p.as_dict()
 
 
+def testing_plan(desc: AttnDesc, cu_count: int) -> dict:
+    """The plan through the test build's host-only hook (same arithmetic as plan())."""
+    p = AttnPlan()
+    _check(load_testing_library().attn_testing_plan(ctypes.byref(desc), cu_count, ctypes.byref(p)),
+           "attn_testing_plan")
+    return p.as_dict()
+
+
 def testing_pieces(desc: AttnDesc, lens, cu_count: int, w: int):
     """Host view of workgroup w's pieces: [(segment, t0, t1, slot), ...]."""
     import numpy as np
-    lib = load_library()
+    lib = load_testing_library()
     arr = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32)
     cap = 64
     while True:
@@ -184,20 +220,15 @@ def testing_pieces(desc: AttnDesc, lens, cu_count: int, w: int):
 
 def testing_anchor_fuses(desc: "AttnAnchorDesc", cu_count: int) -> bool:
     """Whether attn_prefill_anchor finalises rows in its local split for this shape."""
-    r = load_library().attn_testing_anchor_fuses(ctypes.byref(desc), cu_count)
+    r = load_testing_library().attn_testing_anchor_fuses(ctypes.byref(desc), cu_count)
     if r < 0:
         raise AttnError(int(-r), "attn_testing_anchor_fuses")
     return bool(r)
 
 
-def testing_set_anchor_fusion(enabled: bool) -> None:
-    """Process-wide: False forces attn_prefill_anchor's unfused path (tests only)."""
-    load_library().attn_testing_set_anchor_fusion(1 if enabled else 0)
-
-
 def testing_segment_slots(desc: AttnDesc, lens, cu_count: int, segment: int):
     import numpy as np
-    lib = load_library()
+    lib = load_testing_library()
     arr = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32)
     out = np.zeros(3, dtype=np.int64)
     _check(lib.attn_testing_segment_slots(ctypes.byref(desc), None if arr is None else arr.ctypes.data,
@@ -243,10 +274,25 @@ def _workspace(nbytes: int, device, workspace):
     if nbytes == 0:
         return None
     if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {device}")
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return workspace
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _output(t, shape, device, name):
+    """A caller-supplied output (float32, contiguous, on `device`, of `shape`)
+    or a new one.  Checked here because the library sees only a pointer."""
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if t.dtype != torch.float32 or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    return t
 
 
 def _decode_desc(q, k, kv_lens, scale, causal, chunk_len) -> AttnDesc:
@@ -291,10 +337,8 @@ def decode(q, k, v, kv_lens=None, *, scale: Optional[float] = None, causal: bool
     desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
     B, q_len, Hq, D = q.shape
     with torch.cuda.device(q.device):
-        if out is None:
-            out = torch.empty((B, q_len, Hq, D), dtype=torch.float32, device=q.device)
-        if lse is None:
-            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        out = _output(out, (B, q_len, Hq, D), q.device, "out")
+        lse = _output(lse, (B, q_len, Hq), q.device, "lse")
         ws = _workspace(workspace_bytes(desc), q.device, workspace)
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(lib.attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
@@ -355,8 +399,7 @@ def decode_energy(q, k, kv_lens=None, *, scale: Optional[float] = None, causal: 
     desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
     B, q_len, Hq, D = q.shape
     with torch.cuda.device(q.device):
-        if lse is None:
-            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        lse = _output(lse, (B, q_len, Hq), q.device, "lse")
         ws = _workspace(workspace_bytes(desc), q.device, workspace)
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(lib.attn_decode_energy(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(ws),
@@ -376,8 +419,7 @@ def decode_energy_zeta(q, k, v, zeta, kv_lens=None, *, scale: Optional[float] = 
     desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
     B, q_len, Hq, D = q.shape
     with torch.cuda.device(q.device):
-        if lse is None:
-            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        lse = _output(lse, (B, q_len, Hq), q.device, "lse")
         ws = _workspace(workspace_bytes(desc), q.device, workspace)
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(lib.attn_decode_energy_zeta(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
@@ -444,10 +486,8 @@ def decode_paged(q, paged: PagedCache, kv_lens=None, *, scale: Optional[float] =
     desc = _paged_desc(q, paged, kv_lens, scale, causal, chunk_len)
     B, q_len, Hq, D = q.shape
     with torch.cuda.device(q.device):
-        if out is None:
-            out = torch.empty((B, q_len, Hq, D), dtype=torch.float32, device=q.device)
-        if lse is None:
-            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        out = _output(out, (B, q_len, Hq, D), q.device, "out")
+        lse = _output(lse, (B, q_len, Hq), q.device, "lse")
         ws = _workspace(workspace_bytes(desc), q.device, workspace)
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(lib.attn_decode_paged(ctypes.byref(desc), ctypes.byref(paged.kv), _ptr(q),
@@ -465,8 +505,7 @@ def decode_energy_paged(q, paged: PagedCache, kv_lens=None, *, scale: Optional[f
     desc = _paged_desc(q, paged, kv_lens, scale, causal, chunk_len)
     B, q_len, Hq, D = q.shape
     with torch.cuda.device(q.device):
-        if lse is None:
-            lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+        lse = _output(lse, (B, q_len, Hq), q.device, "lse")
         ws = _workspace(workspace_bytes(desc), q.device, workspace)
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(lib.attn_decode_energy_paged(ctypes.byref(desc), ctypes.byref(paged.kv), _ptr(q),
@@ -499,10 +538,8 @@ def decode_bifurcated(q, k_prefix, v_prefix, k_suffix, v_suffix, *, scale: Optio
     desc = bifurcated_desc(q, k_prefix, k_suffix, scale)
     S, Hq, D = q.shape
     with torch.cuda.device(q.device):
-        if out is None:
-            out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
-        if lse is None:
-            lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+        out = _output(out, (S, Hq, D), q.device, "out")
+        lse = _output(lse, (S, Hq), q.device, "lse")
         n = ctypes.c_size_t(0)
         _check(lib.attn_bifurcated_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
                "attn_bifurcated_workspace_bytes")
@@ -576,10 +613,8 @@ def prefill_anchor(q, k_anchor, v_anchor, k_blocks, v_blocks, *, scale: Optional
     desc = anchor_desc(q, k_anchor, k_blocks, scale)
     N, Lb, Hq, D = q.shape
     with torch.cuda.device(q.device):
-        if out is None:
-            out = torch.empty((N, Lb, Hq, D), dtype=torch.float32, device=q.device)
-        if lse is None:
-            lse = torch.empty((N, Lb, Hq), dtype=torch.float32, device=q.device)
+        out = _output(out, (N, Lb, Hq, D), q.device, "out")
+        lse = _output(lse, (N, Lb, Hq), q.device, "lse")
         n = ctypes.c_size_t(0)
         _check(lib.attn_anchor_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
                "attn_anchor_workspace_bytes")
@@ -589,4 +624,27 @@ def prefill_anchor(q, k_anchor, v_anchor, k_blocks, v_blocks, *, scale: Optional
                                        _ptr(k_blocks), _ptr(v_blocks), _ptr(out), _ptr(lse),
                                        _ptr(ws), nbytes, _stream_ptr(q.device)),
                "attn_prefill_anchor")
+    return out, lse
+
+
+def testing_prefill_anchor_unfused(q, k_anchor, v_anchor, k_blocks, v_blocks, *,
+                                   scale: Optional[float] = None):
+    """prefill_anchor forced onto its three-launch path (test build only)."""
+    torch = _torch()
+    lib = load_testing_library()
+    _check_tensors(q, k_anchor, v_anchor, k_blocks, v_blocks)
+    desc = anchor_desc(q, k_anchor, k_blocks, scale)
+    N, Lb, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        out = _output(None, (N, Lb, Hq, D), q.device, "out")
+        lse = _output(None, (N, Lb, Hq), q.device, "lse")
+        n = ctypes.c_size_t(0)
+        _check(load_library().attn_anchor_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+               "attn_anchor_workspace_bytes")
+        ws = _workspace(n.value, q.device, None)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib.attn_testing_prefill_anchor_unfused(
+            ctypes.byref(desc), _ptr(q), _ptr(k_anchor), _ptr(v_anchor), _ptr(k_blocks),
+            _ptr(v_blocks), _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream_ptr(q.device)),
+            "attn_testing_prefill_anchor_unfused")
     return out, lse

@@ -1,7 +1,10 @@
 """Build ``libattn_decode.so`` for gfx950 with hipcc (in-tree).
 
 Every HIP/C++ source under ``csrc/`` is compiled to an object in ``_build/``
-(in parallel), then linked into the shared library next to this file.
+(in parallel), then linked into the shared library next to this file.  The
+test build ``libattn_decode_testing.so`` links the same objects plus the
+test-only hooks under ``csrc/testing/``; the product library holds none of
+them.  Symbols are hidden unless the public headers mark them ATTN_API.
 """
 from __future__ import annotations
 
@@ -17,11 +20,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libattn_decode.so"
+TESTING_LIB_NAME = "libattn_decode_testing.so"
 PROBE_NAME = "libhbm_probe.so"  # HBM read-stream / copy reference kernels
 ARCH = "gfx950"
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
-          "-I", INCLUDE, "-I", CSRC]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
+          "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 # Packed fp32 VALU ops are kept out of the generated code.
 HIP_ONLY = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Optional kernel tuning parameters (e.g. "-DATTN_SPLIT_KT_SMALL=16"); the
@@ -53,6 +57,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+def testing_sources():
+    return sorted(glob.glob(os.path.join(CSRC, "testing", "*.cpp")))
+
+
 def _link(objs, name, verbose, out_dir=PKG):
     out = os.path.join(out_dir, name)
     tmp = out + ".tmp"
@@ -72,11 +80,14 @@ def build(verbose: bool = False, out_dir: str = PKG, build_dir: str = BUILD) -> 
     BUILD = build_dir
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
+    tsrcs = testing_sources()
     probe = os.path.join(CSRC, "probe", "hbm_probe.hip")
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + [probe]))
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + tsrcs + [probe]))
+    lib_objs, test_objs = objs[:len(srcs)], objs[len(srcs):len(srcs) + len(tsrcs)]
     _link(objs[-1:], PROBE_NAME, verbose, out_dir)
-    return _link(objs[:-1], LIB_NAME, verbose, out_dir)
+    _link(lib_objs + test_objs, TESTING_LIB_NAME, verbose, out_dir)
+    return _link(lib_objs, LIB_NAME, verbose, out_dir)
 
 
 if __name__ == "__main__":

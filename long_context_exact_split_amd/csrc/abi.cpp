@@ -7,7 +7,7 @@
 #include <cstdint>
 
 #include "attn_decode.h"
-#include "attn_decode_testing.h"
+#include "abi_internal.h"
 #include "kernels.h"
 #include "plan.h"
 
@@ -38,8 +38,6 @@ attn_status_t device_cu_count(int *cu) {
   *cu = c;
   return ATTN_OK;
 }
-
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -116,29 +114,8 @@ attn_status_t prepare(const attn_desc_t *d, bool mfma, void *ws, size_t ws_bytes
   int cu = 0;
   if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
   if ((st = make_plan(d, cu, mfma, p)) != ATTN_OK) return st;
-  if (p->workspace_bytes > 0 && !ws) return ATTN_ERR_NULL;
-  if (ws_bytes < p->workspace_bytes) return ATTN_ERR_WORKSPACE;
-  if (!aligned(ws, 16)) return ATTN_ERR_ALIGN;
+  if ((st = check_workspace(p->workspace_bytes, ws, ws_bytes)) != ATTN_OK) return st;
   *part = carve(static_cast<char *>(ws), *p, d->head_dim);
-  return ATTN_OK;
-}
-
-attn_status_t check_inputs(const attn_desc_t *d, const void *q, const void *k, const void *v,
-                           bool need_v) {
-  attn_status_t st = validate_desc(d);
-  if (st != ATTN_OK) return st;
-  // An empty call may pass null tensors (torch gives empty tensors a null base).
-  const bool any_q = d->batch > 0, any_kv = any_q && d->max_kv_len > 0;
-  if ((any_q && !q) || (any_kv && (!k || (need_v && !v)))) return ATTN_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(k, 16) || (v && !aligned(v, 16))) return ATTN_ERR_ALIGN;
-  return ATTN_OK;
-}
-
-attn_status_t check_outputs(const attn_desc_t *d, const float *o, const float *lse, bool need_o) {
-  attn_status_t st = validate_desc(d);
-  if (st != ATTN_OK) return st;
-  if (!lse || (need_o && !o)) return ATTN_ERR_NULL;
-  if (!aligned(lse, 4) || (o && !aligned(o, 4))) return ATTN_ERR_ALIGN;
   return ATTN_OK;
 }
 
@@ -199,68 +176,6 @@ attn_status_t decode_impl(const attn_desc_t *d, const attn_paged_kv_t *paged, co
                           zeta, mode, ws, ws_bytes, stream)) != ATTN_OK)
     return st;
   return merge_impl(d, mfma_for(mode), need_o ? o : nullptr, lse, ws, ws_bytes, stream);
-}
-
-struct BifPlans {
-  attn_desc_t pre, suf;
-  attn_plan_t pp, sp;
-  size_t pre_bytes, total;
-};
-
-attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans *b) {
-  bifurcated_descs(d, &b->pre, &b->suf);
-  attn_status_t st;
-  if ((st = make_plan(&b->pre, cu, kMfma, &b->pp)) != ATTN_OK) return st;
-  if ((st = make_plan(&b->suf, cu, kMfma, &b->sp)) != ATTN_OK) return st;
-  b->pre_bytes = (size_t)round_up((int64_t)b->pp.workspace_bytes, 256);
-  b->total = b->pre_bytes + b->sp.workspace_bytes;
-  return ATTN_OK;
-}
-
-// Anchor-block context encoding: the anchor part as one call over a cache
-// shared by every block (sequence stride 0), the local part as a causal call
-// over each block's own cache; both leave records for the same rows, merged
-// by the merge kernel, or by the local call itself when every segment of
-// both parts is one piece (fuse).
-struct AnchorPlans {
-  attn_desc_t anc, loc;
-  attn_plan_t ap, lp;
-  size_t anc_bytes, total;
-  bool fuse;  // the local split merges each row's two records and writes O, lse
-};
-
-// True when every segment of a balanced layout is a single piece: each
-// workgroup's share then starts at a segment's first unit (its first piece
-// starts at token 0), so no workgroup boundary falls inside a segment.
-bool whole_segment_pieces(const WorkMap &m) {
-  if (m.mode != 1 || m.n_wg <= 0) return false;
-  const int64_t U = total_units(m);
-  for (int64_t w = 0; w < m.n_wg; ++w) {
-    PieceCursor c = first_piece(m, U, w);
-    Piece p;
-    if (next_piece(m, w, c, &p) && p.t0 != 0) return false;
-  }
-  return true;
-}
-
-std::atomic<int> g_anchor_fusion{1};
-
-attn_status_t anchor_plans(const attn_anchor_desc_t *d, int cu, AnchorPlans *a) {
-  anchor_descs(d, &a->anc, &a->loc);
-  attn_status_t st;
-  if ((st = make_plan(&a->anc, cu, kMfma, &a->ap)) != ATTN_OK) return st;
-  if ((st = make_plan(&a->loc, cu, kMfma, &a->lp)) != ATTN_OK) return st;
-  a->anc_bytes = (size_t)round_up((int64_t)a->ap.workspace_bytes, 256);
-  a->total = a->anc_bytes + a->lp.workspace_bytes;
-  // The local split can finalise the rows itself when both parts run on the
-  // shared-tile kernel with the same row blocks and every segment of both is
-  // one piece: each row then has exactly one record of each part.
-  a->fuse = g_anchor_fusion.load(std::memory_order_relaxed) != 0 && a->ap.work_items > 0 &&
-            a->lp.work_items > 0 && a->ap.kernel == 2 && a->lp.kernel == 2 &&
-            a->ap.rows_per_block == a->lp.rows_per_block &&
-            whole_segment_pieces(work_map(&a->anc, a->ap)) &&
-            whole_segment_pieces(work_map(&a->loc, a->lp));
-  return ATTN_OK;
 }
 
 }  // namespace
@@ -430,9 +345,7 @@ attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const v
     if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
     BifPlans b;
     if ((st = bifurcated_plans(desc, cu, &b)) != ATTN_OK) return st;
-    if (b.total > 0 && !workspace) return ATTN_ERR_NULL;
-    if (workspace_bytes < b.total) return ATTN_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+    if ((st = check_workspace(b.total, workspace, workspace_bytes)) != ATTN_OK) return st;
     char *ws = static_cast<char *>(workspace);
     const PartialLayout pre = carve(ws, b.pp, desc->head_dim);
     const PartialLayout suf = carve(ws + b.pre_bytes, b.sp, desc->head_dim);
@@ -477,7 +390,7 @@ attn_status_t attn_anchor_workspace_bytes(const attn_anchor_desc_t *desc, size_t
     int cu = 0;
     if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
     AnchorPlans a;
-    if ((st = anchor_plans(desc, cu, &a)) != ATTN_OK) return st;
+    if ((st = anchor_plans(desc, cu, true, &a)) != ATTN_OK) return st;
     *bytes = a.total;
     return ATTN_OK;
   } catch (...) {
@@ -491,138 +404,11 @@ attn_status_t attn_prefill_anchor(const attn_anchor_desc_t *desc, const void *q,
                                   float *lse, void *workspace, size_t workspace_bytes,
                                   void *stream) {
   try {
-    attn_status_t st = validate_anchor(desc);
-    if (st != ATTN_OK) return st;
-    const bool any = desc->num_blocks > 0;
-    if (any && (!q || !k_blocks || !v_blocks || !o || !lse ||
-                (desc->anchor_len > 0 && (!k_anchor || !v_anchor))))
-      return ATTN_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k_anchor, 16) || !aligned(v_anchor, 16) ||
-        !aligned(k_blocks, 16) || !aligned(v_blocks, 16) || !aligned(o, 4) || !aligned(lse, 4))
-      return ATTN_ERR_ALIGN;
-    if (!any) return ATTN_OK;
-    int cu = 0;
-    if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
-    AnchorPlans a;
-    if ((st = anchor_plans(desc, cu, &a)) != ATTN_OK) return st;
-    if (a.total > 0 && !workspace) return ATTN_ERR_NULL;
-    if (workspace_bytes < a.total) return ATTN_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
-    char *ws = static_cast<char *>(workspace);
-    const PartialLayout anc = carve(ws, a.ap, desc->head_dim);
-    const PartialLayout loc = carve(ws + a.anc_bytes, a.lp, desc->head_dim);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    KvPaging shared = dense_paging(&a.anc);
-    shared.seq_stride = 0;  // every block reads the one anchor
-    (void)hipGetLastError();
-    if (launch_split(&a.anc, a.ap, split_args(&a.anc, a.ap, q, k_anchor, v_anchor, nullptr, shared, anc),
-                     SplitMode::kFull, s) != hipSuccess)
-      return ATTN_ERR_HIP;
-    SplitArgs la = split_args(&a.loc, a.lp, q, k_blocks, v_blocks, nullptr,
-                              dense_paging(&a.loc), loc);
-    if (a.fuse) {
-      la.fin = 1;
-      la.fin_map = work_map(&a.anc, a.ap);
-      la.fin_part = anc;
-      la.fin_o = o;
-      la.fin_lse = lse;
-    }
-    if (launch_split(&a.loc, a.lp, la, SplitMode::kFull, s) != hipSuccess) return ATTN_ERR_HIP;
-    if (a.fuse) return ATTN_OK;
-    MergeArgs m{};
-    m.map = work_map(&a.loc, a.lp);
-    m.part = loc;
-    m.has_shared = a.ap.work_items > 0;
-    m.shared_same_rows = 1;
-    m.smap = work_map(&a.anc, a.ap);
-    m.shared = anc;
-    m.q_len = desc->block_len;
-    m.Hq = desc->num_q_heads;
-    m.G = desc->num_q_heads / desc->num_kv_heads;
-    m.R = a.lp.rows;
-    m.o = o;
-    m.lse = lse;
-    if (launch_merge(m, desc->head_dim, s) != hipSuccess) return ATTN_ERR_HIP;
-    return ATTN_OK;
+    return prefill_anchor_impl(desc, q, k_anchor, v_anchor, k_blocks, v_blocks, o, lse,
+                               workspace, workspace_bytes, stream, true);
   } catch (...) {
     return ATTN_ERR_HIP;
   }
-}
-
-int64_t attn_testing_pieces(const attn_desc_t *desc, const int32_t *host_lens, int32_t cu_count,
-                            int64_t w, int64_t *out, int64_t max_pieces) {
-  try {
-    attn_plan_t p;
-    attn_status_t st = make_plan(desc, cu_count, kMfma, &p);
-    if (st != ATTN_OK) return -(int64_t)st;
-    if (w < 0 || w >= p.work_items || (!out && max_pieces > 0)) return -(int64_t)ATTN_ERR_VALUE;
-    attn_desc_t d = *desc;
-    d.kv_lens = host_lens;
-    const WorkMap m = work_map(&d, p);
-    int64_t n = 0;
-    auto emit = [&](int64_t sigma, int64_t t0, int64_t t1, int64_t slot) {
-      if (n < max_pieces) {
-        out[4 * n] = sigma;
-        out[4 * n + 1] = t0;
-        out[4 * n + 2] = t1;
-        out[4 * n + 3] = slot;
-      }
-      ++n;
-    };
-    if (m.mode == 0) {
-      const int64_t sigma = w / m.n_chunks, c = w % m.n_chunks;
-      const int b = (int)(sigma / segs_per_seq(m));
-      const int64_t L = seq_len(m, b), c0 = c * m.chunk_len;
-      if (c0 < L) emit(sigma, c0, c0 + m.chunk_len < L ? c0 + m.chunk_len : L, w);
-    } else {
-      const int64_t U = total_units(m);
-      PieceCursor cur = first_piece(m, U, w);
-      Piece pc;
-      while (next_piece(m, w, cur, &pc)) emit(pc.sigma, pc.t0, pc.t1, pc.slot);
-    }
-    return n;
-  } catch (...) {
-    return -(int64_t)ATTN_ERR_HIP;
-  }
-}
-
-attn_status_t attn_testing_segment_slots(const attn_desc_t *desc, const int32_t *host_lens,
-                                         int32_t cu_count, int64_t segment, int64_t out[3]) {
-  try {
-    attn_plan_t p;
-    attn_status_t st = make_plan(desc, cu_count, kMfma, &p);
-    if (st != ATTN_OK) return st;
-    if (!out) return ATTN_ERR_NULL;
-    attn_desc_t d = *desc;
-    d.kv_lens = host_lens;
-    const WorkMap m = work_map(&d, p);
-    if (segment < 0 || segment >= (int64_t)m.B * segs_per_seq(m)) return ATTN_ERR_VALUE;
-    const SlotRange r = segment_slots(m, total_units(m), (int)(segment / segs_per_seq(m)), segment);
-    out[0] = r.first;
-    out[1] = r.stride;
-    out[2] = r.count;
-    return ATTN_OK;
-  } catch (...) {
-    return ATTN_ERR_HIP;
-  }
-}
-
-int32_t attn_testing_anchor_fuses(const attn_anchor_desc_t *desc, int32_t cu_count) {
-  try {
-    attn_status_t st = validate_anchor(desc);
-    if (st != ATTN_OK) return -(int32_t)st;
-    if (cu_count < 1) return -(int32_t)ATTN_ERR_VALUE;
-    if (desc->num_blocks == 0) return 0;
-    AnchorPlans a;
-    if ((st = anchor_plans(desc, cu_count, &a)) != ATTN_OK) return -(int32_t)st;
-    return a.fuse ? 1 : 0;
-  } catch (...) {
-    return -(int32_t)ATTN_ERR_HIP;
-  }
-}
-
-void attn_testing_set_anchor_fusion(int32_t enabled) {
-  g_anchor_fusion.store(enabled ? 1 : 0, std::memory_order_relaxed);
 }
 
 const char *attn_status_string(attn_status_t status) {
@@ -643,3 +429,70 @@ const char *attn_status_string(attn_status_t status) {
 }
 
 }  // extern "C"
+
+namespace attn {
+
+// Anchor-block context encoding: the anchor part as one call over a cache
+// shared by every block (sequence stride 0), the local part as a causal call
+// over each block's own cache; both leave records for the same rows, merged
+// by the merge kernel, or by the local call itself when every segment of
+// both parts is one piece (fusion).
+attn_status_t prefill_anchor_impl(const attn_anchor_desc_t *desc, const void *q,
+                                  const void *k_anchor, const void *v_anchor,
+                                  const void *k_blocks, const void *v_blocks, float *o,
+                                  float *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream, bool allow_fusion) {
+  attn_status_t st = validate_anchor(desc);
+  if (st != ATTN_OK) return st;
+  const bool any = desc->num_blocks > 0;
+  if (any && (!q || !k_blocks || !v_blocks || !o || !lse ||
+              (desc->anchor_len > 0 && (!k_anchor || !v_anchor))))
+    return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_anchor, 16) || !aligned(v_anchor, 16) ||
+      !aligned(k_blocks, 16) || !aligned(v_blocks, 16) || !aligned(o, 4) || !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
+  if (!any) return ATTN_OK;
+  int cu = 0;
+  if ((st = device_cu_count(&cu)) != ATTN_OK) return st;
+  AnchorPlans a;
+  if ((st = anchor_plans(desc, cu, allow_fusion, &a)) != ATTN_OK) return st;
+  if ((st = check_workspace(a.total, workspace, workspace_bytes)) != ATTN_OK) return st;
+  char *ws = static_cast<char *>(workspace);
+  const PartialLayout anc = carve(ws, a.ap, desc->head_dim);
+  const PartialLayout loc = carve(ws + a.anc_bytes, a.lp, desc->head_dim);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KvPaging shared = dense_paging(&a.anc);
+  shared.seq_stride = 0;  // every block reads the one anchor
+  (void)hipGetLastError();
+  if (launch_split(&a.anc, a.ap, split_args(&a.anc, a.ap, q, k_anchor, v_anchor, nullptr, shared, anc),
+                   SplitMode::kFull, s) != hipSuccess)
+    return ATTN_ERR_HIP;
+  SplitArgs la = split_args(&a.loc, a.lp, q, k_blocks, v_blocks, nullptr, dense_paging(&a.loc),
+                            loc);
+  if (a.fuse) {
+    la.fin = 1;
+    la.fin_map = work_map(&a.anc, a.ap);
+    la.fin_part = anc;
+    la.fin_o = o;
+    la.fin_lse = lse;
+  }
+  if (launch_split(&a.loc, a.lp, la, SplitMode::kFull, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (a.fuse) return ATTN_OK;
+  MergeArgs m{};
+  m.map = work_map(&a.loc, a.lp);
+  m.part = loc;
+  m.has_shared = a.ap.work_items > 0;
+  m.shared_same_rows = 1;
+  m.smap = work_map(&a.anc, a.ap);
+  m.shared = anc;
+  m.q_len = desc->block_len;
+  m.Hq = desc->num_q_heads;
+  m.G = desc->num_q_heads / desc->num_kv_heads;
+  m.R = a.lp.rows;
+  m.o = o;
+  m.lse = lse;
+  if (launch_merge(m, desc->head_dim, s) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+}  // namespace attn

@@ -10,12 +10,23 @@
 #include "plan.h"
 
 #include <cmath>
+#include <cstring>
 #include <limits>
 
 namespace attn {
 namespace {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// The element type as the integer a C caller stored.  A C enum object may
+// hold any int, but loading a value outside the enumerators through the C++
+// enum type is undefined, so the field is read as its bytes.
+int dtype_code(const attn_dtype_t &t) {
+  int v;
+  static_assert(sizeof(v) == sizeof(t), "attn_dtype_t is an int");
+  std::memcpy(&v, &t, sizeof v);
+  return v;
+}
 
 }  // namespace
 
@@ -29,10 +40,11 @@ int items_per_cu(int kernel, int64_t units, int cu_count) {
 
 attn_status_t validate_desc(const attn_desc_t *d) {
   if (!d) return ATTN_ERR_NULL;
-  if (d->dtype != ATTN_BF16 && d->dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  const int dt = dtype_code(d->dtype);
+  if (dt != ATTN_BF16 && dt != ATTN_F32) return ATTN_ERR_DTYPE;
   if (d->batch < 0 || d->q_len < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
-      d->num_q_heads % d->num_kv_heads != 0 || d->max_kv_len < 0 ||
-      d->max_kv_len > std::numeric_limits<int32_t>::max() || d->head_dim < 1)
+      d->num_q_heads % d->num_kv_heads != 0 || d->max_kv_len < 0 || d->max_kv_len > kMaxKvLen ||
+      d->head_dim < 1)
     return ATTN_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(d->scale)) return ATTN_ERR_VALUE;
@@ -173,11 +185,11 @@ size_t partial_bytes(int64_t records, int head_dim) {
 
 attn_status_t validate_bifurcated(const attn_bifurcated_desc_t *d) {
   if (!d) return ATTN_ERR_NULL;
-  if (d->dtype != ATTN_BF16) return d->dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_DTYPE;
+  const int dt = dtype_code(d->dtype);
+  if (dt != ATTN_BF16) return dt == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_DTYPE;
   if (d->num_samples < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
       d->num_q_heads % d->num_kv_heads != 0 || d->prefix_len < 0 || d->suffix_len < 0 ||
-      d->prefix_len > std::numeric_limits<int32_t>::max() ||
-      d->suffix_len > std::numeric_limits<int32_t>::max() || d->head_dim < 1)
+      d->prefix_len > kMaxKvLen || d->suffix_len > kMaxKvLen || d->head_dim < 1)
     return ATTN_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(d->scale)) return ATTN_ERR_VALUE;
@@ -212,10 +224,11 @@ namespace attn {
 
 attn_status_t validate_anchor(const attn_anchor_desc_t *d) {
   if (!d) return ATTN_ERR_NULL;
-  if (d->dtype != ATTN_BF16) return d->dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_DTYPE;
+  const int dt = dtype_code(d->dtype);
+  if (dt != ATTN_BF16) return dt == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_DTYPE;
   if (d->num_blocks < 0 || d->block_len < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
-      d->num_q_heads % d->num_kv_heads != 0 || d->anchor_len < 0 ||
-      d->anchor_len > std::numeric_limits<int32_t>::max() || d->head_dim < 1)
+      d->num_q_heads % d->num_kv_heads != 0 || d->anchor_len < 0 || d->anchor_len > kMaxKvLen ||
+      d->head_dim < 1)
     return ATTN_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(d->scale)) return ATTN_ERR_VALUE;
@@ -241,6 +254,78 @@ void anchor_descs(const attn_anchor_desc_t *d, attn_desc_t *anchor, attn_desc_t 
   *local = c;
   local->causal = 1;                // query i sees the block's keys t <= i
   local->max_kv_len = d->block_len;
+}
+
+}  // namespace attn
+
+namespace attn {
+
+constexpr bool kMfmaPlans = true;  // dense query blocks go to the matrix-core kernels
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+attn_status_t check_inputs(const attn_desc_t *d, const void *q, const void *k, const void *v,
+                           bool need_v) {
+  attn_status_t st = validate_desc(d);
+  if (st != ATTN_OK) return st;
+  // An empty call may pass null tensors (torch gives empty tensors a null base).
+  const bool any_q = d->batch > 0, any_kv = any_q && d->max_kv_len > 0;
+  if ((any_q && !q) || (any_kv && (!k || (need_v && !v)))) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || (v && !aligned(v, 16))) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+attn_status_t check_outputs(const attn_desc_t *d, const float *o, const float *lse, bool need_o) {
+  attn_status_t st = validate_desc(d);
+  if (st != ATTN_OK) return st;
+  if (!lse || (need_o && !o)) return ATTN_ERR_NULL;
+  if (!aligned(lse, 4) || (o && !aligned(o, 4))) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+attn_status_t check_workspace(size_t need, const void *ws, size_t ws_bytes) {
+  if (need > 0 && !ws) return ATTN_ERR_NULL;
+  if (ws_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans *b) {
+  bifurcated_descs(d, &b->pre, &b->suf);
+  attn_status_t st;
+  if ((st = make_plan(&b->pre, cu, kMfmaPlans, &b->pp)) != ATTN_OK) return st;
+  if ((st = make_plan(&b->suf, cu, kMfmaPlans, &b->sp)) != ATTN_OK) return st;
+  b->pre_bytes = (size_t)round_up((int64_t)b->pp.workspace_bytes, 256);
+  b->total = b->pre_bytes + b->sp.workspace_bytes;
+  return ATTN_OK;
+}
+
+// Each workgroup's share then starts at a segment's first unit (its first
+// piece starts at token 0), so no workgroup boundary falls inside a segment.
+bool whole_segment_pieces(const WorkMap &m) {
+  if (m.mode != 1 || m.n_wg <= 0) return false;
+  const int64_t U = total_units(m);
+  for (int64_t w = 0; w < m.n_wg; ++w) {
+    PieceCursor c = first_piece(m, U, w);
+    Piece p;
+    if (next_piece(m, w, c, &p) && p.t0 != 0) return false;
+  }
+  return true;
+}
+
+attn_status_t anchor_plans(const attn_anchor_desc_t *d, int cu, bool allow_fusion,
+                           AnchorPlans *a) {
+  anchor_descs(d, &a->anc, &a->loc);
+  attn_status_t st;
+  if ((st = make_plan(&a->anc, cu, kMfmaPlans, &a->ap)) != ATTN_OK) return st;
+  if ((st = make_plan(&a->loc, cu, kMfmaPlans, &a->lp)) != ATTN_OK) return st;
+  a->anc_bytes = (size_t)round_up((int64_t)a->ap.workspace_bytes, 256);
+  a->total = a->anc_bytes + a->lp.workspace_bytes;
+  a->fuse = allow_fusion && a->ap.work_items > 0 && a->lp.work_items > 0 && a->ap.kernel == 2 &&
+            a->lp.kernel == 2 && a->ap.rows_per_block == a->lp.rows_per_block &&
+            whole_segment_pieces(work_map(&a->anc, a->ap)) &&
+            whole_segment_pieces(work_map(&a->loc, a->lp));
+  return ATTN_OK;
 }
 
 }  // namespace attn

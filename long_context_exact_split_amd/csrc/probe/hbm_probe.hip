@@ -47,7 +47,7 @@ extern "C" {
 
 // Reads `bytes` (a multiple of 16) from src; sink holds >= blocks words.
 // nontemporal != 0 marks the loads as streaming (not kept in the caches).
-int hbm_read_probe(const void *src, size_t bytes, void *sink, int blocks, int nontemporal,
+__attribute__((visibility("default"))) int hbm_read_probe(const void *src, size_t bytes, void *sink, int blocks, int nontemporal,
                    void *stream) {
   if (!src || !sink || bytes % 16 || blocks < 1) return 1;
   if (nontemporal)
@@ -60,7 +60,7 @@ int hbm_read_probe(const void *src, size_t bytes, void *sink, int blocks, int no
 }
 
 // Copies `bytes` (a multiple of 16) from src to dst.
-int hbm_copy_probe(void *dst, const void *src, size_t bytes, int blocks, void *stream) {
+__attribute__((visibility("default"))) int hbm_copy_probe(void *dst, const void *src, size_t bytes, int blocks, void *stream) {
   if (!src || !dst || bytes % 16 || blocks < 1) return 1;
   hipLaunchKernelGGL(copy_stream, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
                      (uint4 *)dst, (const uint4 *)src, bytes / 16);

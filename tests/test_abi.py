@@ -1,7 +1,8 @@
 """C-ABI boundary on the CPU: symbols, struct layout, validation errors.
 
-Every call here fails validation (or is a pure-host plan query), so no HIP
-runtime call is made and no GPU is needed."""
+Every call here fails validation, or is a pure-host plan query, or (valid
+descriptors) is given a 1-byte workspace: no kernel is ever launched, even
+where a GPU is visible, and none is needed."""
 import ctypes
 import os
 import re
@@ -45,14 +46,29 @@ def test_header_declares_the_boundary():
     assert set(names) == set(binding.EXPORTS)
 
 
-def test_library_exports_every_declared_symbol(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
-                         capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (attn_[a-z_]+)\b", out))
-    assert "attn_testing_pieces" in all_declared_functions()
-    for name in all_declared_functions():
+def exported_functions(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return set(re.findall(r"\bT (\S+)$", out, flags=re.M))
+
+
+def test_library_exports_exactly_the_declared_boundary(lib):
+    exported = exported_functions(binding.library_path())
+    for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
+    # Nothing else: no test hook, no internal C++ symbol.
+    assert exported == set(declared_functions()), sorted(exported - set(declared_functions()))
+
+
+def test_testing_library_exports_its_hooks_and_the_boundary(lib):
+    path = os.path.join(os.path.dirname(binding.library_path()), binding.TESTING_LIB_NAME)
+    if not os.path.exists(path):
+        pytest.skip("test build not built")
+    exported = exported_functions(path)
+    hooks = declared_functions(os.path.join(ROOT, "include", "attn_decode_testing.h"))
+    assert "attn_testing_pieces" in hooks
+    assert exported == set(all_declared_functions()), sorted(exported ^ set(all_declared_functions()))
 
 
 def test_struct_layouts_match_c(tmp_path):
@@ -108,6 +124,10 @@ BAD = [
     (dict(batch=-1), "ATTN_ERR_SHAPE"),
     (dict(max_kv_len=-5), "ATTN_ERR_SHAPE"),
     (dict(max_kv_len=2 ** 31), "ATTN_ERR_SHAPE"),
+    # token indices stay in int32 with the kernels' read-ahead: at most 2^31 - 2^16
+    (dict(max_kv_len=2 ** 31 - 2 ** 16 + 1), "ATTN_ERR_SHAPE"),
+    (dict(max_kv_len=2 ** 31 - 1), "ATTN_ERR_SHAPE"),
+    (dict(max_kv_len=2 ** 31 - 2 ** 16), None),  # valid: the largest extent
     (dict(num_kv_heads=0), "ATTN_ERR_SHAPE"),
     (dict(head_dim=96), "ATTN_ERR_UNSUPPORTED"),
     (dict(head_dim=0), "ATTN_ERR_SHAPE"),
@@ -123,10 +143,11 @@ BAD = [
 @pytest.mark.parametrize("kw,status", BAD)
 def test_validation_errors_before_any_hip_call(lib, kw, status):
     d = _desc(**kw)
-    code = lib.attn_decode(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 1 << 30, None)
-    e = lib.attn_decode_energy(ctypes.byref(d), 16, 16, 16, 16, 1 << 30, None)
+    code = lib.attn_decode(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 1, None)
+    e = lib.attn_decode_energy(ctypes.byref(d), 16, 16, 16, 16, 1, None)
     if status is None:
-        assert code not in (1, 2, 3, 4, 7, 8)  # may be ATTN_ERR_HIP without a GPU
+        # ATTN_ERR_HIP without a GPU, ATTN_ERR_WORKSPACE with one
+        assert code in (5, 6) and e in (5, 6)
         return
     assert binding.STATUS[code] == status and binding.STATUS[e] == status
 
@@ -150,7 +171,7 @@ def test_bifurcated_validation(lib):
     d = binding.AttnBifDesc()
     d.num_samples, d.num_q_heads, d.num_kv_heads, d.head_dim = 4, 8, 2, 128
     d.prefix_len, d.suffix_len, d.scale, d.dtype = 100, 10, 0.1, binding.ATTN_BF16
-    args = [16] * 7 + [16, 1 << 30, None]
+    args = [16] * 7 + [16, 1, None]
     d.num_q_heads = 7
     assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *args)] == "ATTN_ERR_SHAPE"
     d.num_q_heads = 8
@@ -162,7 +183,12 @@ def test_bifurcated_validation(lib):
     d.head_dim = 128
     d.suffix_len = -1
     assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *args)] == "ATTN_ERR_SHAPE"
+    d.suffix_len = 2 ** 31 - 2 ** 16 + 1
+    assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *args)] == "ATTN_ERR_SHAPE"
     d.suffix_len = 10
+    d.prefix_len = 2 ** 31 - 2 ** 16 + 1
+    assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *args)] == "ATTN_ERR_SHAPE"
+    d.prefix_len = 100
     assert binding.STATUS[lib.attn_decode_bifurcated(ctypes.byref(d), *([16] * 6 + [0, 16, 1, None]))] == "ATTN_ERR_NULL"
     d.num_samples = 0
     assert lib.attn_decode_bifurcated(ctypes.byref(d), *args) == 0
@@ -202,11 +228,11 @@ def test_paged_validation_before_any_hip_call(lib, kw, status):
     d = _desc()
     pk = _paged(**kw)
     codes = [lib.attn_decode_paged(ctypes.byref(d), ctypes.byref(pk), 16, 16, 16, 16, 16, 16,
-                                   1 << 30, None),
+                                   1, None),
              lib.attn_decode_energy_paged(ctypes.byref(d), ctypes.byref(pk), 16, 16, 16, 16,
-                                          1 << 30, None),
+                                          1, None),
              lib.attn_decode_partials_paged(ctypes.byref(d), ctypes.byref(pk), 16, 16, 16, 16,
-                                            1 << 30, None)]
+                                            1, None)]
     for code in codes:
         if status is None:
             assert code not in (1, 2, 3, 4, 7, 8)  # may be ATTN_ERR_HIP without a GPU
@@ -222,8 +248,8 @@ def test_paged_and_zeta_null_checks(lib):
     f = _desc(dtype=binding.ATTN_F32)
     pk = _paged(token_stride=132, head_stride=16 * 132, page_stride=2 * 16 * 132)
     assert lib.attn_decode_paged(ctypes.byref(f), ctypes.byref(pk), 16, 16, 16, 16, 16, 16,
-                                 1 << 30, None) not in (1, 2, 3, 4, 7, 8)
-    args = [16, 16, 16, 16, 16, 16, 1 << 30, None]
+                                 1, None) not in (1, 2, 3, 4, 7, 8)
+    args = [16, 16, 16, 16, 16, 16, 1, None]
     assert binding.STATUS[lib.attn_decode_energy_zeta(ctypes.byref(d), *args)] not in (
         "ATTN_ERR_NULL", "ATTN_ERR_ALIGN")
     z = list(args); z[3] = 0
@@ -238,7 +264,7 @@ def test_anchor_validation(lib):
     d = binding.AttnAnchorDesc()
     d.num_blocks, d.block_len, d.num_q_heads, d.num_kv_heads, d.head_dim = 2, 64, 8, 2, 128
     d.anchor_len, d.scale, d.dtype = 100, 0.1, binding.ATTN_BF16
-    args = [16] * 7 + [16, 1 << 30, None]
+    args = [16] * 7 + [16, 1, None]
 
     def st(*a):
         return binding.STATUS[lib.attn_prefill_anchor(ctypes.byref(d), *(a or args))]
@@ -255,12 +281,14 @@ def test_anchor_validation(lib):
     d.dtype = binding.ATTN_BF16
     d.anchor_len = -1
     assert st() == "ATTN_ERR_SHAPE"
+    d.anchor_len = 2 ** 31 - 2 ** 16 + 1
+    assert st() == "ATTN_ERR_SHAPE"
     d.anchor_len = 100
     assert st(*([16] * 3 + [0] + [16] * 4 + [1, None])) == "ATTN_ERR_NULL"   # k_blocks
     assert st(*([16] * 5 + [18] + [16] * 2 + [1, None])) == "ATTN_ERR_ALIGN"  # o not 4-byte aligned
     assert st(*([16] * 3 + [24] + [16] * 4 + [1, None])) == "ATTN_ERR_ALIGN"  # k_blocks not 16-byte
     d.anchor_len = 0  # no anchor: its tensors may be null
-    assert st(*([16, 0, 0] + [16] * 5 + [1 << 30, None])) not in ("ATTN_ERR_NULL", "ATTN_ERR_ALIGN")
+    assert st(*([16, 0, 0] + [16] * 5 + [1, None])) not in ("ATTN_ERR_NULL", "ATTN_ERR_ALIGN")
     d.num_blocks = 0
     assert lib.attn_prefill_anchor(ctypes.byref(d), *args) == 0
 

@@ -6,9 +6,14 @@ The library decides this from the workgroups' first pieces; here the same
 fact is checked through a different route, the merge's own enumeration of a
 segment's record slots, for shapes that fuse and shapes that do not.
 """
+import os
+
 import pytest
 
 from long_context_exact_split_amd import binding as B
+
+# Under the host sanitizer test the plan comes from the sanitized host build.
+host_plan = B.testing_plan if os.environ.get("ATTN_TESTING_LIB") else B.plan
 
 CU = 256
 
@@ -32,7 +37,7 @@ def part_descs(N, Lb, Hq, Hkv, D, A):
 
 
 def slot_counts(d):
-    p = B.plan(d, CU)
+    p = host_plan(d, CU)
     segs = d.batch * d.num_kv_heads * p["row_blocks"]
     return p, [B.testing_segment_slots(d, None, CU, s)[2] for s in range(segs)]
 

@@ -4,7 +4,7 @@ For shapes where every segment of both parts is one piece, the local split
 merges each row's two records itself and writes O and lse (no merge launch).
 Each case checks that the path is taken, compares every row with the fp64
 oracle, and compares with the unfused path (anchor split, local split,
-merge) forced through the testing hook: the same two records are merged by
+merge) that the test build of the library runs on request: the same two records are merged by
 the same rule in the same order, so the results agree to rounding of a
 fused multiply-add.
 """
@@ -53,11 +53,7 @@ def test_fused_anchor_matches_oracle_and_unfused(case):
     t = [dev(x) for x in (q, ka, va, kb, vb)]
     scale = 1.0 / np.sqrt(D)
     O, lse = binding.prefill_anchor(*t, scale=scale)
-    try:
-        binding.testing_set_anchor_fusion(False)
-        Ou, lseu = binding.prefill_anchor(*t, scale=scale)
-    finally:
-        binding.testing_set_anchor_fusion(True)
+    Ou, lseu = binding.testing_prefill_anchor_unfused(*t, scale=scale)
     torch.cuda.synchronize()
     O, lse, Ou, lseu = (x.cpu().numpy() for x in (O, lse, Ou, lseu))
     Or, lr = oracle.attend_anchor_blocks(q, ka, va, kb, vb, scale)

@@ -9,12 +9,16 @@ Checked here, with host-side lengths through the testing hook:
 * the balanced layout gives every workgroup the same number of tokens (+-1).
 """
 import math
+import os
 
 import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
 from long_context_exact_split_amd import binding
+
+# Under the host sanitizer test the plan comes from the sanitized host build.
+host_plan = binding.testing_plan if os.environ.get("ATTN_TESTING_LIB") else binding.plan
 
 
 def desc(**kw):
@@ -24,7 +28,7 @@ def desc(**kw):
 
 
 def plan(cu=256, **kw):
-    return binding.plan(desc(**kw), cu)
+    return host_plan(desc(**kw), cu)
 
 
 def test_forced_chunk_len_single_query_fp32():
@@ -81,7 +85,7 @@ def segment_keys(d, p, L_b, rb):
 
 
 def check_cover(d, lens, cu):
-    p = binding.plan(d, cu)
+    p = host_plan(d, cu)
     B, Hkv = d.batch, d.num_kv_heads
     rbk = p["row_blocks"]
     L = np.full(B, d.max_kv_len) if lens is None else np.minimum(np.maximum(lens, 0), d.max_kv_len)
@@ -149,7 +153,7 @@ def test_anchor_prefill_local_part_is_balanced_over_visible_keys():
     """Causal prefill of 2 blocks of 8192 tokens (Hq=32, Hkv=8): 128 row
     blocks of 64 tokens per KV head, which see 64, 128, ..., 8192 keys."""
     d = desc(batch=2, q_len=8192, num_q_heads=32, num_kv_heads=8, max_kv_len=8192, causal=True)
-    p = binding.plan(d, 256)
+    p = host_plan(d, 256)
     assert p["kernel"] == 2 and p["row_blocks"] == 128
     units = 2 * 8 * sum(64 * (rb + 1) for rb in range(128))
     per_wg = []
@@ -176,4 +180,43 @@ def test_plan_rejects_invalid_descriptor():
     d = binding.make_desc(batch=1, q_len=1, num_q_heads=3, num_kv_heads=2, head_dim=64,
                           max_kv_len=10)
     with pytest.raises(binding.AttnError):
-        binding.plan(d, 256)
+        host_plan(d, 256)
+
+
+# Extremes of the descriptor: the longest cache the boundary accepts (2^31 -
+# 2^16 tokens) and the most query rows per KV head (2^16), alone and together
+# under a causal mask, where the closed-form row-block sums run on their
+# largest arguments.
+KMAX = 2 ** 31 - 2 ** 16
+EXTREMES = [
+    dict(batch=1, num_q_heads=8, num_kv_heads=8, q_len=1, max_kv_len=KMAX),
+    dict(batch=3, num_q_heads=32, num_kv_heads=8, q_len=1, max_kv_len=KMAX, ragged=True),
+    dict(batch=1, num_q_heads=4, num_kv_heads=1, q_len=16384, max_kv_len=16384, causal=True),
+    dict(batch=1, num_q_heads=4, num_kv_heads=1, q_len=16384, max_kv_len=KMAX, causal=True),
+    dict(batch=2, num_q_heads=6, num_kv_heads=1, q_len=5461, max_kv_len=KMAX // 2, causal=True,
+         ragged=True),
+    dict(batch=1, num_q_heads=2, num_kv_heads=1, q_len=32768, max_kv_len=40000, causal=True),
+]
+
+
+@pytest.mark.parametrize("shape", EXTREMES, ids=[str(i) for i in range(len(EXTREMES))])
+def test_extreme_shapes_tile_exactly(shape):
+    shape = dict(shape)
+    ragged = shape.pop("ragged", False)
+    lens = None
+    if ragged:
+        rng = np.random.default_rng(7)
+        lens = rng.integers(shape["max_kv_len"] // 2, shape["max_kv_len"], endpoint=True,
+                            size=shape["batch"]).astype(np.int32)
+        lens[0] = shape["max_kv_len"]
+    d = desc(kv_lens_ptr=0x1000 if ragged else 0, **shape)
+    p = check_cover(d, lens, 256)
+    assert p["rows"] == (shape["num_q_heads"] // shape["num_kv_heads"]) * shape["q_len"]
+
+
+def test_share_beyond_int32_is_refused():
+    """A workgroup's share of the layout is an int32 token count: a call whose
+    segments hold more than 256 * (2^31 - 1) tokens in all is refused."""
+    d = desc(batch=2, num_q_heads=12, num_kv_heads=2, q_len=5461, max_kv_len=KMAX, causal=True)
+    with pytest.raises(binding.AttnError):
+        host_plan(d, 256)
