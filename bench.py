@@ -16,6 +16,13 @@ given as median / 10th / 90th percentile, for the back-to-back timed calls
 Infinity Cache (call_ms_cold_cache; the bifurcated batch, ~203 MB, would
 otherwise stay cache-resident between calls), and for the call captured once
 into a HIP graph and replayed (call_ms_graph, with the wall time per replay).
+
+With the default workload the same line also carries ``configs``: every other
+measured configuration (single-query fp32, Llama-3-8B-shaped GQA, the
+5.12M-token cache with its energy-only and F(zeta) calls, the shared-prefix
+batch and the Llama-3.1-70B-shaped ragged batch), each timed the same way and
+checked against the oracle on sampled rows.  The run exits non-zero when any
+sampled row misses the parity bar.
 """
 import argparse
 import json
@@ -31,9 +38,12 @@ if ROOT not in sys.path:
 METRIC = "KV tokens/s and achieved HBM GB/s (% of peak), 1M-token GQA decode"
 PEAK_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+O_TOL, LSE_RTOL = 2e-3, 1e-4   # parity bar: max|dO|, |dlse| / max(1, |lse|)
 WORKLOADS = {
     "long_context_1m": "long-context GQA decode (1M tokens)",
     "long_context_5m": "long-context GQA decode (5.12M tokens)",
+    "long_context_5m_energy": "long-context GQA energy only, lse from K (5.12M tokens)",
+    "long_context_5m_zeta": "long-context GQA energy F(zeta) from K and V (5.12M tokens)",
     "llama3_8b_gqa": "Llama-3-8B-shaped GQA decode (B=8, L=32768)",
     "llama31_70b_ragged": "Llama-3.1-70B-shaped ragged decode (B=16, 4 causal query tokens)",
     "single_query_fp32": "single-query fp32 decode (L=4096, 8 chunks)",
@@ -49,9 +59,26 @@ WORKLOADS = {
 VARIANTS = {
     "long_context_1m_energy": ("long_context_1m", "energy", None),
     "long_context_1m_zeta": ("long_context_1m", "zeta", None),
+    "long_context_5m_energy": ("long_context_5m", "energy", None),
+    "long_context_5m_zeta": ("long_context_5m", "zeta", None),
     "paged_long_context_1m": ("long_context_1m", "full", (16, "head_major")),
     "paged_llama31_70b_ragged": ("llama31_70b_ragged", "full", (16, "token_major")),
 }
+# The configurations reported beside the headline: (workload, timed steps,
+# oracle rows sampled for parity).  Steps follow the per-config iteration
+# counts of the measurement plan; rows are chosen so that the oracle (which
+# reads every key of a row's KV head) stays within seconds.
+CONFIGS = [
+    ("single_query_fp32", 200, None),
+    ("llama3_8b_gqa", 50, 16),
+    ("long_context_5m", 10, 8),
+    ("long_context_5m_energy", 10, 8),
+    ("long_context_5m_zeta", 10, 2),
+    ("bifurcated_prefix", 200, 16),
+    ("llama31_70b_ragged", 30, 16),
+]
+# Configs whose oracle is also timed on one core (small enough to do whole).
+ONE_CORE = ("single_query_fp32", "llama3_8b_gqa")
 # rocprofv3 counter summaries (HBM bytes per launch of the dominant kernel),
 # one per workload.  A summary's figures are used only while the kernel
 # sources it lists still hash to its source_sha256.
@@ -60,10 +87,13 @@ COUNTERS = {
     "long_context_1m_energy": "profiles/split_kv_valu_energy_long_context_1m.counters.txt",
     "paged_long_context_1m": "profiles/split_kv_valu_paged_long_context_1m.counters.txt",
     "llama31_70b_ragged": "profiles/split_kv_mfma_llama31_70b_ragged.counters.txt",
+    "llama3_8b_gqa": "profiles/split_kv_valu_llama3_8b_gqa.counters.txt",
+    "long_context_5m": "profiles/split_kv_valu_long_context_5m.counters.txt",
+    "bifurcated_prefix": "profiles/bifurcated_call_bifurcated_prefix.counters.txt",
 }
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -76,6 +106,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the HBM read-stream reference measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="do not measure the other configurations beside the headline")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged workloads: tokens per page (0: the workload's own, 16)")
     ap.add_argument("--graph-calls", type=int, default=100,
@@ -83,7 +115,7 @@ def parse():
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="extra calls after the timed steps, each behind a 1 GiB read that "
                          "evicts L2 and the Infinity Cache (0: skip)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # ----------------------------------------------------------------------------
@@ -143,36 +175,54 @@ def read_ceiling(torch):
     return best
 
 
-def cpu_threads():
+def host_cores():
     try:
-        from threadpoolctl import threadpool_info
-        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        return 1
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
 
 
 # ----------------------------------------------------------------------------
 # Workloads
 # ----------------------------------------------------------------------------
+_WORKLOAD_CACHE = {}
+
+
 def make_workload(name):
     from long_context_exact_split_amd import inputs
     if name in VARIANTS:
         return make_workload(VARIANTS[name][0])
+    if name in _WORKLOAD_CACHE:
+        return _WORKLOAD_CACHE[name]
     if name == "long_context_1m":
-        return inputs.long_context_gqa(L=1 << 20, seed=31)
-    if name == "long_context_5m":
-        return inputs.long_context_gqa(L=5_120_000, seed=3)
-    if name == "llama3_8b_gqa":
-        return inputs.llama3_8b_gqa(seed=2)
-    if name == "llama31_70b_ragged":
-        return inputs.llama31_70b_ragged(seed=5)
-    if name == "single_query_fp32":
-        return inputs.single_query_fp32(seed=1)
-    if name == "bifurcated_prefix":
-        return inputs.bifurcated_prefix(seed=4)
-    if name == "anchor_prefill":
-        return inputs.anchor_blocks(seed=6)
-    raise ValueError(name)
+        w = inputs.long_context_gqa(L=1 << 20, seed=31)
+    elif name == "long_context_5m":
+        w = inputs.long_context_gqa(L=5_120_000, seed=3)
+    elif name == "llama3_8b_gqa":
+        w = inputs.llama3_8b_gqa(seed=2)
+    elif name == "llama31_70b_ragged":
+        w = inputs.llama31_70b_ragged(seed=5)
+    elif name == "single_query_fp32":
+        w = inputs.single_query_fp32(seed=1)
+    elif name == "bifurcated_prefix":
+        w = inputs.bifurcated_prefix(seed=4)
+    elif name == "anchor_prefill":
+        w = inputs.anchor_blocks(seed=6)
+    else:
+        raise ValueError(name)
+    _WORKLOAD_CACHE[name] = w
+    return w
 
 
 def dev(torch, a):
@@ -180,6 +230,26 @@ def dev(torch, a):
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+_DEVICE_CACHE = {}
+
+
+def device_kv(torch, w):
+    """q, k, v of a workload on the GPU, uploaded once per workload (the
+    5.12M-token cache serves three configs)."""
+    key = id(w)
+    if key not in _DEVICE_CACHE:
+        _DEVICE_CACHE[key] = (dev(torch, w.q), dev(torch, w.k), dev(torch, w.v))
+    return _DEVICE_CACHE[key]
+
+
+def forget(torch, w):
+    _DEVICE_CACHE.pop(id(w), None)
+    for k, v in list(_WORKLOAD_CACHE.items()):
+        if v is w:
+            del _WORKLOAD_CACHE[k]
+    torch.cuda.empty_cache()
 
 
 class DecodeRunner:
@@ -195,7 +265,6 @@ class DecodeRunner:
         from long_context_exact_split_amd import binding, inputs
         self.w, self.mode, self.binding = w, mode, binding
         self.pc = None
-        q = dev(torch, w.q)
         lens = None
         if not (w.kv_lens == w.L_max).all() or paging is not None:
             lens = torch.from_numpy(w.kv_lens.astype(np.int32)).cuda()
@@ -205,12 +274,13 @@ class DecodeRunner:
             self.pc = inputs.page_cache(w, P, layout=layout, seed=11)
             shape = ((self.pc.num_pages, w.Hkv, P, w.D) if layout == "head_major"
                      else (self.pc.num_pages, P, w.Hkv, w.D))
+            q = dev(torch, w.q)
             k = dev(torch, self.pc.k_pool.reshape(shape))
             v = dev(torch, self.pc.v_pool.reshape(shape))
             table = torch.from_numpy(self.pc.block_table).cuda()
             paged = binding.PagedCache(k, v, table, layout=layout, max_kv_len=w.L_max)
         else:
-            k, v = dev(torch, w.k), dev(torch, w.v)
+            q, k, v = device_kv(torch, w)
         self.q, self.k, self.v, self.lens = q, k, v, lens
         if mode == "zeta":
             rng = np.random.default_rng(17)
@@ -244,6 +314,7 @@ class DecodeRunner:
             ("" if mode == "full" else f",{mode}") + \
             ("" if paging is None else f",pages={paging[0]} {paging[1]}") + ">" + \
             (" + merge (one call)" if mode == "zeta" else "")
+        self.bound = "hbm"
 
     def first(self):
         if self.mode == "zeta":
@@ -276,10 +347,15 @@ class DecodeRunner:
         return (None if self.ph.out is None else self.ph.out.cpu().numpy()), self.ph.lse.cpu().numpy()
 
     def oracle_rows(self, n_rows):
+        """n_rows rows spread over the call; with planted needles, the needle
+        rows (the group's first query head, whose logit the needle dominates)
+        come first."""
         w = self.w
         rows = [(b, i, h) for b in range(w.B) for i in range(w.q_len) for h in range(w.Hq)]
-        step = max(1, len(rows) // n_rows)
-        return rows[::step][:n_rows]
+        first = [(b, 0, w.G * kvh) for (b, kvh, _) in w.notes.get("needles", [])]
+        rest = [r for r in rows if r not in set(first)]
+        step = max(1, len(rest) // max(1, n_rows - len(first)))
+        return (first + rest[::step])[:n_rows]
 
     def oracle(self, rows):
         import oracle
@@ -297,6 +373,14 @@ class DecodeRunner:
                                        L_max=w.L_max, causal=w.causal, rows=rows)
         return oracle.attend(w.q, w.k, v, w.kv_lens, w.scale, w.causal, rows=rows)
 
+    def row_groups(self, rows):
+        """Rows split into independent oracle calls: one per (sequence, KV head)."""
+        G = self.w.G
+        groups = {}
+        for r in rows:
+            groups.setdefault((r[0], r[2] // G), []).append(r)
+        return list(groups.values())
+
 
 class BifurcatedRunner:
     """The shared-prefix call, timed as one unit (three launches)."""
@@ -313,7 +397,9 @@ class BifurcatedRunner:
         self.q_bytes = w.S * w.Hq * w.D * 2
         self.out_bytes = w.S * w.Hq * (w.D + 1) * 4
         self.flops = 4 * w.S * w.Hq * w.D * (w.Lp + w.Ls)
+        self.prefix_flops = 4 * w.S * w.Hq * w.D * w.Lp
         self.kernel = "bifurcated (prefix split kernel + suffix split kernel + merge)"
+        self.bound = "hbm"
 
     def first(self):
         self.call.run()
@@ -340,6 +426,12 @@ class BifurcatedRunner:
         samples = sorted({s for (s, _, _) in rows})
         O, lse = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale, samples=samples)
         return O[:, None], lse[:, None]
+
+    def row_groups(self, rows):
+        groups = {}
+        for r in rows:
+            groups.setdefault(r[0], []).append(r)
+        return list(groups.values())
 
 
 class AnchorRunner:
@@ -370,6 +462,7 @@ class AnchorRunner:
         pairs = N * Hkv * G * (Lb * A + Lb * (Lb + 1) // 2)
         self.flops = 4 * D * pairs
         self.kernel = "anchor prefill (anchor split + local causal split + merge)"
+        self.bound = "mfma"
 
     def first(self):
         self.binding.prefill_anchor(*self.t, scale=self.w.scale, out=self.out, lse=self.lse,
@@ -392,29 +485,97 @@ class AnchorRunner:
         w = self.w
         return oracle.attend_anchor_blocks(w.q, w.ka, w.va, w.kb, w.vb, w.scale, rows=rows)
 
+    def row_groups(self, rows):
+        groups = {}
+        for r in rows:
+            groups.setdefault(r[0], []).append(r)
+        return list(groups.values())
+
+
+def make_runner(torch, name, page_size=0):
+    w = make_workload(name)
+    if name == "bifurcated_prefix":
+        return BifurcatedRunner(torch, w)
+    if name == "anchor_prefill":
+        return AnchorRunner(torch, w)
+    _, mode, paging = VARIANTS.get(name, (None, "full", None))
+    if paging is not None and page_size:
+        paging = (page_size, paging[1])
+    return DecodeRunner(torch, w, mode, paging)
+
+
+# ----------------------------------------------------------------------------
+# The oracle on sampled rows, and parity
+# ----------------------------------------------------------------------------
+def run_oracle(run, rows, threads):
+    """The oracle over `rows`, its independent (sequence, KV head) calls spread
+    over `threads` host threads (numpy's BLAS pinned to one thread each, so the
+    thread count is the core count used).  Returns (O, lse, seconds, threads
+    actually used)."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    groups = run.row_groups(rows)
+    used = max(1, min(threads, len(groups)))
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1, user_api="blas"):
+        if used == 1:
+            parts = [run.oracle(g) for g in groups]
+        else:
+            with ThreadPoolExecutor(used) as ex:
+                parts = list(ex.map(run.oracle, groups))
+    dt = time.perf_counter() - t0
+    O, lse = parts[0]
+    for g, (Og, lg) in zip(groups[1:], parts[1:]):
+        for r in g:
+            lse[r] = lg[r]
+            if O is not None:
+                O[r] = Og[r]
+    return O, lse, dt, used
+
+
+def parity(rows, O_gpu, lse_gpu, Or, lr):
+    """Worst deviations on the sampled rows and whether they meet the bar
+    (an empty row must give lse = -inf and O = 0 exactly; NaN never)."""
+    import numpy as np
+    idx = tuple(np.array(rows).T)
+    lg, lo = lse_gpu[idx].astype(np.float64), lr[idx]
+    empty = np.isneginf(lo)
+    ok = bool(not np.isnan(lg).any() and (lg[empty] == -np.inf).all())
+    dl = float((np.abs(lg[~empty] - lo[~empty]) / np.maximum(1.0, np.abs(lo[~empty]))).max()) \
+        if (~empty).any() else 0.0
+    ok = ok and dl <= LSE_RTOL
+    dO = None
+    if O_gpu is not None and Or is not None:
+        og, oo = O_gpu[idx].astype(np.float64), Or[idx]
+        ok = ok and not np.isnan(og).any() and bool((og[empty] == 0).all())
+        dO = float(np.abs(og[~empty] - oo[~empty]).max()) if (~empty).any() else 0.0
+        ok = ok and dO <= O_TOL
+    return {"rows": len(rows), "max_abs_dO": dO, "max_rel_dlse": dl, "ok": bool(ok)}
+
 
 def cpu_baseline(run, n_rows, O_gpu, lse_gpu):
     """Time the fp64 oracle on a sample of the workload's query rows (each row
     over its full visible cache) and check the GPU's values on those rows."""
-    import numpy as np
     rows = run.oracle_rows(n_rows)
-    t0 = time.perf_counter()
-    Or, lr = run.oracle(rows)
-    dt = time.perf_counter() - t0
-    idx = tuple(np.array(rows).T)
-    dO = float(np.abs(O_gpu[idx] - Or[idx]).max()) if O_gpu is not None and Or is not None else None
-    fin = np.isfinite(lr[idx])
-    dl = float((np.abs(lse_gpu[idx][fin] - lr[idx][fin]) /
-                np.maximum(1.0, np.abs(lr[idx][fin]))).max()) if fin.any() else 0.0
+    cores = host_cores()
+    Or, lr, dt, used = run_oracle(run, rows, cores)
     total_rows = lse_gpu.shape[0] * lse_gpu.shape[1] * lse_gpu.shape[2]
     frac = len(rows) / total_rows
-    return {"value": run.kv_tokens * frac / dt, "unit": "KV tokens/s", "cores": int(cpu_threads()),
+    par = parity(rows, O_gpu, lse_gpu, Or, lr)
+    return {"value": run.kv_tokens * frac / dt, "unit": "KV tokens/s", "cores": used,
             "kind": "oracle",
             "sample": f"{len(rows)} of {total_rows} query rows, each over its whole visible cache "
-                      f"({dt:.2f} s); rate = KV tokens of the call x {len(rows)}/{total_rows} / time",
-            "seconds": dt, "parity_max_abs_dO": dO, "parity_max_rel_dlse": dl}
+                      f"({dt:.2f} s on {used} threads, one (sequence, KV head) group each); "
+                      f"rate = KV tokens of the call x {len(rows)}/{total_rows} / time",
+            "seconds": dt, "host_cores": cores, "cpu_model": cpu_model(), "blas_threads": 1,
+            "parity_max_abs_dO": par["max_abs_dO"], "parity_max_rel_dlse": par["max_rel_dlse"],
+            "parity_ok": par["ok"]}
 
 
+# ----------------------------------------------------------------------------
+# Timing
+# ----------------------------------------------------------------------------
 FLUSH_BYTES = 1 << 30  # > 8 x 4 MB L2 + 256 MB Infinity Cache
 
 
@@ -425,6 +586,38 @@ def spread(ms):
     def pct(p):
         return xs[min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))]
     return {"median": statistics.median(xs), "p10": pct(10), "p90": pct(90), "calls": len(xs)}
+
+
+def timed_steps(torch, run, K, warmup, min_warmup_s):
+    """Untimed warm-up (at least `warmup` steps and `min_warmup_s` seconds:
+    from idle the GPU needs ~30-40 back-to-back steps to reach its steady
+    clocks), then K steps, each bracketed by HIP events on the launch stream
+    (first launch, second launch).  Returns the per-step event times and the
+    wall time of the K steps."""
+    # Events are created before the warm-up: creating them afterwards would
+    # leave the GPU idle long enough for its clocks to drop again.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    stream = torch.cuda.current_stream()
+    warm, t_w = 0, time.perf_counter()
+    while warm < warmup or time.perf_counter() - t_w < min_warmup_s:
+        run.first()
+        run.second()
+        warm += 1
+        if warm % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()  # barrier (one rank)
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        run.first()
+        ev[i][1].record(stream)
+        run.second()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"first_ms": [e[0].elapsed_time(e[1]) for e in ev],
+            "second_ms": [e[1].elapsed_time(e[2]) for e in ev],
+            "call_ms": [e[0].elapsed_time(e[2]) for e in ev], "wall_s": wall, "warmup": warm}
 
 
 def cold_calls(torch, run, n):
@@ -490,8 +683,60 @@ def graph_calls(torch, run, n):
     return out
 
 
-def main():
-    args = parse()
+def roofline(run, first_avg_ms, workload):
+    """Roofline record of the dominant launch (or of the whole call for the
+    bifurcated and anchor workloads, which time their launches together)."""
+    if run.bound == "mfma":
+        tf = run.flops / (first_avg_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": run.kernel,
+                "algorithmic_flops_per_launch": run.flops}
+    alg = run.kv_bytes + run.q_bytes
+    gbps = alg / (first_avg_ms * 1e-3) / 1e9
+    traffic = counter_traffic(workload)
+    return {"bound": "hbm", "achieved": gbps, "peak": PEAK_GBPS, "unit": "GB/s",
+            "frac": gbps / PEAK_GBPS, "traffic": traffic,
+            "traffic_ratio": None if traffic is None else traffic / alg,
+            "kernel": run.kernel, "algorithmic_bytes_per_launch": alg}
+
+
+def measure_config(torch, name, K, n_rows, warmup, min_warmup_s):
+    """One configuration beside the headline: timed steps, roofline of its
+    dominant launch, whole-call times with cold caches where the inputs fit in
+    the Infinity Cache, and oracle parity on sampled rows (with the oracle's
+    time on them; one-core times too for the small configs)."""
+    w = make_workload(name)
+    run = make_runner(torch, name)
+    t = timed_steps(torch, run, K, warmup, min_warmup_s)
+    first_avg = statistics.mean(t["first_ms"])
+    call_avg = statistics.mean(t["call_ms"])
+    rec = {"workload": WORKLOADS[name], "seed": getattr(w, "seed", None),
+           "dtype": getattr(w, "dtype", "bf16"), "steps": K,
+           "ms_per_step": t["wall_s"] * 1e3 / K, "call_ms_mean": call_avg,
+           "call_ms": spread(t["call_ms"]), "dominant_kernel_ms": first_avg,
+           "kv_tokens_per_call": run.kv_tokens,
+           "kv_tokens_per_s": run.kv_tokens / (call_avg * 1e-3),
+           "roofline": roofline(run, first_avg, name)}
+    if isinstance(run, BifurcatedRunner):
+        rec["call_ms_cold_cache"] = cold_calls(torch, run, 20)
+        rec["kv_tokens_physical"] = w.Lp + w.S * w.Ls
+        rec["tflops_counted"] = run.flops / (first_avg * 1e-3) / 1e12
+    O, lse = run.outputs()
+    rows = run.oracle_rows(n_rows if n_rows else lse.size)
+    Or, lr, dt, used = run_oracle(run, rows, host_cores())
+    rec["parity"] = parity(rows, O, lse, Or, lr)
+    total_rows = lse.size
+    rec["oracle"] = {"seconds": dt, "threads": used,
+                     "kv_tokens_per_s": run.kv_tokens * len(rows) / total_rows / dt}
+    if name in ONE_CORE:
+        _, _, dt1, _ = run_oracle(run, rows, 1)
+        rec["oracle"]["one_core_seconds"] = dt1
+        rec["oracle"]["one_core_kv_tokens_per_s"] = run.kv_tokens * len(rows) / total_rows / dt1
+    return rec
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1 "
                                    "(sharding the KV cache across GPUs is not implemented)"}))
@@ -506,51 +751,14 @@ def main():
     w = make_workload(args.workload)
     print(f"# generated {args.workload} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
-    if args.workload == "bifurcated_prefix":
-        run = BifurcatedRunner(torch, w)
-    elif args.workload == "anchor_prefill":
-        run = AnchorRunner(torch, w)
-    else:
-        _, mode, paging = VARIANTS.get(args.workload, (None, "full", None))
-        if paging is not None and args.page_size:
-            paging = (args.page_size, paging[1])
-        run = DecodeRunner(torch, w, mode, paging)
+    run = make_runner(torch, args.workload, args.page_size)
     print(f"# plan {run.plan}", file=sys.stderr, flush=True)
 
     K = args.steps
-    # Events are created before the warm-up: creating them afterwards would
-    # leave the GPU idle long enough for its clocks to drop again.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    stream = torch.cuda.current_stream()
-
-    # Untimed warm-up: at least --warmup steps and --min-warmup-s seconds.  From
-    # idle the GPU needs ~30-40 back-to-back steps (~25 ms) to reach its
-    # steady clocks; the timed region measures the steady state.
-    warm, t_w = 0, time.perf_counter()
-    while warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
-        run.first()
-        run.second()
-        warm += 1
-        if warm % 16 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()  # barrier (one rank)
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        run.first()
-        ev[i][1].record(stream)
-        run.second()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    first_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    second_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    call_ms = [e[0].elapsed_time(e[2]) for e in ev]
-
-    step_ms = wall * 1e3 / K
-    first_avg = statistics.mean(first_ms)
+    t = timed_steps(torch, run, K, args.warmup, args.min_warmup_s)
+    step_ms = t["wall_s"] * 1e3 / K
+    first_avg = statistics.mean(t["first_ms"])
     alg = run.kv_bytes + run.q_bytes
-    dom_gbps = alg / (first_avg * 1e-3) / 1e9
     path_gbps = (alg + run.out_bytes) / (step_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -559,7 +767,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "warmup_steps_run": warm,
+        "warmup_steps_run": t["warmup"],
         "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -570,23 +778,14 @@ def main():
         "hbm_gbps": path_gbps,
         "hbm_frac_of_peak": path_gbps / PEAK_GBPS,
         "dominant_kernel_ms": first_avg,
-        "dominant_kernel_ms_median": statistics.median(first_ms),
-        "second_launch_ms": statistics.mean(second_ms),
-        "call_ms": spread(call_ms),
+        "dominant_kernel_ms_median": statistics.median(t["first_ms"]),
+        "second_launch_ms": statistics.mean(t["second_ms"]),
+        "call_ms": spread(t["call_ms"]),
         "tflops": run.flops / (first_avg * 1e-3) / 1e12,
-        "roofline": {"bound": "hbm", "achieved": dom_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom_gbps / PEAK_GBPS, "traffic": counter_traffic(args.workload),
-                     "kernel": run.kernel, "algorithmic_bytes_per_launch": alg},
+        "roofline": roofline(run, first_avg, args.workload),
     }
     if args.workload == "bifurcated_prefix":
         result["kv_tokens_physical"] = w.Lp + w.S * w.Ls
-    if args.workload == "anchor_prefill":
-        # A dense contraction (256 and more query rows per KV tile): bound by
-        # the bf16 matrix cores, priced against their dense peak.
-        tf = result["tflops"]
-        result["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
-                              "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
-                              "kernel": run.kernel, "algorithmic_flops_per_launch": run.flops}
     if args.cold_calls > 0:
         result["call_ms_cold_cache"] = cold_calls(torch, run, args.cold_calls)
     if args.graph_calls > 0:
@@ -594,11 +793,33 @@ def main():
     if not args.no_ceiling:
         ceil = read_ceiling(torch)
         result["hbm_read_ceiling_gbps"] = ceil
-        result["roofline"]["frac_of_read_ceiling"] = dom_gbps / ceil
+        result["roofline"]["frac_of_read_ceiling"] = result["roofline"]["achieved"] / ceil \
+            if result["roofline"]["unit"] == "GB/s" else None
+    parity_ok = True
     if not args.no_cpu_baseline:
         O, lse = run.outputs()
         result["cpu_baseline"] = cpu_baseline(run, args.cpu_rows, O, lse)
+        parity_ok = result["cpu_baseline"]["parity_ok"]
+    if args.workload == "long_context_1m" and not args.no_configs:
+        del run
+        forget(torch, w)
+        configs = {}
+        for name, steps, n_rows in CONFIGS:
+            t_c = time.perf_counter()
+            configs[name] = measure_config(torch, name, steps, n_rows, args.warmup,
+                                           min(args.min_warmup_s, 0.3))
+            parity_ok = parity_ok and configs[name]["parity"]["ok"]
+            print(f"# config {name}: {configs[name]['call_ms_mean']:.4f} ms per call, parity "
+                  f"{configs[name]['parity']} ({time.perf_counter() - t_c:.1f} s)",
+                  file=sys.stderr, flush=True)
+            if name in ("long_context_5m_zeta", "llama31_70b_ragged", "bifurcated_prefix"):
+                forget(torch, make_workload(name))
+        result["configs"] = configs
+    result["parity_ok"] = parity_ok
     print(json.dumps(result), flush=True)
+    if not parity_ok:
+        print("# parity bar missed on sampled rows", file=sys.stderr, flush=True)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

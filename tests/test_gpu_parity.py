@@ -27,6 +27,32 @@ def oracle_decode(w, rows=None):
     return oracle.attend(w.q, w.k, w.v, w.kv_lens, w.scale, w.causal, rows=rows)
 
 
+def oracle_decode_parallel(w, rows, energy_only=False):
+    """The oracle on sampled rows of a long cache: one call per (sequence, KV
+    head) group, the groups in parallel host threads (numpy releases the
+    interpreter in its kernels), each printing when it is done."""
+    from concurrent.futures import ThreadPoolExecutor
+    groups = {}
+    for r in rows:
+        groups.setdefault((r[0], r[2] // w.G), []).append(r)
+
+    def one(g):
+        out = oracle.attend(w.q, w.k, None if energy_only else w.v, w.kv_lens, w.scale,
+                            w.causal, rows=g)
+        say(f"  oracle group (b, kvh) = ({g[0][0]}, {g[0][2] // w.G}) done")
+        return g, out
+    with ThreadPoolExecutor(min(8, len(groups))) as ex:
+        parts = list(ex.map(one, groups.values()))
+    O = None if energy_only else np.full(w.q.shape, np.nan)
+    lse = np.full(w.q.shape[:3], np.nan)
+    for g, (Og, lg) in parts:
+        for r in g:
+            lse[r] = lg[r]
+            if O is not None:
+                O[r] = Og[r]
+    return O, lse
+
+
 # ----------------------------------------------------------------------------
 # The five workload shapes
 # ----------------------------------------------------------------------------
@@ -356,14 +382,32 @@ def _needle_rows(w, extra_heads=(5, 18, 27)):
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 def test_long_context_1m_needle():
+    """The headline shape: decode, energy only and F(zeta) on one 1M-token
+    cache, each against the oracle on the needle rows and three others; the
+    energy-only lse equals the decode lse bit for bit on every row."""
     w = inputs.long_context_gqa(L=1 << 20, seed=31)
     say("generated 1M-token cache")
-    O, lse = run_decode(w)
+    q, k, v, lens = workload_tensors(w)
+    O, lse = binding.decode(q, k, v, lens, scale=w.scale)
+    lse_e = binding.decode_energy(q, k, lens, scale=w.scale)
+    zrng = np.random.default_rng(17)
+    zeta = inputs.f32_to_bf16(zrng.standard_normal(w.q.shape, dtype=np.float32) * np.float32(0.25))
+    F = binding.decode_energy_zeta(q, k, v, dev(zeta), lens, scale=w.scale)
+    torch.cuda.synchronize()
+    O, lse, lse_e, F = (x.cpu().numpy() for x in (O, lse, lse_e, F))
+    del q, k, v
+    torch.cuda.empty_cache()
+    assert np.array_equal(lse_e, lse), "energy-only lse differs from the decode lse"
     rows = _needle_rows(w)
-    Or, lr = oracle_decode(w, rows=rows)
+    Or, lr = oracle_decode_parallel(w, rows)
     check_rows(O, lse, Or, lr, rows=rows, what="long_context_gqa L=1,048,576")
+    check_rows(None, lse_e, None, lr, rows=rows, what="energy only, L=1,048,576")
     for (_, kvh, n) in w.notes["needles"]:
         assert 29.0 < lse[0, 0, w.G * kvh] < 31.0
+    zrows = rows[:4]
+    Fr = oracle.energy_rows(w.q, w.k, w.v, w.kv_lens, w.scale, inputs.bf16_to_f32(zeta),
+                            rows=zrows)
+    check_rows(None, F, None, Fr, rows=zrows, what="F(zeta), L=1,048,576")
 
 
 @pytest.mark.slow
@@ -377,9 +421,9 @@ def test_long_context_5m_needle():
     O, lse = O.cpu().numpy(), lse.cpu().numpy()
     del q, k, v
     torch.cuda.empty_cache()
-    # three KV-head groups (the oracle streams 5.12M tokens per group)
-    rows = [r for r in _needle_rows(w, extra_heads=(1, 29)) if r[2] // w.G in (0, 3, 7)]
-    Or, lr = oracle_decode(w, rows=rows)
+    # every needle row (all eight KV-head groups) and two other heads
+    rows = _needle_rows(w, extra_heads=(1, 29))
+    Or, lr = oracle_decode_parallel(w, rows)
     check_rows(O, lse, Or, lr, rows=rows, what="long_context_gqa L=5,120,000")
     # the needle dominates: O is its V row up to the weight left to the others
     for (_, kvh, n) in w.notes["needles"]:
@@ -400,12 +444,16 @@ def test_llama31_70b_ragged_full_size():
     w = inputs.llama31_70b_ragged(seed=5)
     say(f"lengths {w.kv_lens.tolist()}")
     O, lse = run_decode(w)
+    # every sequence, one KV-head group of each (all 32 of its rows), and a
+    # second group for the longest and the shortest sequence
     rng = np.random.default_rng(0)
+    picks = [(b, int(rng.integers(0, w.Hkv))) for b in range(w.B)]
+    for b in (int(np.argmax(w.kv_lens)), int(np.argmin(w.kv_lens))):
+        picks.append((b, (dict(picks)[b] + 1) % w.Hkv))
     rows = []
-    for b in rng.choice(w.B, size=6, replace=False):
-        kvh = int(rng.integers(0, w.Hkv))
-        rows += [(int(b), i, h) for i in range(w.q_len) for h in range(kvh * w.G, (kvh + 1) * w.G)]
-    Or, lr = oracle_decode(w, rows=rows)
+    for b, kvh in picks:
+        rows += [(b, i, h) for i in range(w.q_len) for h in range(kvh * w.G, (kvh + 1) * w.G)]
+    Or, lr = oracle_decode_parallel(w, rows)
     check_rows(O, lse, Or, lr, rows=rows, what="llama31_70b_ragged (sampled groups)")
 
 
