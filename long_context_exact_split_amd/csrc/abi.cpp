@@ -350,17 +350,19 @@ attn_status_t attn_decode_bifurcated(const attn_bifurcated_desc_t *desc, const v
     const PartialLayout pre = carve(ws, b.pp, desc->head_dim);
     const PartialLayout suf = carve(ws + b.pre_bytes, b.sp, desc->head_dim);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const SplitArgs pa = split_args(&b.pre, b.pp, q, k_prefix, v_prefix, nullptr,
+                                    dense_paging(&b.pre), pre);
+    const SplitArgs sa = split_args(&b.suf, b.sp, q, k_suffix, v_suffix, nullptr,
+                                    dense_paging(&b.suf), suf);
     (void)hipGetLastError();
-    if (launch_split(&b.pre, b.pp,
-                     split_args(&b.pre, b.pp, q, k_prefix, v_prefix, nullptr,
-                                dense_paging(&b.pre), pre),
-                     SplitMode::kFull, s) != hipSuccess)
-      return ATTN_ERR_HIP;
-    if (launch_split(&b.suf, b.sp,
-                     split_args(&b.suf, b.sp, q, k_suffix, v_suffix, nullptr,
-                                dense_paging(&b.suf), suf),
-                     SplitMode::kFull, s) != hipSuccess)
-      return ATTN_ERR_HIP;
+    if (b.fused) {
+      if (launch_bifurcated(pa, sa, desc->head_dim, b.sp.rows_per_block, b.workgroups, s) !=
+          hipSuccess)
+        return ATTN_ERR_HIP;
+    } else {
+      if (launch_split(&b.pre, b.pp, pa, SplitMode::kFull, s) != hipSuccess) return ATTN_ERR_HIP;
+      if (launch_split(&b.suf, b.sp, sa, SplitMode::kFull, s) != hipSuccess) return ATTN_ERR_HIP;
+    }
     MergeArgs m{};
     m.map = work_map(&b.suf, b.sp);
     m.part = suf;

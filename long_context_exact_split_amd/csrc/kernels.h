@@ -69,5 +69,11 @@ hipError_t launch_split_valu(const attn_plan_t &plan, const SplitArgs &a, attn_d
 hipError_t launch_split_mfma(const attn_plan_t &plan, const SplitArgs &a, int head_dim,
                              bool energy_only, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream);
+// Both parts of a shared-prefix call in one launch of `workgroups` 8-wave
+// workgroups: the prefix split (shared-tile kernel, 256-row blocks) and the
+// suffix split (vector-ALU code, suffix_rows_per_block rows), each over its
+// own balanced map with n_wg == workgroups; full mode, dense caches.
+hipError_t launch_bifurcated(const SplitArgs &pre, const SplitArgs &suf, int head_dim,
+                             int suffix_rows_per_block, int64_t workgroups, hipStream_t stream);
 
 }  // namespace attn

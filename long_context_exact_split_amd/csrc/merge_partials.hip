@@ -6,6 +6,8 @@
 // statistics at its query host), then O = o / l and lse = (m + log2 l) ln 2.
 // The records of a row are found in closed form from the work map
 // (work_map.h), which the split kernels followed.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -73,21 +75,48 @@ __device__ __forceinline__ RowRecords row_records(const MergeArgs &a, int b, int
   return rr;
 }
 
-// Rows with many records (a long cache cut into many pieces): one workgroup
-// per output row.  The row's records are read in parallel: 16 bytes of o per
-// lane, kMergeThreads / (D/4) record groups, each combining its records in
-// one pass with the rule itself (running max, earlier sums rescaled when it
-// grows), so no separate pass over the records' maxima has to come first.
-// The groups' results are then combined through LDS in a fixed order
-// (deterministic).  Every wave works out where the row's records are by
-// itself, so no barrier comes before the first record load.
+// The merge rule on one lane's share of two records: (ma, la, oa) becomes
+// (ma, la, oa) + (mb, lb, ob).  The identity (-inf, 0, 0) is guarded
+// (rescale_factor is 0 for a -inf maximum).
+template <int N>
+__device__ __forceinline__ void combine(float &ma, float &la, float (&oa)[N], float mb, float lb,
+                                        const float (&ob)[N]) {
+  const float M = fmaxf(ma, mb);
+  const float fa = rescale_factor(ma, M), fb = rescale_factor(mb, M);
+  la = la * fa + lb * fb;
+#pragma unroll
+  for (int e = 0; e < N; ++e) oa[e] = oa[e] * fa + ob[e] * fb;
+  ma = M;
+}
+
+// Rows with many records (a long cache cut into many pieces, or a shared
+// prefix cut into pieces for all samples): one workgroup per output row.
+// The row's records are combined by a tree of the associative merge rule
+// (Tree Attention article, an energy view of attention), in a fixed order:
+//   * record groups of LPR lanes (16 bytes of o per lane); group g takes
+//     records g, g + NG, g + 2NG, ... and loads up to kBatch of them at once
+//     (one memory round trip for up to NG * kBatch records);
+//   * each group reduces its batch as a binary tree in registers, and folds
+//     the batch into what earlier batches left (rows with more than
+//     NG * kBatch records);
+//   * the groups of a wave pair up across lanes (v_permlane swaps), then the
+//     waves' results pair up through LDS.
+// Every wave works out where the row's records are by itself, so no barrier
+// comes before the first record load.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / kWave;
+#ifndef ATTN_MERGE_BATCH
+#define ATTN_MERGE_BATCH 8
+#endif
+constexpr int kBatch = ATTN_MERGE_BATCH;  // records per group loaded together
 
 template <int D, bool ENERGY, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   constexpr int LPR = D / 4;                 // lanes per record (float4 each)
   constexpr int NG = kMergeThreads / LPR;    // record groups
+  constexpr int EO = ENERGY ? 1 : 4;         // o elements per lane
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int64_t row = blockIdx.x;
   const int r = (int)(row % a.R);
   const int group = (int)(row / a.R);
@@ -98,65 +127,105 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   const int n = rr.P + rr.S;
   const int cg = tid / LPR;   // record group
   const int dl = tid % LPR;   // float4 slot within the record
-  float Mg = -INFINITY, lg = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4  // four records of a group in flight (unroll 2: 2-8% slower, 8: 18%)
-  for (int c = cg; c < n; c += NG) {
-    const bool shared = c >= rr.P;
-    const int64_t rec = shared ? rr.srow + (c - rr.P) * rr.sstride : rr.prow + c * rr.pstride;
-    // Pointers chosen as values: a reference to either argument struct would
-    // be read back from argument memory before every record.
-    const float mc = (shared ? a.shared.m : a.part.m)[rec];
-    const float lc = (shared ? a.shared.l : a.part.l)[rec];
-    const float Mn = fmaxf(Mg, mc);
-    const float fa = rescale_factor(Mg, Mn), fb = rescale_factor(mc, Mn);
-    lg = lg * fa + lc * fb;
-    if constexpr (!ENERGY) {
-      const float4 v =
-          *reinterpret_cast<const float4 *>((shared ? a.shared.o : a.part.o) + rec * D + dl * 4);
-      acc.x = acc.x * fa + v.x * fb;
-      acc.y = acc.y * fa + v.y * fb;
-      acc.z = acc.z * fa + v.z * fb;
-      acc.w = acc.w * fa + v.w * fb;
+  float Mg = -INFINITY, lg = 0.0f, og[EO];
+#pragma unroll
+  for (int e = 0; e < EO; ++e) og[e] = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += NG * kBatch) {
+    float mc[kBatch], lc[kBatch], oc[kBatch][EO];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = c0 + cg + k * NG;
+      mc[k] = -INFINITY;
+      lc[k] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EO; ++e) oc[k][e] = 0.0f;
+      if (c < n) {
+        const bool shared = c >= rr.P;
+        const int64_t rec = shared ? rr.srow + (c - rr.P) * rr.sstride : rr.prow + c * rr.pstride;
+        // Pointers chosen as values: a reference to either argument struct
+        // would be read back from argument memory before every record.
+        mc[k] = (shared ? a.shared.m : a.part.m)[rec];
+        lc[k] = (shared ? a.shared.l : a.part.l)[rec];
+        if constexpr (!ENERGY) {
+          const float4 v = *reinterpret_cast<const float4 *>(
+              (shared ? a.shared.o : a.part.o) + rec * D + dl * 4);
+          oc[k][0] = v.x;
+          oc[k][1] = v.y;
+          oc[k][2] = v.z;
+          oc[k][3] = v.w;
+        }
+      }
     }
-    Mg = Mn;
+    // Binary tree over the batch: (0,1) (2,3) ..., then (01,23) ..., in place.
+#pragma unroll
+    for (int step = 1; step < kBatch; step *= 2)
+#pragma unroll
+      for (int k = 0; k + step < kBatch; k += 2 * step)
+        combine<EO>(mc[k], lc[k], oc[k], mc[k + step], lc[k + step], oc[k + step]);
+    combine<EO>(Mg, lg, og, mc[0], lc[0], oc[0]);
   }
-  __shared__ float sm[NG], sl[NG];
-  __shared__ float4 so[ENERGY ? 1 : NG][ENERGY ? 1 : LPR];
-  if (dl == 0) {
-    sm[cg] = Mg;
-    sl[cg] = lg;
+  // Groups of one wave: lanes 16 and 32 apart hold the same slot of o of
+  // neighbouring groups (LPR is 16 or 32); both lanes of a pair get the
+  // lower lane's record first, so both combine the same two in one order.
+  static_assert(LPR == 16 || LPR == 32, "head_dim 64 or 128");
+  auto pair = [&](auto off_c) {
+    constexpr int OFF = decltype(off_c)::value;
+    float ma, mb, la, lb, oa[EO], ob[EO];
+    lane_pair<OFF>(Mg, ma, mb);
+    lane_pair<OFF>(lg, la, lb);
+#pragma unroll
+    for (int e = 0; e < EO; ++e) lane_pair<OFF>(og[e], oa[e], ob[e]);
+    combine<EO>(ma, la, oa, mb, lb, ob);
+    Mg = ma;
+    lg = la;
+#pragma unroll
+    for (int e = 0; e < EO; ++e) og[e] = oa[e];
+  };
+  if constexpr (LPR == 16) pair(std::integral_constant<int, 16>{});
+  pair(std::integral_constant<int, 32>{});
+  // Waves: (0,1) and (2,3), then the two pairs.
+  __shared__ float sm[kMergeWaves], sl[kMergeWaves];
+  __shared__ float4 so[ENERGY ? 1 : kMergeWaves][ENERGY ? 1 : LPR];
+  if (lane < LPR) {
+    if (lane == 0) {
+      sm[wave] = Mg;
+      sl[wave] = lg;
+    }
+    if constexpr (!ENERGY) so[wave][lane] = make_float4(og[0], og[1], og[2], og[3]);
   }
-  if constexpr (!ENERGY) so[cg][dl] = acc;
   __syncthreads();
+  if (wave != 0 || lane >= LPR) return;
+  float wm[kMergeWaves], wl[kMergeWaves], wo[kMergeWaves][EO];
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    wm[w] = sm[w];
+    wl[w] = sl[w];
+    if constexpr (!ENERGY) {
+      const float4 v = so[w][lane];
+      wo[w][0] = v.x;
+      wo[w][1] = v.y;
+      wo[w][2] = v.z;
+      wo[w][3] = v.w;
+    } else {
+      wo[w][0] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int step = 1; step < kMergeWaves; step *= 2)
+#pragma unroll
+    for (int w = 0; w + step < kMergeWaves; w += 2 * step)
+      combine<EO>(wm[w], wl[w], wo[w], wm[w + step], wl[w + step], wo[w + step]);
 
   const int i = r / a.G;
   const int h = kvh * a.G + (r - i * a.G);
   const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
-  float M = sm[0];
-#pragma unroll
-  for (int g = 1; g < NG; ++g) M = fmaxf(M, sm[g]);
-  float f[NG];
-  float ltot = 0.0f;
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    f[g] = rescale_factor(sm[g], M);
-    ltot += sl[g] * f[g];
-  }
-  const bool empty = M == -INFINITY || !(ltot > 0.0f);
-  if (tid == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(ltot)) * kLn2;
+  const bool empty = wm[0] == -INFINITY || !(wl[0] > 0.0f);
+  if (lane == 0) a.lse[orow] = empty ? -INFINITY : (wm[0] + log2f(wl[0])) * kLn2;
   if constexpr (!ENERGY) {
-    if (tid < LPR) {
-      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float inv = empty ? 0.0f : 1.0f / wl[0];
+    float *dst = a.o + orow * D + lane * 4;  // O is only 4-byte aligned
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const float4 v = so[g][tid];
-        t.x += v.x * f[g]; t.y += v.y * f[g]; t.z += v.z * f[g]; t.w += v.w * f[g];
-      }
-      const float inv = empty ? 0.0f : 1.0f / ltot;
-      float *dst = a.o + orow * D + tid * 4;  // O is only 4-byte aligned
-      dst[0] = t.x * inv; dst[1] = t.y * inv; dst[2] = t.z * inv; dst[3] = t.w * inv;
-    }
+    for (int e = 0; e < 4; ++e) dst[e] = wo[0][e] * inv;
   }
 }
 

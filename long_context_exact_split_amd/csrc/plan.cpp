@@ -290,11 +290,38 @@ attn_status_t check_workspace(size_t need, const void *ws, size_t ws_bytes) {
   return ATTN_OK;
 }
 
+attn_status_t set_workgroups(const attn_desc_t *d, int64_t W, attn_plan_t *p) {
+  if (!p->balanced || W < 1 || W > 65535) return ATTN_ERR_VALUE;
+  const WorkMap shape = work_map(d, *p);
+  const int64_t units = (int64_t)d->batch * seq_units(shape, d->max_kv_len);
+  const int64_t per = (units + W - 1) / W;
+  if (per > std::numeric_limits<int32_t>::max()) return ATTN_ERR_UNSUPPORTED;
+  p->work_items = units > 0 ? W : 0;
+  p->chunk_len = (int32_t)per;
+  const WorkMap m = work_map(d, *p);
+  p->record_slots = record_slots(m);
+  p->workspace_bytes = partial_bytes(p->record_slots * p->rows_per_block, d->head_dim);
+  return ATTN_OK;
+}
+
 attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans *b) {
   bifurcated_descs(d, &b->pre, &b->suf);
   attn_status_t st;
   if ((st = make_plan(&b->pre, cu, kMfmaPlans, &b->pp)) != ATTN_OK) return st;
   if ((st = make_plan(&b->suf, cu, kMfmaPlans, &b->sp)) != ATTN_OK) return st;
+  // One launch for both parts when the prefix takes the shared-tile kernel's
+  // 256-row blocks and the suffix the vector-ALU code: one 8-wave workgroup
+  // per CU, each with a share of both (the shared tiles need one workgroup
+  // per CU anyway).
+  b->fused = b->pp.work_items > 0 && b->sp.work_items > 0 && b->pp.kernel == 2 &&
+             b->pp.rows_per_block == 8 * kMfmaRows && b->sp.kernel == 0 && b->pp.balanced &&
+             b->sp.balanced;
+  b->workgroups = 0;
+  if (b->fused) {
+    b->workgroups = cu;
+    if ((st = set_workgroups(&b->pre, cu, &b->pp)) != ATTN_OK) return st;
+    if ((st = set_workgroups(&b->suf, cu, &b->sp)) != ATTN_OK) return st;
+  }
   b->pre_bytes = (size_t)round_up((int64_t)b->pp.workspace_bytes, 256);
   b->total = b->pre_bytes + b->sp.workspace_bytes;
   return ATTN_OK;

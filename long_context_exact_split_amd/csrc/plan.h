@@ -57,11 +57,19 @@ attn_status_t check_workspace(size_t need, const void *ws, size_t ws_bytes);
 // The shared-prefix call as two decode calls (prefix: one sequence whose
 // query tokens are the samples; suffix: one token per sample) and their
 // plans; the suffix records follow the prefix records in the workspace.
+// fused: both splits run in one launch of `workgroups` workgroups (the
+// prefix on the shared-tile kernel in 256-row blocks, the suffix on the
+// vector-ALU code), each plan rebalanced over that many workgroups.
 struct BifPlans {
   attn_desc_t pre, suf;
   attn_plan_t pp, sp;
   size_t pre_bytes, total;
+  bool fused;
+  int64_t workgroups;
 };
+// A balanced plan re-cut over W workgroups (the record slots and workspace
+// follow).
+attn_status_t set_workgroups(const attn_desc_t *d, int64_t W, attn_plan_t *p);
 attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans *b);
 
 // The anchor-block prefill as two calls over the same rows: the anchor part

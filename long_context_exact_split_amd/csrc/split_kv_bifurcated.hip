@@ -1,0 +1,96 @@
+// One launch for both parts of a shared-prefix batch (Bifurcated Attention,
+// TL;DR: decode attention splits into one contraction over the shared
+// prefix and one over each sample's own decoded KV, with the same flops and
+// far less memory traffic than attending each sample over its own copy).
+//
+// Each workgroup (8 waves, one per CU) takes its share of both parts: a
+// piece of the prefix, where the shared-tile matrix-core code serves the
+// query rows of all samples from every K/V tile (the prefix is read once),
+// and its share of the suffix segments.  A suffix segment is one sample's
+// own decoded KV of one KV head: a few hundred keys for the G query heads of
+// the group.  It runs on the 32-row matrix-core code with only G rows valid:
+// the matrix cores have the capacity to spare, and the dot products and the
+// P.V product leave the vector ALUs only the softmax, where the vector-ALU
+// decode code spends several hundred instructions per 16 keys on segments
+// that short (measured 13-14 us per 512-token segment per CU against
+// about 4 us here).  Half of the workgroups of
+// every XCD run their prefix piece first and the other half their suffix
+// share first, so while some CUs are busy on the matrix cores others keep
+// HBM streaming, instead of a matrix-core phase with HBM half idle followed
+// by a streaming phase with the matrix cores idle.  Both parts write their
+// (m, l, o) records as their own kernels do (work_map.h, one map each, with
+// the launch's workgroup count), and the merge kernel combines them.
+#include "mfma_piece.h"
+
+namespace attn {
+namespace {
+
+constexpr int kBifWaves = 8;  // the shared-tile code's 256-row blocks: 8 waves of 32 rows
+constexpr int kBifThreads = kBifWaves * kWave;
+
+
+template <int D>
+union BifSmem {
+  mfma::RowsSmem<D, kBifWaves, false> pre;
+  mfma::MfmaSmem<D, false, kBifWaves> suf;
+};
+
+template <int D>
+__global__ __launch_bounds__(kBifThreads) void split_kv_bifurcated(SplitArgs pre, SplitArgs suf) {
+  __shared__ BifSmem<D> sh;
+  const int w = blockIdx.x;
+  WorkMap pm = pre.map, sm = suf.map;
+  pm.causal_rows = 0;  // neither part is causal (the launcher checks)
+  sm.causal_rows = 0;
+  auto prefix = [&]() {
+    const int64_t U = total_units(pm);
+    PieceCursor cur = first_piece(pm, U, w);
+    Piece p;
+    while (next_piece(pm, w, cur, &p))
+      mfma::rows_piece<D, kBifWaves, false, false>(pre, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1,
+                                                   p.slot, sh.pre);
+  };
+  auto suffix = [&]() {
+    const int64_t U = total_units(sm);
+    PieceCursor cur = first_piece(sm, U, w);
+    Piece p;
+    while (next_piece(sm, w, cur, &p))
+      mfma::mfma_piece<D, false, false, kBifWaves>(suf, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1,
+                                                  p.slot, sh.suf);
+  };
+  // Workgroup w runs on XCD w % 8; consecutive workgroups of one XCD
+  // alternate the order.  Every piece starts with a workgroup barrier before
+  // it touches the shared memory, so switching parts needs no other.
+  if ((w / 8) & 1) {
+    suffix();
+    prefix();
+  } else {
+    prefix();
+    suffix();
+  }
+}
+
+template <int D>
+hipError_t launch_d(const SplitArgs &pre, const SplitArgs &suf, int64_t wgs, hipStream_t stream) {
+  hipLaunchKernelGGL((split_kv_bifurcated<D>), dim3((unsigned)wgs), dim3(kBifThreads), 0, stream,
+                     pre, suf);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bifurcated(const SplitArgs &pre, const SplitArgs &suf, int head_dim,
+                             int suffix_rows_per_block, int64_t workgroups, hipStream_t stream) {
+  if (workgroups <= 0) return hipSuccess;
+  if (pre.map.causal_rows || suf.map.causal_rows || pre.map.mode != 1 || suf.map.mode != 1 ||
+      pre.map.n_wg != workgroups || suf.map.n_wg != workgroups ||
+      pre.part.rows != mfma::kRows * kBifWaves || suf.map.row_blocks != 1 ||
+      suf.part.rows != suffix_rows_per_block || suf.R > suffix_rows_per_block ||
+      suffix_rows_per_block > mfma::kRows)
+    return hipErrorInvalidValue;
+  if (head_dim == 64) return launch_d<64>(pre, suf, workgroups, stream);
+  if (head_dim == 128) return launch_d<128>(pre, suf, workgroups, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -177,8 +177,12 @@ ATTN_HD int64_t position_of(const WorkMap &m, int64_t L, int64_t rem) {
   return lo;
 }
 
-// Total token units U of the balanced layout.
+// Total token units U of the balanced layout.  Without per-sequence lengths
+// every sequence holds L_max tokens: one product instead of a loop over the
+// batch (a loop of 64-bit arithmetic per sequence costs microseconds on the
+// device for batches of dozens of sequences).
 ATTN_HD int64_t total_units(const WorkMap &m) {
+  if (!m.kv_lens) return (int64_t)m.B * seq_units(m, m.L_max);
   int64_t u = 0;
   for (int b = 0; b < m.B; ++b) u += seq_units(m, seq_len(m, b));
   return u;
@@ -230,6 +234,13 @@ ATTN_HD bool next_piece(const WorkMap &m, int64_t w, PieceCursor &c, Piece *p) {
   if (c.x >= c.xe) return false;
   int64_t L = seq_len(m, c.b);
   int64_t Tk = head_units(m, L);
+  if (!m.kv_lens && c.PB + m.Hkv * Tk <= c.x) {
+    // Equal sequences: jump straight to the one holding unit x.
+    const int64_t per_seq = m.Hkv * Tk;  // > 0 here
+    const int64_t skip = (c.x - c.PB) / per_seq;
+    c.PB += skip * per_seq;
+    c.b += (int32_t)skip;
+  }
   while (c.PB + m.Hkv * Tk <= c.x) {  // skip whole sequences (empty ones included)
     c.PB += m.Hkv * Tk;
     ++c.b;
@@ -288,8 +299,13 @@ ATTN_HD SlotRange segment_slots_at(const WorkMap &m, int64_t U, int64_t PB, int 
 
 ATTN_HD SlotRange segment_slots(const WorkMap &m, int64_t U, int b, int64_t sigma) {
   int64_t PB = 0;
-  if (m.mode != 0)
-    for (int bb = 0; bb < b; ++bb) PB += seq_units(m, seq_len(m, bb));
+  if (m.mode != 0) {
+    if (!m.kv_lens) {
+      PB = (int64_t)b * seq_units(m, m.L_max);
+    } else {
+      for (int bb = 0; bb < b; ++bb) PB += seq_units(m, seq_len(m, bb));
+    }
+  }
   return segment_slots_at(m, U, PB, b, sigma);
 }
 

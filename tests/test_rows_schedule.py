@@ -21,7 +21,7 @@ import re
 import pytest
 
 SRC = os.path.join(os.path.dirname(__file__), "..", "long_context_exact_split_amd", "csrc",
-                   "split_kv_mfma.hip")
+                   "mfma_piece.h")
 
 
 def _constants():
