@@ -78,8 +78,10 @@ typedef enum {
   ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returned     */
   ATTN_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed          */
   ATTN_ERR_UNSUPPORTED = 7, /* head_dim other than 64 or 128, or a shape the kernels do not cover */
-  ATTN_ERR_VALUE = 8        /* non-finite scale, chunk_len not a multiple of 64, or a bad */
+  ATTN_ERR_VALUE = 8,       /* non-finite scale, chunk_len not a multiple of 64, or a bad */
                             /* paging description (page size, strides, table extent)     */
+  ATTN_ERR_SCRATCH = 9      /* attn_decode_static: the call's records exceed the static   */
+                            /* scratch array (ATTN_STATIC_SCRATCH_BYTES)                   */
 } attn_status_t;
 
 typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype_t;
@@ -293,6 +295,24 @@ ATTN_API attn_status_t attn_prefill_anchor(const attn_anchor_desc_t *desc, const
                                   const void *k_blocks, const void *v_blocks, float *o,
                                   float *lse, void *workspace, size_t workspace_bytes,
                                   void *stream);
+
+/* attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The partial records go to a device
+ * array the library holds, ATTN_STATIC_SCRATCH_BYTES bytes on every GPU it
+ * runs on, kept until the process ends; its address is looked up on the
+ * first call on each device.  The call allocates nothing.  Same arguments
+ * (minus the workspace), results and errors as attn_decode, plus
+ * ATTN_ERR_SCRATCH when the call needs more record space than the array
+ * holds (attn_workspace_bytes tells; 16 MiB covers, e.g., the 5.12M-token
+ * GQA decode and a 16-sequence batch of 4-token query blocks over 128K
+ * tokens each).  Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (on different streams, or from different threads
+ * without ordering) race and give wrong results.  Each call writes every
+ * record it reads, so nothing needs clearing between calls. */
+#define ATTN_STATIC_SCRATCH_BYTES (16u << 20)
+ATTN_API attn_status_t attn_decode_static(const attn_desc_t *desc, const void *q, const void *k,
+                                          const void *v, float *o, float *lse, void *stream);
 
 /* Static text for a status code. */
 ATTN_API const char *attn_status_string(attn_status_t status);

@@ -23,12 +23,13 @@ TESTING_LIB_NAME = "libattn_decode_testing.so"
 ATTN_BF16, ATTN_F32 = 0, 1
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
           4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP",
-          7: "ATTN_ERR_UNSUPPORTED", 8: "ATTN_ERR_VALUE"}
+          7: "ATTN_ERR_UNSUPPORTED", 8: "ATTN_ERR_VALUE", 9: "ATTN_ERR_SCRATCH"}
 EXPORTS = ("attn_decode_plan", "attn_workspace_bytes", "attn_decode_energy", "attn_decode",
            "attn_decode_partials", "attn_decode_merge", "attn_decode_energy_zeta",
            "attn_decode_paged", "attn_decode_energy_paged", "attn_decode_partials_paged",
            "attn_bifurcated_workspace_bytes", "attn_decode_bifurcated",
-           "attn_anchor_workspace_bytes", "attn_prefill_anchor", "attn_status_string")
+           "attn_anchor_workspace_bytes", "attn_prefill_anchor", "attn_decode_static",
+           "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -127,6 +128,7 @@ def load_library():
             c.c_size_t, c.c_void_p]
         lib.attn_decode_bifurcated.argtypes = [P(AttnBifDesc)] + [c.c_void_p] * 8 + [
             c.c_size_t, c.c_void_p]
+        lib.attn_decode_static.argtypes = [P(AttnDesc)] + [c.c_void_p] * 6
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = c.c_int
         lib.attn_status_string.argtypes = [c.c_int]
@@ -343,6 +345,26 @@ def decode(q, k, v, kv_lens=None, *, scale: Optional[float] = None, causal: bool
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
         _check(lib.attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                _ptr(lse), _ptr(ws), nbytes, _stream_ptr(q.device)), "attn_decode")
+    return out, lse
+
+
+def decode_static(q, k, v, kv_lens=None, *, scale: Optional[float] = None, causal: bool = False,
+                  chunk_len: int = 0, out=None, lse=None) -> Tuple[object, object]:
+    """attn_decode_static: as decode(), with the partial records in the
+    library's own device array (no workspace; the C call allocates nothing).
+    Calls that overlap on one GPU race on that array."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensors(q, k, v)
+    if v.shape != k.shape:
+        raise ValueError("v must have the shape of k")
+    desc = _decode_desc(q, k, kv_lens, scale, causal, chunk_len)
+    B, q_len, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        out = _output(out, (B, q_len, Hq, D), q.device, "out")
+        lse = _output(lse, (B, q_len, Hq), q.device, "lse")
+        _check(lib.attn_decode_static(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                      _ptr(lse), _stream_ptr(q.device)), "attn_decode_static")
     return out, lse
 
 

@@ -426,6 +426,8 @@ const char *attn_status_string(attn_status_t status) {
     case ATTN_ERR_VALUE: return "invalid scalar: non-finite scale, causal not 0/1, chunk_len "
                                 "not a non-negative multiple of 64, or an invalid paging "
                                 "description";
+    case ATTN_ERR_SCRATCH: return "the call needs more record space than the static scratch "
+                                  "array holds (ATTN_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -433,6 +435,13 @@ const char *attn_status_string(attn_status_t status) {
 }  // extern "C"
 
 namespace attn {
+
+attn_status_t decode_with_workspace(const attn_desc_t *desc, const void *q, const void *k,
+                                    const void *v, float *o, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  return decode_impl(desc, nullptr, q, k, v, nullptr, o, lse, workspace, workspace_bytes, stream,
+                     SplitMode::kFull);
+}
 
 // Anchor-block context encoding: the anchor part as one call over a cache
 // shared by every block (sequence stride 0), the local part as a causal call

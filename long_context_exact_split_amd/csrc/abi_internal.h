@@ -17,4 +17,10 @@ attn_status_t prefill_anchor_impl(const attn_anchor_desc_t *desc, const void *q,
                                   float *lse, void *workspace, size_t workspace_bytes,
                                   void *stream, bool allow_fusion);
 
+// attn_decode on a given workspace (the static-scratch entry point passes
+// the library's own array).
+attn_status_t decode_with_workspace(const attn_desc_t *desc, const void *q, const void *k,
+                                    const void *v, float *o, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 }  // namespace attn
