@@ -138,22 +138,36 @@ __device__ __forceinline__ u32x4 v_to_f16(u32x4 w) {
 // The three parts of one 32-key tile in one wave.
 //
 // qk_tile: S^T = K.Q^T (raw logits), K read from LDS (row pitch KROW).
+// K fragments of a tile (A operand of S^T, one per k-step), read from LDS.
 template <int D>
-__device__ __forceinline__ f32x16_t qk_tile(const uint16_t *ks, const bf16x8_t (&qf)[D / 16]) {
+__device__ __forceinline__ void k_frags(const uint16_t *ks, bf16x8_t (&kf)[D / 16]) {
   using T = Tiles<D>;
   const int lane = threadIdx.x & (kWave - 1);
   const int h = lane >> 5;
   const int j = lane & 31;
+#pragma unroll
+  for (int s = 0; s < T::KS; ++s)
+    kf[s] = __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const u32x4 *>(ks + j * T::KROW + h * (D / 2) + 8 * s));
+}
+
+template <int D>
+__device__ __forceinline__ f32x16_t qk_frags(const bf16x8_t (&kf)[D / 16],
+                                             const bf16x8_t (&qf)[D / 16]) {
   f32x16_t sacc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
 #pragma unroll
-  for (int s = 0; s < T::KS; ++s) {
-    const bf16x8_t kf = __builtin_bit_cast(
-        bf16x8_t, *reinterpret_cast<const u32x4 *>(ks + j * T::KROW + h * (D / 2) + 8 * s));
-    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
-  }
+  for (int s = 0; s < D / 16; ++s)
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
   return sacc;
+}
+
+template <int D>
+__device__ __forceinline__ f32x16_t qk_tile(const uint16_t *ks, const bf16x8_t (&qf)[D / 16]) {
+  bf16x8_t kf[D / 16];
+  k_frags<D>(ks, kf);
+  return qk_frags<D>(kf, qf);
 }
 
 // softmax_tile: masked online softmax of the lane's row over the tile
@@ -285,16 +299,23 @@ union MfmaSmem {
 // One piece: tokens [c0, c1) of KV head kvh of sequence b, for row block rb;
 // writes the piece's record at `slot`: rows r < a.part.rows of the 32
 // (a.part.rows = 32 here, or fewer when a call with fewer query rows per KV
-// head keeps records of that many rows).  WAVES waves take the tiles in turn.
+// head keeps records of that many rows).  WAVES waves take the tiles in turn:
+// threads tbase .. tbase + 64*WAVES - 1 of the workgroup, with shared memory
+// `sh` of their own, so that two groups of waves can run two pieces side by
+// side.  Every call passes the workgroup barriers the same number of times
+// (three), so such groups stay in step; write = false runs a piece without
+// writing its record (a group with no piece of its own takes an empty one).
 template <int D, bool ENERGY, bool PAGED, int WAVES = kWaves>
 __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, int rb, int c0,
                                            int c1, int64_t slot,
-                                           MfmaSmem<D, ENERGY, WAVES> &sh) {
+                                           MfmaSmem<D, ENERGY, WAVES> &sh, int tbase = 0,
+                                           bool write = true) {
   using T = Tiles<D>;
   constexpr int LPK = T::LPK, KPI = T::KPI, NL = T::NL, KS = T::KS, NT = T::NT;
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int tid = (int)threadIdx.x - tbase;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int h = lane >> 5;   // lane half
   const int j = lane & 31;   // query row owned by this lane (and key slot in A layouts)
   const int Lb = (int)seq_len(a.map, b);
@@ -416,7 +437,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
   const int rows_out = a.part.rows;  // <= kRows
   const int64_t rec0 = slot * rows_out;
   const int n_out = ENERGY ? rows_out : rows_out * D;
-  for (int idx = threadIdx.x; idx < n_out; idx += WAVES * kWave) {
+  for (int idx = tid; write && idx < n_out; idx += WAVES * kWave) {
     const int r = ENERGY ? idx : idx / D;
     const int d = ENERGY ? 0 : idx - r * D;
     float M = -INFINITY;
@@ -713,26 +734,34 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
 #pragma unroll
   for (int off = 1; off < kWave; off *= 2) wave_lim = min(wave_lim, __shfl_xor(wave_lim, off));
   const int full = (wave_lim - c0) / kTile;
-  // The matrix and vector work of one iteration, interleaved: the LDS reads
-  // of both products first, then each MFMA followed by a few VALU
-  // instructions of the softmax (the sched_group_barrier sequence fixes this
-  // order within the iteration's basic block).
+  // The matrix and vector work of one iteration, interleaved: all eight K
+  // fragment reads of S^T first (S^T is a chain of dependent MFMAs; with each
+  // read issued just before its MFMA, every link waited out a whole LDS
+  // latency), then each MFMA followed by a few VALU instructions of the
+  // softmax, the V reads two at a time behind the MFMAs (the
+  // sched_group_barrier sequence fixes this order within the iteration).
   // PAR = tile % 2: S^T of tile + 2 replaces that of tile (consumed by the
   // previous iteration's softmax), so the two S^T registers alternate roles
   // with no copy between iterations.
   auto body = [&](int tile, auto par, auto mask) {
     constexpr int PAR = decltype(par)::value;
     constexpr int MASK = decltype(mask)::value;
+    bf16x8_t kf[KS];
+    k_frags<D>(kbuf(tile + 2), kf);
     if constexpr (!ENERGY) pv_tile<D>(vbuf(tile), pf, oacc);
-    sbuf[PAR] = qk_tile<D>(kbuf(tile + 2), qf);
+    sbuf[PAR] = qk_frags<D>(kf, qf);
     pend = softmax_tile<ENERGY, MASK>(sbuf[1 - PAR], c0 + (tile + 1) * kTile, lim, scale_log2,
                                       m, lsum, pf);
-    constexpr int kMfma = (ENERGY ? 0 : 2 * NT) + KS;
-    __builtin_amdgcn_sched_group_barrier(0x100, ENERGY ? 2 : 4, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // the K reads
 #pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an LDS read for a later one
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an S^T MFMA
+      if constexpr (!ENERGY) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
+    }
+#pragma unroll
+    for (int i = 0; i < (ENERGY ? 0 : 2 * NT); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a P.V MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
     }
   };

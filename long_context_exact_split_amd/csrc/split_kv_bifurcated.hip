@@ -6,7 +6,7 @@
 // Each workgroup (8 waves, one per CU) takes its share of both parts: a
 // piece of the prefix, where the shared-tile matrix-core code serves the
 // query rows of all samples from every K/V tile (the prefix is read once),
-// and its share of the suffix segments.  A suffix segment is one sample's
+// and its share of the suffix segments, two at a time (four waves each).  A suffix segment is one sample's
 // own decoded KV of one KV head: a few hundred keys for the G query heads of
 // the group.  It runs on the 32-row matrix-core code with only G rows valid:
 // the matrix cores have the capacity to spare, and the dot products and the
@@ -29,10 +29,15 @@ constexpr int kBifWaves = 8;  // the shared-tile code's 256-row blocks: 8 waves 
 constexpr int kBifThreads = kBifWaves * kWave;
 
 
+// The suffix runs as two groups of four waves, each on a segment of its own
+// (a segment's pieces carry a latency chain of their own: query loads, the
+// first tiles, the epilogue; two in flight overlap them).
+constexpr int kSufWaves = kBifWaves / 2;
+
 template <int D>
 union BifSmem {
   mfma::RowsSmem<D, kBifWaves, false> pre;
-  mfma::MfmaSmem<D, false, kBifWaves> suf;
+  mfma::MfmaSmem<D, false, kSufWaves> suf[2];
 };
 
 template <int D>
@@ -53,10 +58,18 @@ __global__ __launch_bounds__(kBifThreads) void split_kv_bifurcated(SplitArgs pre
   auto suffix = [&]() {
     const int64_t U = total_units(sm);
     PieceCursor cur = first_piece(sm, U, w);
-    Piece p;
-    while (next_piece(sm, w, cur, &p))
-      mfma::mfma_piece<D, false, false, kBifWaves>(suf, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1,
-                                                  p.slot, sh.suf);
+    const int grp = threadIdx.x / (kSufWaves * kWave);  // wave-uniform: 0 or 1
+    Piece p[2];
+    // Pieces two at a time, one per group; with an odd count the second
+    // group runs an empty piece (same barriers, nothing written).
+    while (next_piece(sm, w, cur, &p[0])) {
+      const bool two = next_piece(sm, w, cur, &p[1]);
+      const bool mine = grp == 0 || two;
+      const Piece &q = mine ? p[grp] : p[0];
+      mfma::mfma_piece<D, false, false, kSufWaves>(suf, q.b, q.kvh, q.rb, (int)q.t0,
+                                                  mine ? (int)q.t1 : (int)q.t0, q.slot,
+                                                  sh.suf[grp], grp * kSufWaves * kWave, mine);
+    }
   };
   // Workgroup w runs on XCD w % 8; consecutive workgroups of one XCD
   // alternate the order.  Every piece starts with a workgroup barrier before
