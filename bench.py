@@ -115,6 +115,10 @@ def parse(argv=None):
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="extra calls after the timed steps, each behind a 1 GiB read that "
                          "evicts L2 and the Infinity Cache (0: skip)")
+    ap.add_argument("--wg-stamps", type=int, default=0, metavar="REPS",
+                    help="instead of the bench line: time every workgroup of the vector-ALU "
+                         "split kernel (start, end, XCD) over REPS launches with the "
+                         "stamping build of the library, and print a per-XCD summary")
     return ap.parse_args(argv)
 
 
@@ -735,18 +739,96 @@ def measure_config(torch, name, K, n_rows, warmup, min_warmup_s):
     return rec
 
 
+def stamp_summary(st, ev_ms):
+    """Per-workgroup stamps of one launch ([n, 4]: start, end, XCC id, HW id;
+    clocks in 10 ns ticks) -> summary dict (microseconds)."""
+    import numpy as np
+    t0, t1 = st[:, 0].astype(np.int64), st[:, 1].astype(np.int64)
+    base = t0.min()
+    start, end, dur = (t0 - base) * 0.01, (t1 - base) * 0.01, (t1 - t0) * 0.01
+    xcc = (st[:, 2] & 0xF).astype(np.int64)
+    per = {}
+    for x in sorted(set(xcc.tolist())):
+        sel = xcc == x
+        per[str(x)] = {"workgroups": int(sel.sum()),
+                       "end_median_us": float(np.median(end[sel])),
+                       "end_max_us": float(end[sel].max()),
+                       "duration_median_us": float(np.median(dur[sel])),
+                       "duration_spread_us": float(dur[sel].max() - dur[sel].min())}
+    ends = np.array([v["end_max_us"] for v in per.values()])
+    span = float(end.max())
+    return {"event_us": ev_ms * 1e3, "span_us": span,
+            "start_spread_us": float(start.max()),
+            "duration_min_med_max_us": [float(dur.min()), float(np.median(dur)), float(dur.max())],
+            "xcd_end_min_max_us": [float(ends.min()), float(ends.max())],
+            # if the work had been shared out in proportion to each XCD's own rate
+            "balanced_span_us": float(len(ends) / np.sum(1.0 / ends)),
+            "xcd": per}
+
+
+def wg_stamps(torch, args):
+    """Per-workgroup timing of the headline split kernel: after the warm-up,
+    REPS launches each following an idle gap (isolated) and, after a run of
+    back-to-back steps, the last of them (sustained)."""
+    import ctypes
+    import numpy as np
+    from long_context_exact_split_amd import binding
+    lib = binding.load_library()
+    if not hasattr(lib, "attn_probe_wg_stamps"):
+        raise RuntimeError(f"{binding.library_path()} is not the stamping build")
+    lib.attn_probe_wg_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    run = make_runner(torch, args.workload, args.page_size)
+    if run.plan["kernel"] != 0 or getattr(run, "mode", "full") == "zeta":
+        raise RuntimeError("--wg-stamps covers the vector-ALU split kernel's decode workloads")
+    n = int(run.plan["work_items"])
+    stream = torch.cuda.current_stream()
+
+    def launch_and_read(back_to_back):
+        for _ in range(back_to_back):
+            run.first()
+            run.second()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run.first()
+        b.record(stream)
+        torch.cuda.synchronize()
+        st = np.zeros((n, 4), dtype=np.uint64)
+        if lib.attn_probe_wg_stamps(st.ctypes.data, n) != 0:
+            raise RuntimeError("attn_probe_wg_stamps failed")
+        run.second()
+        torch.cuda.synchronize()
+        return stamp_summary(st, a.elapsed_time(b))
+
+    timed_steps(torch, run, 20, args.warmup, args.min_warmup_s)
+    out = {"workload": WORKLOADS[args.workload], "kernel": run.kernel, "workgroups": n,
+           "library": os.path.basename(binding.library_path()), "isolated": [], "sustained": []}
+    for rep in range(args.wg_stamps):
+        time.sleep(0.005)
+        out["isolated"].append(launch_and_read(0))
+        out["sustained"].append(launch_and_read(100))
+        print(f"# rep {rep}: isolated {out['isolated'][-1]['event_us']:.1f} us, sustained "
+              f"{out['sustained'][-1]['event_us']:.1f} us", file=sys.stderr, flush=True)
+    print(json.dumps(out))
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1 "
                                    "(sharding the KV cache across GPUs is not implemented)"}))
         sys.exit(2)
+    if args.wg_stamps > 0:
+        from long_context_exact_split_amd import build
+        os.environ["ATTN_LIB"] = os.path.join(build.PKG, build.STAMPS_LIB_NAME)
     import torch
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.wg_stamps > 0:
+        wg_stamps(torch, args)
+        return
     t_gen = time.perf_counter()
     w = make_workload(args.workload)
     print(f"# generated {args.workload} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,

@@ -62,6 +62,15 @@ ATTN_API attn_status_t attn_testing_check_decode(const attn_desc_t *desc,
 ATTN_API attn_status_t attn_testing_check_bifurcated(const attn_bifurcated_desc_t *desc,
                                                      int32_t cu_count, size_t *workspace_bytes);
 
+/* How attn_decode_bifurcated would launch on cu_count CUs: *prefix_wgs and
+ * *suffix_wgs are the workgroup counts of the two parts' work maps.  One
+ * launch of both parts: their sum is cu_count when the CUs are split between
+ * them, both are cu_count when every workgroup takes a share of both; two
+ * separate split launches: *fused = 0. */
+ATTN_API attn_status_t attn_testing_bifurcated_form(const attn_bifurcated_desc_t *desc,
+                                                   int32_t cu_count, int32_t *fused,
+                                                   int64_t *prefix_wgs, int64_t *suffix_wgs);
+
 /* attn_prefill_anchor always on its three-launch path (anchor split, local
  * split, merge), whatever the shape; arguments, results and errors as
  * attn_prefill_anchor.  For comparing the two paths in tests. */

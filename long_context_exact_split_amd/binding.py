@@ -89,7 +89,10 @@ _lock = threading.Lock()
 
 
 def library_path() -> str:
-    return os.path.join(PKG, LIB_NAME)
+    """The product library next to this file; ATTN_LIB names another build of
+    it (the bench's per-workgroup timing build), which must export the same
+    entry points."""
+    return os.environ.get("ATTN_LIB") or os.path.join(PKG, LIB_NAME)
 
 
 def load_library():
@@ -163,6 +166,9 @@ def load_testing_library():
         lib.attn_testing_check_decode.restype = c.c_int
         lib.attn_testing_check_bifurcated.argtypes = [P(AttnBifDesc), c.c_int32, P(c.c_size_t)]
         lib.attn_testing_check_bifurcated.restype = c.c_int
+        lib.attn_testing_bifurcated_form.argtypes = [P(AttnBifDesc), c.c_int32, P(c.c_int32),
+                                                     P(c.c_int64), P(c.c_int64)]
+        lib.attn_testing_bifurcated_form.restype = c.c_int
         if hasattr(lib, "attn_testing_prefill_anchor_unfused"):  # absent in host-only builds
             lib.attn_testing_prefill_anchor_unfused.argtypes = [P(AttnAnchorDesc)] + [
                 c.c_void_p] * 8 + [c.c_size_t, c.c_void_p]

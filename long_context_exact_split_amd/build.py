@@ -22,6 +22,11 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libattn_decode.so"
 TESTING_LIB_NAME = "libattn_decode_testing.so"
 PROBE_NAME = "libhbm_probe.so"  # HBM read-stream / copy reference kernels
+# The product library with the vector-ALU split kernel built to record each
+# workgroup's start and end clocks and XCD (csrc/probe/wg_stamps.h); loaded
+# only by the bench's --wg-stamps measurement.
+STAMPS_LIB_NAME = "libattn_decode_stamps.so"
+STAMPED_SOURCE = "split_kv_valu.hip"
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
@@ -40,11 +45,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + DEFINES
+def _compile(src: str, verbose: bool, extra=(), suffix: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + suffix + ".o")
+    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + DEFINES + list(extra)
     if src.endswith(".hip"):
-        cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + HIP_ONLY + COMMON + DEFINES
+        cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + HIP_ONLY + COMMON + DEFINES + \
+            list(extra)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -82,11 +88,17 @@ def build(verbose: bool = False, out_dir: str = PKG, build_dir: str = BUILD) -> 
     srcs = sources()
     tsrcs = testing_sources()
     probe = os.path.join(CSRC, "probe", "hbm_probe.hip")
+    stamped = os.path.join(CSRC, STAMPED_SOURCE)
+    jobs = [(s, (), "") for s in srcs + tsrcs + [probe]]
+    jobs.append((stamped, ("-DATTN_WG_STAMPS",), ".stamps"))
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + tsrcs + [probe]))
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1], j[2]), jobs))
     lib_objs, test_objs = objs[:len(srcs)], objs[len(srcs):len(srcs) + len(tsrcs)]
-    _link(objs[-1:], PROBE_NAME, verbose, out_dir)
+    probe_obj, stamped_obj = objs[-2], objs[-1]
+    _link([probe_obj], PROBE_NAME, verbose, out_dir)
     _link(lib_objs + test_objs, TESTING_LIB_NAME, verbose, out_dir)
+    _link([stamped_obj if os.path.basename(s) == STAMPED_SOURCE else o
+           for s, o in zip(srcs, lib_objs)], STAMPS_LIB_NAME, verbose, out_dir)
     return _link(lib_objs, LIB_NAME, verbose, out_dir)
 
 

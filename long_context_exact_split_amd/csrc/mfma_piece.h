@@ -472,6 +472,12 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
 // of its first use a tile is stored into them (one barrier per two tiles).
 constexpr int kRowsBufs = 6;
 constexpr int kStoreAhead = 4;
+#ifndef ATTN_ROWS_RING
+#define ATTN_ROWS_RING 2        // register ring stages with eight waves (3: 1% slower)
+#endif
+#ifndef ATTN_ROWS_VALU_PER_MFMA
+#define ATTN_ROWS_VALU_PER_MFMA 5  // softmax VALU instructions placed after each MFMA
+#endif
 
 template <int D, int RW, bool ENERGY>
 union RowsSmem {
@@ -637,7 +643,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   // Tiles in flight: a ring of NS register stages (tile t lives in stage
   // t % NS) feeding the LDS tile buffers.  Stage indices are compile-time
   // inside the unrolled inner loop, so the ring stays in registers.
-  constexpr int NS = RW >= 8 ? 3 : (RW >= 4 ? 2 : 1);
+  constexpr int NS = RW >= 8 ? ATTN_ROWS_RING : (RW >= 4 ? 2 : 1);
   constexpr int SA = kStoreAhead;
   u32x4 kr[NS][PER], vr[NS][ENERGY ? 1 : PER];
   // Token of this thread's copy piece i of a tile (clamped to a valid row).
@@ -757,12 +763,12 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
     for (int i = 0; i < KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an S^T MFMA
       if constexpr (!ENERGY) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, ATTN_ROWS_VALU_PER_MFMA, 0);  // softmax VALU
     }
 #pragma unroll
     for (int i = 0; i < (ENERGY ? 0 : 2 * NT); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a P.V MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, ATTN_ROWS_VALU_PER_MFMA, 0);  // softmax VALU
     }
   };
   // U iterations per unrolled round: a multiple of NS (ring stages), of the

@@ -304,6 +304,41 @@ attn_status_t set_workgroups(const attn_desc_t *d, int64_t W, attn_plan_t *p) {
   return ATTN_OK;
 }
 
+// Workgroups of the one-launch shared-prefix kernel given to the prefix alone,
+// in eighths of the launch: -1 = from the cost estimate below, 0 = every
+// workgroup takes a share of both parts.
+#ifndef ATTN_BIF_PREFIX_EIGHTHS
+#define ATTN_BIF_PREFIX_EIGHTHS -1
+#endif
+
+// How many of W workgroups should run the prefix (the rest run the suffix),
+// or 0 for a share of both in every workgroup.  The prefix is matrix-core
+// work and the suffix a stream from HBM, so the two run side by side on
+// different CUs; the split follows their times on the whole GPU: 4·D flops
+// per (query row, prefix key) at the shared-tile kernel's rate, against the
+// suffix bytes at the decode kernels' rate.  The kernels measured here run
+// about 128 flops in the time they stream one byte (0.9 PFLOP/s against
+// 7 TB/s).  Rounded to whole rounds of the eight XCDs; a part that would get
+// less than one round, or more than all but one, leaves the shared form.
+int64_t bifurcated_prefix_workgroups(const attn_bifurcated_desc_t *d, int64_t W) {
+  if (ATTN_BIF_PREFIX_EIGHTHS == 0 || W < 16) return 0;
+  if (ATTN_BIF_PREFIX_EIGHTHS > 0) {
+    const int64_t wp = W * ATTN_BIF_PREFIX_EIGHTHS / 8;
+    return wp - wp % 8;
+  }
+  constexpr double kFlopsPerByte = 128.0;
+  const double esz = d->dtype == ATTN_BF16 ? 2.0 : 4.0;
+  const double rows = (double)d->num_samples * d->num_q_heads;  // every (sample, query head)
+  const double pre_flops = 4.0 * d->head_dim * rows * (double)d->prefix_len;
+  const double suf_bytes =
+      2.0 * esz * d->head_dim * (double)d->num_samples * d->num_kv_heads * (double)d->suffix_len;
+  const double tp = pre_flops / kFlopsPerByte, ts = suf_bytes;
+  if (!(tp > 0.0) || !(ts > 0.0)) return 0;
+  int64_t wp = (int64_t)(tp / (tp + ts) * (double)W / 8.0 + 0.5) * 8;
+  if (wp < 8 || wp > W - 8) return 0;
+  return wp;
+}
+
 attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans *b) {
   bifurcated_descs(d, &b->pre, &b->suf);
   attn_status_t st;
@@ -311,16 +346,19 @@ attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans
   if ((st = make_plan(&b->suf, cu, kMfmaPlans, &b->sp)) != ATTN_OK) return st;
   // One launch for both parts when the prefix takes the shared-tile kernel's
   // 256-row blocks and the suffix the vector-ALU code: one 8-wave workgroup
-  // per CU, each with a share of both (the shared tiles need one workgroup
-  // per CU anyway).
+  // per CU (the shared tiles need one workgroup per CU anyway), the CUs split
+  // between the parts by bifurcated_prefix_workgroups, or each workgroup
+  // with a share of both.
   b->fused = b->pp.work_items > 0 && b->sp.work_items > 0 && b->pp.kernel == 2 &&
              b->pp.rows_per_block == 8 * kMfmaRows && b->sp.kernel == 0 && b->pp.balanced &&
              b->sp.balanced;
   b->workgroups = 0;
   if (b->fused) {
     b->workgroups = cu;
-    if ((st = set_workgroups(&b->pre, cu, &b->pp)) != ATTN_OK) return st;
-    if ((st = set_workgroups(&b->suf, cu, &b->sp)) != ATTN_OK) return st;
+    int64_t wp = bifurcated_prefix_workgroups(d, cu), ws = cu - wp;
+    if (wp == 0) wp = ws = cu;  // shared form: every workgroup both parts
+    if ((st = set_workgroups(&b->pre, wp, &b->pp)) != ATTN_OK) return st;
+    if ((st = set_workgroups(&b->suf, ws, &b->sp)) != ATTN_OK) return st;
   }
   b->pre_bytes = (size_t)round_up((int64_t)b->pp.workspace_bytes, 256);
   b->total = b->pre_bytes + b->sp.workspace_bytes;

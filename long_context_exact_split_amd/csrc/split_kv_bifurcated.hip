@@ -3,23 +3,25 @@
 // prefix and one over each sample's own decoded KV, with the same flops and
 // far less memory traffic than attending each sample over its own copy).
 //
-// Each workgroup (8 waves, one per CU) takes its share of both parts: a
-// piece of the prefix, where the shared-tile matrix-core code serves the
-// query rows of all samples from every K/V tile (the prefix is read once),
-// and its share of the suffix segments, two at a time (four waves each).  A suffix segment is one sample's
+// One workgroup of 8 waves per CU.  The prefix runs on the shared-tile
+// matrix-core code, which serves the query rows of all samples from every
+// K/V tile (the prefix is read once); the suffix segments run two at a time
+// (four waves each).  The planner either splits the CUs between the two
+// parts (the first workgroups take prefix pieces, the others suffix
+// segments: matrix-core work on some CUs while the others stream from HBM),
+// or gives every workgroup a share of both.  A suffix segment is one sample's
 // own decoded KV of one KV head: a few hundred keys for the G query heads of
 // the group.  It runs on the 32-row matrix-core code with only G rows valid:
 // the matrix cores have the capacity to spare, and the dot products and the
 // P.V product leave the vector ALUs only the softmax, where the vector-ALU
 // decode code spends several hundred instructions per 16 keys on segments
 // that short (measured 13-14 us per 512-token segment per CU against
-// about 4 us here).  Half of the workgroups of
-// every XCD run their prefix piece first and the other half their suffix
-// share first, so while some CUs are busy on the matrix cores others keep
-// HBM streaming, instead of a matrix-core phase with HBM half idle followed
-// by a streaming phase with the matrix cores idle.  Both parts write their
-// (m, l, o) records as their own kernels do (work_map.h, one map each, with
-// the launch's workgroup count), and the merge kernel combines them.
+// about 4 us here).  In the shared form half of the workgroups of every XCD
+// run their prefix piece first and the other half their suffix share first,
+// so that there too some CUs are busy on the matrix cores while others keep
+// HBM streaming.  Both parts write their (m, l, o) records as their own
+// kernels do (work_map.h, one map each, with the workgroup count of its
+// part), and the merge kernel combines them.
 #include "mfma_piece.h"
 
 namespace attn {
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kBifThreads) void split_kv_bifurcated(SplitArgs pre
   WorkMap pm = pre.map, sm = suf.map;
   pm.causal_rows = 0;  // neither part is causal (the launcher checks)
   sm.causal_rows = 0;
-  auto prefix = [&]() {
+  auto prefix = [&](int w) __attribute__((always_inline)) {
     const int64_t U = total_units(pm);
     PieceCursor cur = first_piece(pm, U, w);
     Piece p;
@@ -55,32 +57,38 @@ __global__ __launch_bounds__(kBifThreads) void split_kv_bifurcated(SplitArgs pre
       mfma::rows_piece<D, kBifWaves, false, false>(pre, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1,
                                                    p.slot, sh.pre);
   };
-  auto suffix = [&]() {
+  auto suffix = [&](int w) __attribute__((always_inline)) {
     const int64_t U = total_units(sm);
     PieceCursor cur = first_piece(sm, U, w);
     const int grp = threadIdx.x / (kSufWaves * kWave);  // wave-uniform: 0 or 1
-    Piece p[2];
+    Piece p0, p1;
     // Pieces two at a time, one per group; with an odd count the second
-    // group runs an empty piece (same barriers, nothing written).
-    while (next_piece(sm, w, cur, &p[0])) {
-      const bool two = next_piece(sm, w, cur, &p[1]);
+    // group runs an empty piece (same barriers, nothing written).  The
+    // group's piece is picked field by field (indexing an array of the two
+    // by the group would put it in scratch memory).
+    while (next_piece(sm, w, cur, &p0)) {
+      const bool two = next_piece(sm, w, cur, &p1);
+      const bool second = grp == 1 && two;  // this group takes p1
       const bool mine = grp == 0 || two;
-      const Piece &q = mine ? p[grp] : p[0];
-      mfma::mfma_piece<D, false, false, kSufWaves>(suf, q.b, q.kvh, q.rb, (int)q.t0,
-                                                  mine ? (int)q.t1 : (int)q.t0, q.slot,
-                                                  sh.suf[grp], grp * kSufWaves * kWave, mine);
+      const int t0 = (int)(second ? p1.t0 : p0.t0);
+      mfma::mfma_piece<D, false, false, kSufWaves>(
+          suf, second ? p1.b : p0.b, second ? p1.kvh : p0.kvh, second ? p1.rb : p0.rb, t0,
+          mine ? (int)(second ? p1.t1 : p0.t1) : t0, second ? p1.slot : p0.slot, sh.suf[grp],
+          grp * kSufWaves * kWave, mine);
     }
   };
   // Workgroup w runs on XCD w % 8; consecutive workgroups of one XCD
   // alternate the order.  Every piece starts with a workgroup barrier before
   // it touches the shared memory, so switching parts needs no other.
-  if ((w / 8) & 1) {
-    suffix();
-    prefix();
-  } else {
-    prefix();
-    suffix();
-  }
+  // Split launches (the two maps' workgroup counts add up to the grid) give
+  // each workgroup one part: the first pm.n_wg the prefix, the rest the
+  // suffix.  Otherwise every workgroup takes a share of both.
+  const bool split = pm.n_wg + sm.n_wg == (int)gridDim.x;
+  const bool suffix_first = !split && ((w / 8) & 1);
+  const int ws = split ? w - pm.n_wg : w;  // index in the suffix map
+  if (suffix_first) suffix(ws);
+  if (!split || w < pm.n_wg) prefix(w);
+  if (!suffix_first && (!split || w >= pm.n_wg)) suffix(ws);
 }
 
 template <int D>
@@ -96,7 +104,8 @@ hipError_t launch_bifurcated(const SplitArgs &pre, const SplitArgs &suf, int hea
                              int suffix_rows_per_block, int64_t workgroups, hipStream_t stream) {
   if (workgroups <= 0) return hipSuccess;
   if (pre.map.causal_rows || suf.map.causal_rows || pre.map.mode != 1 || suf.map.mode != 1 ||
-      pre.map.n_wg != workgroups || suf.map.n_wg != workgroups ||
+      !((pre.map.n_wg == workgroups && suf.map.n_wg == workgroups) ||
+        (pre.map.n_wg > 0 && suf.map.n_wg > 0 && pre.map.n_wg + suf.map.n_wg == workgroups)) ||
       pre.part.rows != mfma::kRows * kBifWaves || suf.map.row_blocks != 1 ||
       suf.part.rows != suffix_rows_per_block || suf.R > suffix_rows_per_block ||
       suffix_rows_per_block > mfma::kRows)

@@ -28,6 +28,12 @@
 #include "kernels.h"
 #include "kv_rows.h"
 
+#ifdef ATTN_WG_STAMPS
+#include "probe/wg_stamps.h"  // per-workgroup clocks: measurement builds only
+#else
+#define ATTN_WG_STAMP()
+#endif
+
 namespace attn {
 namespace {
 
@@ -497,6 +503,7 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
 
 template <typename T, int D, int RB, int KT, SplitMode MODE, bool PAGED>
 __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
+  ATTN_WG_STAMP();
   __shared__ ValuSmem<D, RB, MODE != SplitMode::kFull> sh;
   WorkMap m = a.map;
   m.causal_rows = 0;  // never set for this kernel's maps (the launcher checks)

@@ -128,4 +128,26 @@ attn_status_t attn_testing_check_bifurcated(const attn_bifurcated_desc_t *desc, 
   }
 }
 
+attn_status_t attn_testing_bifurcated_form(const attn_bifurcated_desc_t *desc, int32_t cu_count,
+                                           int32_t *fused, int64_t *prefix_wgs,
+                                           int64_t *suffix_wgs) {
+  try {
+    attn_status_t st = validate_bifurcated(desc);
+    if (st != ATTN_OK) return st;
+    if (!fused || !prefix_wgs || !suffix_wgs) return ATTN_ERR_NULL;
+    *fused = 0;
+    *prefix_wgs = *suffix_wgs = 0;
+    if (desc->num_samples == 0) return ATTN_OK;
+    if (cu_count < 1) return ATTN_ERR_VALUE;
+    BifPlans b;
+    if ((st = bifurcated_plans(desc, cu_count, &b)) != ATTN_OK) return st;
+    *fused = b.fused ? 1 : 0;
+    *prefix_wgs = work_map(&b.pre, b.pp).n_wg;
+    *suffix_wgs = work_map(&b.suf, b.sp).n_wg;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
 }  // extern "C"

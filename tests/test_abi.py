@@ -71,6 +71,18 @@ def test_testing_library_exports_its_hooks_and_the_boundary(lib):
     assert exported == set(all_declared_functions()), sorted(exported ^ set(all_declared_functions()))
 
 
+def test_stamping_build_exports_the_boundary_and_its_probe(lib):
+    """The bench's per-workgroup timing build: the same boundary plus the
+    stamp read-back, which the product library does not have."""
+    from long_context_exact_split_amd import build
+    path = os.path.join(build.PKG, build.STAMPS_LIB_NAME)
+    if not os.path.exists(path):
+        pytest.skip("stamping build not built")
+    exported = exported_functions(path)
+    assert exported == set(declared_functions()) | {"attn_probe_wg_stamps"}
+    assert "attn_probe_wg_stamps" not in exported_functions(binding.library_path())
+
+
 def test_struct_layouts_match_c(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text("""

@@ -4,6 +4,8 @@ Small shapes are compared on every output; the full-size workloads are
 compared on every row the oracle can afford (all rows for the 8B-shaped GQA
 decode and the bifurcated batch; sampled KV-head groups for the 5.12M-token
 cache and the 70B-shaped ragged batch)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -559,6 +561,35 @@ def test_graph_replays_match_eager_calls():
         torch.cuda.synchronize()
         assert torch.equal(ph.out, O0) and torch.equal(ph.lse, lse0), f"decode, replay {rep}"
         assert torch.equal(bc.out, Ob0) and torch.equal(bc.lse, lseb0), f"bifurcated, replay {rep}"
+
+
+# The one-launch shared-prefix kernel in each of its forms (64 samples x 4
+# query heads per KV head: the prefix takes 256-row blocks): CUs split with
+# most on the prefix, CUs split with most on the suffix, and every workgroup
+# on both parts (a suffix too short to be worth a round of the XCDs).
+BIF_FORMS = [("split_prefix_heavy", 4096, 8), ("split_suffix_heavy", 1024, 1024),
+             ("shared", 4096, 2)]
+
+
+@pytest.mark.parametrize("form,Lp,Ls", BIF_FORMS, ids=[f[0] for f in BIF_FORMS])
+def test_bifurcated_forms(form, Lp, Ls):
+    say(f"bifurcated form {form} Lp={Lp} Ls={Ls}")
+    w = inputs.bifurcated_prefix(seed=47 + Ls, Lp=Lp, Ls=Ls)
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    lib = binding.load_testing_library()
+    d = binding.AttnBifDesc(num_samples=w.S, num_q_heads=w.Hq, num_kv_heads=w.Hkv,
+                            head_dim=w.D, prefix_len=Lp, suffix_len=Ls, scale=w.scale, dtype=0)
+    f, p, s = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    assert lib.attn_testing_bifurcated_form(ctypes.byref(d), cu, ctypes.byref(f), ctypes.byref(p),
+                                            ctypes.byref(s)) == 0
+    assert f.value == 1
+    if form == "shared":
+        assert p.value == s.value == cu
+    else:
+        assert p.value + s.value == cu and (p.value > s.value) == (form == "split_prefix_heavy")
+    O, lse = run_bifurcated(w)
+    Or, lr = oracle.attend_bifurcated(w.q, w.kp, w.vp, w.ks, w.vs, w.scale)
+    check_rows(O[:, None], lse[:, None], Or[:, None], lr[:, None], what=f"bifurcated {form}")
 
 
 def test_bifurcated_full_size():
