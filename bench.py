@@ -769,7 +769,8 @@ def stamp_summary(st, ev_ms):
 def wg_stamps(torch, args):
     """Per-workgroup timing of the headline split kernel: after the warm-up,
     REPS launches each following an idle gap (isolated) and, after a run of
-    back-to-back steps, the last of them (sustained)."""
+    back-to-back steps, the last of them (sustained); then the same for the
+    reference share-read kernel over the same bytes and workgroups."""
     import ctypes
     import numpy as np
     from long_context_exact_split_amd import binding
@@ -808,6 +809,39 @@ def wg_stamps(torch, args):
         out["sustained"].append(launch_and_read(100))
         print(f"# rep {rep}: isolated {out['isolated'][-1]['event_us']:.1f} us, sustained "
               f"{out['sustained'][-1]['event_us']:.1f} us", file=sys.stderr, flush=True)
+
+    # The same bytes read by the reference share-read kernel (the decode's
+    # access pattern without its arithmetic) over as many workgroups.
+    from long_context_exact_split_amd import hbm_probe
+    probe = hbm_probe.load()
+    nbytes = run.kv_bytes // 16 * 16
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
+    sink = torch.zeros(n, dtype=torch.int32, device="cuda")
+
+    def read_and_stamp(back_to_back):
+        for _ in range(back_to_back + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            if probe.hbm_read_share_probe(src.data_ptr(), nbytes, sink.data_ptr(), n,
+                                          stream.cuda_stream) != 0:
+                raise RuntimeError("hbm_read_share_probe failed")
+            b.record(stream)
+        torch.cuda.synchronize()
+        st = np.zeros((n, 4), dtype=np.uint64)
+        if probe.attn_probe_wg_stamps(st.ctypes.data, n) != 0:
+            raise RuntimeError("attn_probe_wg_stamps (probe) failed")
+        return stamp_summary(st, a.elapsed_time(b))
+
+    out["read_share"] = {"bytes": nbytes, "isolated": [], "sustained": []}
+    read_and_stamp(30)
+    for rep in range(args.wg_stamps):
+        time.sleep(0.005)
+        out["read_share"]["isolated"].append(read_and_stamp(0))
+        out["read_share"]["sustained"].append(read_and_stamp(100))
+        print(f"# read_share rep {rep}: isolated "
+              f"{out['read_share']['isolated'][-1]['event_us']:.1f} us, sustained "
+              f"{out['read_share']['sustained'][-1]['event_us']:.1f} us", file=sys.stderr,
+              flush=True)
     print(json.dumps(out))
 
 
@@ -819,7 +853,7 @@ def main(argv=None):
         sys.exit(2)
     if args.wg_stamps > 0:
         from long_context_exact_split_amd import build
-        os.environ["ATTN_LIB"] = os.path.join(build.PKG, build.STAMPS_LIB_NAME)
+        os.environ.setdefault("ATTN_LIB", os.path.join(build.PKG, build.STAMPS_LIB_NAME))
     import torch
 
     if not torch.cuda.is_available():

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "wg_stamps.h"
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -35,6 +37,32 @@ __global__ __launch_bounds__(kThreads) void read_stream(const u32x4 *__restrict_
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
+// The decode kernels' access pattern without their arithmetic: workgroup w
+// reads the w-th contiguous share of the buffer front to back (16-byte
+// non-temporal loads, kUnroll in flight per lane), and records its start and
+// end clocks and XCD as the stamping build of the decode kernel does.
+__global__ __launch_bounds__(kThreads) void read_share(const u32x4 *__restrict__ src, size_t n,
+                                                       uint32_t *__restrict__ sink) {
+  ATTN_WG_STAMP();
+  const size_t per = (n + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = (size_t)blockIdx.x * per;
+  const size_t b1 = b0 + per < n ? b0 + per : n;
+  size_t i = b0 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kUnroll - 1) * kThreads < b1; i += kUnroll * kThreads) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < b1; i += kThreads) {
+    const u32x4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
 __global__ __launch_bounds__(kThreads) void copy_stream(uint4 *__restrict__ dst,
                                                         const uint4 *__restrict__ src, size_t n) {
   const size_t stride = (size_t)gridDim.x * kThreads;
@@ -56,6 +84,17 @@ __attribute__((visibility("default"))) int hbm_read_probe(const void *src, size_
   else
     hipLaunchKernelGGL(read_stream<false>, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
                        (const u32x4 *)src, bytes / 16, (uint32_t *)sink);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// Reads `bytes` (a multiple of 16) from src, one contiguous share per block
+// (blocks <= 4096 for the stamps); sink holds >= blocks words.
+__attribute__((visibility("default"))) int hbm_read_share_probe(const void *src, size_t bytes,
+                                                                void *sink, int blocks,
+                                                                void *stream) {
+  if (!src || !sink || bytes % 16 || blocks < 1 || blocks > attn::probe::kMaxStampedWgs) return 1;
+  hipLaunchKernelGGL(read_share, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u32x4 *)src, bytes / 16, (uint32_t *)sink);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

@@ -24,6 +24,9 @@ def load():
                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.hbm_copy_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_read_share_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p]
+    lib.attn_probe_wg_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int]
     return lib
 
 
