@@ -229,14 +229,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
   }
 }
 
-// Rows with few records (most calls: a handful of pieces per segment): a
+// Rows with up to 32 records (most calls: a handful of pieces per segment): a
 // wave per output row, or per run of rows_per_wave consecutive rows when
 // there are hundreds of thousands of them (a prefill's query rows), four
 // waves per workgroup.  Rows of one row block have their records in the same
 // slots, one record row apart, so a run works out where they are once per
-// block.  A row's records are loaded together and combined one after another
-// in index order with the merge rule (deterministic); each lane holds D/64 of
-// the row's outputs.
+// block.  A row's records are loaded in batches and combined by a fixed tree
+// of the merge rule (deterministic); each lane holds D/64 of the row's
+// outputs.
 constexpr int kRowsPerMergeBlock = 4;
 constexpr int kRowBatch = 4;  // records of one row loaded together
 
@@ -244,6 +244,7 @@ template <int D, bool ENERGY, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeArgs a,
                                                                           int rows_per_wave) {
   constexpr int EPL = D / kWave;  // output elements per lane
+  constexpr int NO = ENERGY ? 1 : EPL;  // o elements carried per lane (a dummy when ENERGY)
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t rows = (int64_t)a.map.B * a.map.Hkv * a.R;
   const int64_t row0 =
@@ -270,20 +271,21 @@ __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeAr
     }
     const int n = rr.P + rr.S;
     // Up to kRowBatch records are loaded at once (one memory round trip for
-    // a row of that many), then combined in index order with the rule itself.
-    float M = -INFINITY, lsum = 0.0f, acc[EPL];
+    // a row of that many) and combined as a binary tree, (0,1) (2,3) then the
+    // two pairs; the batch then joins what earlier batches left.  Slots past
+    // the row's count hold the identity record (-inf, 0, 0).
+    float M = -INFINITY, lsum = 0.0f, acc[NO];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    for (int e = 0; e < NO; ++e) acc[e] = 0.0f;
     for (int c0 = 0; c0 < n; c0 += kRowBatch) {
-      float mc[kRowBatch], lc[kRowBatch], oc[ENERGY ? 1 : kRowBatch][EPL];
+      float mc[kRowBatch], lc[kRowBatch], oc[kRowBatch][NO];
 #pragma unroll
       for (int k = 0; k < kRowBatch; ++k) {
         const int c = c0 + k;
         mc[k] = -INFINITY;
         lc[k] = 0.0f;
-        if constexpr (!ENERGY)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) oc[k][e] = 0.0f;
+        for (int e = 0; e < NO; ++e) oc[k][e] = 0.0f;
         if (c < n) {
           const bool sh = c >= rr.P;
           const int64_t rec = sh ? rr.srow + (c - rr.P) * rr.sstride : rr.prow + c * rr.pstride;
@@ -297,16 +299,11 @@ __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeAr
         }
       }
 #pragma unroll
-      for (int k = 0; k < kRowBatch; ++k) {
-        if (c0 + k >= n) break;
-        const float Mn = fmaxf(M, mc[k]);
-        const float fa = rescale_factor(M, Mn), fb = rescale_factor(mc[k], Mn);
-        lsum = lsum * fa + lc[k] * fb;
-        if constexpr (!ENERGY)
+      for (int step = 1; step < kRowBatch; step *= 2)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * fa + oc[k][e] * fb;
-        M = Mn;
-      }
+        for (int k = 0; k + step < kRowBatch; k += 2 * step)
+          combine<NO>(mc[k], lc[k], oc[k], mc[k + step], lc[k + step], oc[k + step]);
+      combine<NO>(M, lsum, acc, mc[0], lc[0], oc[0]);
     }
     const int i = r / a.G;
     const int h = kvh * a.G + (r - i * a.G);
@@ -327,9 +324,11 @@ __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeAr
 constexpr int64_t kMergeWavesWanted = 8192;
 constexpr int kMaxRowsPerWave = 16;
 
-// Rows whose record count exceeds this use the workgroup-per-row merge.
+// Rows whose record count exceeds this use the workgroup-per-row merge (the
+// shared-prefix batch's rows of 18 records: wave per row 2 us faster than a
+// workgroup per row; the 1M decode's rows of 33: a workgroup per row).
 #ifndef ATTN_MERGE_WIDE_RECORDS
-#define ATTN_MERGE_WIDE_RECORDS 8
+#define ATTN_MERGE_WIDE_RECORDS 32
 #endif
 constexpr int64_t kMergeWideRecords = ATTN_MERGE_WIDE_RECORDS;
 

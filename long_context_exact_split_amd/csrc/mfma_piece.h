@@ -32,6 +32,7 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef float f32x4e __attribute__((ext_vector_type(4)));
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -188,11 +189,11 @@ __device__ __forceinline__ float softmax_tile(f32x16_t sacc, int t0, int lim, fl
                                               float &m, float &lsum, f16x8_t (&pf)[2]) {
   const int h = (threadIdx.x & (kWave - 1)) >> 5;
   if (MASK == 1 || (MASK == 2 && __any(t0 + kTile > lim))) {
+    // Key t0 + 8(e/4) + 4h + e%4 is visible when its offset 8(e/4) + e%4
+    // (a constant per entry) is below lim - t0 - 4h.
+    const int vis = lim - t0 - 4 * h;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
-      sacc[e] = t < lim ? sacc[e] : -INFINITY;
-    }
+    for (int e = 0; e < 16; ++e) sacc[e] = 8 * (e >> 2) + (e & 3) < vis ? sacc[e] : -INFINITY;
   }
   float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
@@ -450,10 +451,10 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
       if constexpr (!ENERGY) acc += sh.out.o[w][r][d] * f;
       ls += sh.out.l[w][r] * f;
     }
-    if constexpr (!ENERGY) a.part.o[(rec0 + r) * D + d] = acc;
+    if constexpr (!ENERGY) __builtin_nontemporal_store(acc, &a.part.o[(rec0 + r) * D + d]);
     if (d == 0) {
-      a.part.m[rec0 + r] = M;
-      a.part.l[rec0 + r] = ls;
+      __builtin_nontemporal_store(M, &a.part.m[rec0 + r]);
+      __builtin_nontemporal_store(ls, &a.part.l[rec0 + r]);
     }
   }
 }
@@ -808,10 +809,14 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
     finalize_rows<D, RW>(a, b, kvh, rb, m, lsum, oacc, sh);
     return;
   }
+  // Records are written with non-temporal stores (here and in the other
+  // split kernels): the merge launch reads each once, and left in L2 as dirty
+  // lines they lengthened the end-of-kernel write-back (shared-prefix call
+  // 66.7 -> 65.4 us).
   const int64_t rec0 = slot * (kRows * RW) + wave * kRows;  // this wave's first row
   if (h == 0) {
-    a.part.m[rec0 + j] = m;
-    a.part.l[rec0 + j] = lsum;
+    __builtin_nontemporal_store(m, &a.part.m[rec0 + j]);
+    __builtin_nontemporal_store(lsum, &a.part.l[rec0 + j]);
   }
   if constexpr (!ENERGY) {
     // Each wave turns its O^T tiles into row-contiguous stores through its own
@@ -836,7 +841,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
         const int idx = q * kWave + lane;   // 256 float4 = 32 rows x 8
         const int rr = idx >> 3, c4 = (idx & 7) * 4;
         const float4 v = *reinterpret_cast<const float4 *>(stage + rr * OP + (c4 ^ ((rr & 7) * 4)));
-        *reinterpret_cast<float4 *>(a.part.o + (rec0 + rr) * D + 32 * n + c4) = v;
+        __builtin_nontemporal_store(f32x4e{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4e *>(a.part.o + (rec0 + rr) * D + 32 * n + c4));
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();

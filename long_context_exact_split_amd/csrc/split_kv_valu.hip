@@ -493,10 +493,10 @@ __device__ __forceinline__ void valu_piece(const SplitArgs &a, int b, int kvh, i
       if constexpr (!ENERGY) acc += so[w][r][d] * f;
       lsum += sl[w][r] * f;
     }
-    if constexpr (!ENERGY) a.part.o[(rec0 + r) * D + d] = acc;
+    if constexpr (!ENERGY) __builtin_nontemporal_store(acc, &a.part.o[(rec0 + r) * D + d]);
     if (d == 0) {
-      a.part.m[rec0 + r] = M;
-      a.part.l[rec0 + r] = lsum;
+      __builtin_nontemporal_store(M, &a.part.m[rec0 + r]);
+      __builtin_nontemporal_store(lsum, &a.part.l[rec0 + r]);
     }
   }
 }
