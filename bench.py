@@ -775,12 +775,14 @@ def wg_stamps(torch, args):
     import numpy as np
     from long_context_exact_split_amd import binding
     lib = binding.load_library()
-    if not hasattr(lib, "attn_probe_wg_stamps"):
-        raise RuntimeError(f"{binding.library_path()} is not the stamping build")
-    lib.attn_probe_wg_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int]
     run = make_runner(torch, args.workload, args.page_size)
-    if run.plan["kernel"] != 0 or getattr(run, "mode", "full") == "zeta":
-        raise RuntimeError("--wg-stamps covers the vector-ALU split kernel's decode workloads")
+    if run.plan.get("kernel") not in (0, 1) or getattr(run, "mode", "full") == "zeta":
+        raise RuntimeError("--wg-stamps covers the decode split kernels (vector-ALU, 32-row MFMA)")
+    readback = getattr(lib, ("attn_probe_wg_stamps", "attn_probe_wg_stamps_mfma")[run.plan["kernel"]],
+                       None)
+    if readback is None:
+        raise RuntimeError(f"{binding.library_path()} is not the stamping build")
+    readback.argtypes = [ctypes.c_void_p, ctypes.c_int]
     n = int(run.plan["work_items"])
     stream = torch.cuda.current_stream()
 
@@ -794,8 +796,8 @@ def wg_stamps(torch, args):
         b.record(stream)
         torch.cuda.synchronize()
         st = np.zeros((n, 4), dtype=np.uint64)
-        if lib.attn_probe_wg_stamps(st.ctypes.data, n) != 0:
-            raise RuntimeError("attn_probe_wg_stamps failed")
+        if readback(st.ctypes.data, n) != 0:
+            raise RuntimeError("stamp read-back failed")
         run.second()
         torch.cuda.synchronize()
         return stamp_summary(st, a.elapsed_time(b))

@@ -22,11 +22,12 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libattn_decode.so"
 TESTING_LIB_NAME = "libattn_decode_testing.so"
 PROBE_NAME = "libhbm_probe.so"  # HBM read-stream / copy reference kernels
-# The product library with the vector-ALU split kernel built to record each
-# workgroup's start and end clocks and XCD (csrc/probe/wg_stamps.h); loaded
-# only by the bench's --wg-stamps measurement.
+# The product library with the decode split kernels (vector-ALU and 32-row
+# matrix-core) built to record each workgroup's start and end clocks and XCD
+# (csrc/probe/wg_stamps.h); loaded only by the bench's --wg-stamps
+# measurement.  Each stamped source has its own stamp array and read-back.
 STAMPS_LIB_NAME = "libattn_decode_stamps.so"
-STAMPED_SOURCE = "split_kv_valu.hip"
+STAMPED_SOURCES = ("split_kv_valu.hip", "split_kv_mfma.hip")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
@@ -88,17 +89,18 @@ def build(verbose: bool = False, out_dir: str = PKG, build_dir: str = BUILD) -> 
     srcs = sources()
     tsrcs = testing_sources()
     probe = os.path.join(CSRC, "probe", "hbm_probe.hip")
-    stamped = os.path.join(CSRC, STAMPED_SOURCE)
     jobs = [(s, (), "") for s in srcs + tsrcs + [probe]]
-    jobs.append((stamped, ("-DATTN_WG_STAMPS",), ".stamps"))
+    jobs += [(os.path.join(CSRC, name), ("-DATTN_WG_STAMPS",), ".stamps")
+             for name in STAMPED_SOURCES]
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1], j[2]), jobs))
     lib_objs, test_objs = objs[:len(srcs)], objs[len(srcs):len(srcs) + len(tsrcs)]
-    probe_obj, stamped_obj = objs[-2], objs[-1]
+    probe_obj = objs[len(srcs) + len(tsrcs)]
+    stamped = dict(zip(STAMPED_SOURCES, objs[len(srcs) + len(tsrcs) + 1:]))
     _link([probe_obj], PROBE_NAME, verbose, out_dir)
     _link(lib_objs + test_objs, TESTING_LIB_NAME, verbose, out_dir)
-    _link([stamped_obj if os.path.basename(s) == STAMPED_SOURCE else o
-           for s, o in zip(srcs, lib_objs)], STAMPS_LIB_NAME, verbose, out_dir)
+    _link([stamped.get(os.path.basename(s), o) for s, o in zip(srcs, lib_objs)],
+          STAMPS_LIB_NAME, verbose, out_dir)
     return _link(lib_objs, LIB_NAME, verbose, out_dir)
 
 

@@ -11,8 +11,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Each source that includes this has its own array (its own code object)
+// and its own read-back, named by ATTN_WG_STAMPS_READBACK.
+#ifndef ATTN_WG_STAMPS_READBACK
+#define ATTN_WG_STAMPS_READBACK attn_probe_wg_stamps
+#endif
+
 namespace attn {
 namespace probe {
+namespace {
 
 constexpr int kMaxStampedWgs = 4096;
 __device__ uint64_t g_wg_stamps[kMaxStampedWgs * 4];
@@ -36,12 +43,14 @@ struct WgStamp {
   }
 };
 
+}  // namespace
 }  // namespace probe
 }  // namespace attn
 
-// Copies the stamps of workgroups [0, n) to host memory: 4 values each
-// (start clock, end clock, XCC id register, HW id register).  0 on success.
-extern "C" __attribute__((visibility("default"))) int attn_probe_wg_stamps(uint64_t *host, int n) {
+// Copies the stamps of workgroups [0, n) of the last stamped launch of this
+// source's kernels to host memory: 4 values each (start clock, end clock,
+// XCC id register, HW id register).  0 on success.
+extern "C" __attribute__((visibility("default"))) int ATTN_WG_STAMPS_READBACK(uint64_t *host, int n) {
   if (n < 0 || n > attn::probe::kMaxStampedWgs) return (int)hipErrorInvalidValue;
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(attn::probe::g_wg_stamps),
                                   sizeof(uint64_t) * 4 * (size_t)n);

@@ -33,6 +33,13 @@
 // the same merge kernel follows.
 #include "mfma_piece.h"
 
+#ifdef ATTN_WG_STAMPS
+#define ATTN_WG_STAMPS_READBACK attn_probe_wg_stamps_mfma
+#include "probe/wg_stamps.h"  // per-workgroup clocks: measurement builds only
+#else
+#define ATTN_WG_STAMP()
+#endif
+
 namespace attn {
 namespace {
 
@@ -40,6 +47,7 @@ using namespace mfma;
 
 template <int D, bool ENERGY, bool PAGED>
 __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
+  ATTN_WG_STAMP();
   __shared__ MfmaSmem<D, ENERGY> sh;
   WorkMap m = a.map;
   m.causal_rows = 0;  // one row block: never set for this kernel's maps

@@ -79,8 +79,9 @@ def test_stamping_build_exports_the_boundary_and_its_probe(lib):
     if not os.path.exists(path):
         pytest.skip("stamping build not built")
     exported = exported_functions(path)
-    assert exported == set(declared_functions()) | {"attn_probe_wg_stamps"}
-    assert "attn_probe_wg_stamps" not in exported_functions(binding.library_path())
+    probes = {"attn_probe_wg_stamps", "attn_probe_wg_stamps_mfma"}
+    assert exported == set(declared_functions()) | probes
+    assert not probes & exported_functions(binding.library_path())
 
 
 def test_struct_layouts_match_c(tmp_path):
