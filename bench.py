@@ -763,7 +763,9 @@ def stamp_summary(st, ev_ms):
             "xcd_end_min_max_us": [float(ends.min()), float(ends.max())],
             # if the work had been shared out in proportion to each XCD's own rate
             "balanced_span_us": float(len(ends) / np.sum(1.0 / ends)),
-            "xcd": per}
+            "xcd": per,
+            "wg_duration_us": [round(float(x), 1) for x in dur],
+            "wg_hw_id": [int(x) for x in st[:, 3]]}
 
 
 def wg_stamps(torch, args):
