@@ -238,7 +238,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
 // of the merge rule (deterministic); each lane holds D/64 of the row's
 // outputs.
 constexpr int kRowsPerMergeBlock = 4;
-constexpr int kRowBatch = 4;  // records of one row loaded together
+#ifndef ATTN_MERGE_ROW_BATCH
+#define ATTN_MERGE_ROW_BATCH 8
+#endif
+constexpr int kRowBatch = ATTN_MERGE_ROW_BATCH;  // records of one row loaded together (4, 16: slower)
 
 template <int D, bool ENERGY, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeArgs a,
@@ -271,9 +274,9 @@ __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeAr
     }
     const int n = rr.P + rr.S;
     // Up to kRowBatch records are loaded at once (one memory round trip for
-    // a row of that many) and combined as a binary tree, (0,1) (2,3) then the
-    // two pairs; the batch then joins what earlier batches left.  Slots past
-    // the row's count hold the identity record (-inf, 0, 0).
+    // a row of that many) and combined as a binary tree, (0,1) (2,3) ...,
+    // then pairs of pairs; the batch then joins what earlier batches left.
+    // Slots past the row's count hold the identity record (-inf, 0, 0).
     float M = -INFINITY, lsum = 0.0f, acc[NO];
 #pragma unroll
     for (int e = 0; e < NO; ++e) acc[e] = 0.0f;
