@@ -5,8 +5,8 @@
 //
 // One workgroup of 8 waves per CU.  The prefix runs on the shared-tile
 // matrix-core code, which serves the query rows of all samples from every
-// K/V tile (the prefix is read once); the suffix segments run two at a time
-// (four waves each).  The planner either splits the CUs between the two
+// K/V tile (the prefix is read once); the suffix segments run four at a time
+// (two waves each).  The planner either splits the CUs between the two
 // parts (the first workgroups take prefix pieces, the others suffix
 // segments: matrix-core work on some CUs while the others stream from HBM),
 // or gives every workgroup a share of both.  A suffix segment is one sample's
@@ -31,15 +31,19 @@ constexpr int kBifWaves = 8;  // the shared-tile code's 256-row blocks: 8 waves 
 constexpr int kBifThreads = kBifWaves * kWave;
 
 
-// The suffix runs as two groups of four waves, each on a segment of its own
-// (a segment's pieces carry a latency chain of their own: query loads, the
-// first tiles, the epilogue; two in flight overlap them).
-constexpr int kSufWaves = kBifWaves / 2;
+// The suffix runs as kSufGroups groups of waves, each on a segment of its
+// own (a segment's pieces carry a latency chain of their own: query loads,
+// the first tiles, the epilogue; several in flight overlap them).
+#ifndef ATTN_BIF_SUF_GROUPS
+#define ATTN_BIF_SUF_GROUPS 4  // 2: 0.5-1 us slower per call on the 64-sample batch
+#endif
+constexpr int kSufGroups = ATTN_BIF_SUF_GROUPS;
+constexpr int kSufWaves = kBifWaves / kSufGroups;
 
 template <int D>
 union BifSmem {
   mfma::RowsSmem<D, kBifWaves, false> pre;
-  mfma::MfmaSmem<D, false, kSufWaves> suf[2];
+  mfma::MfmaSmem<D, false, kSufWaves> suf[kSufGroups];
 };
 
 template <int D>
@@ -60,26 +64,31 @@ __global__ __launch_bounds__(kBifThreads) void split_kv_bifurcated(SplitArgs pre
   auto suffix = [&](int w) __attribute__((always_inline)) {
     const int64_t U = total_units(sm);
     PieceCursor cur = first_piece(sm, U, w);
-    const int grp = threadIdx.x / (kSufWaves * kWave);  // wave-uniform: 0 or 1
-    Piece p0, p1;
-    // Pieces two at a time, one per group; with an odd count the second
-    // group runs an empty piece (same barriers, nothing written).  The
-    // group's piece is picked field by field (indexing an array of the two
-    // by the group would put it in scratch memory).
-    while (next_piece(sm, w, cur, &p0)) {
-      const bool two = next_piece(sm, w, cur, &p1);
-      const bool second = grp == 1 && two;  // this group takes p1
-      const bool mine = grp == 0 || two;
-      const int t0 = (int)(second ? p1.t0 : p0.t0);
-      mfma::mfma_piece<D, false, false, kSufWaves>(
-          suf, second ? p1.b : p0.b, second ? p1.kvh : p0.kvh, second ? p1.rb : p0.rb, t0,
-          mine ? (int)(second ? p1.t1 : p0.t1) : t0, second ? p1.slot : p0.slot, sh.suf[grp],
-          grp * kSufWaves * kWave, mine);
+    const int grp = threadIdx.x / (kSufWaves * kWave);  // wave-uniform
+    // Pieces kSufGroups at a time, one per group (every group walks the same
+    // cursor and keeps the piece of its own index); a group left without one
+    // runs an empty piece (same barriers, nothing written).  The group's
+    // piece is copied under a wave-uniform branch, not indexed out of an
+    // array (which would put the array in scratch memory).
+    for (;;) {
+      Piece mine, q;
+      bool have = false;
+      if (!next_piece(sm, w, cur, &mine)) break;
+      have = grp == 0;
+#pragma unroll
+      for (int i = 1; i < kSufGroups; ++i) {
+        if (!next_piece(sm, w, cur, &q)) break;
+        if (i == grp) {
+          mine = q;
+          have = true;
+        }
+      }
+      const int t0 = (int)mine.t0;
+      mfma::mfma_piece<D, false, false, kSufWaves>(suf, mine.b, mine.kvh, mine.rb, t0,
+                                                  have ? (int)mine.t1 : t0, mine.slot,
+                                                  sh.suf[grp], grp * kSufWaves * kWave, have);
     }
   };
-  // Workgroup w runs on XCD w % 8; consecutive workgroups of one XCD
-  // alternate the order.  Every piece starts with a workgroup barrier before
-  // it touches the shared memory, so switching parts needs no other.
   // Split launches (the two maps' workgroup counts add up to the grid) give
   // each workgroup one part: the first pm.n_wg the prefix, the rest the
   // suffix.  Otherwise every workgroup takes a share of both.

@@ -68,3 +68,26 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_stamp_summary():
+    """Per-workgroup stamps -> per-XCD summary: ends, spreads and the span had
+    each XCD's share matched its own rate (harmonic mean of the XCD ends)."""
+    import numpy as np
+    n = 16
+    st = np.zeros((n, 4), dtype=np.uint64)
+    for w in range(n):
+        x = w % 8
+        st[w, 0] = 1000 + w            # starts 0.01 us apart (10 ns ticks)
+        st[w, 1] = 1000 + 10000 + 100 * x + (w // 8)  # XCD x ends (100 + x) us after the first start
+        st[w, 2] = x
+        st[w, 3] = w
+    s = bench.stamp_summary(st, 0.2)
+    assert s["event_us"] == 200.0
+    assert abs(s["start_spread_us"] - 0.15) < 1e-9
+    ends = [100 + x + 0.01 for x in range(8)]
+    assert abs(s["span_us"] - (107 + 0.01)) < 1e-9
+    assert abs(s["xcd_end_min_max_us"][0] - 100.01) < 1e-9
+    assert abs(s["balanced_span_us"] - 8 / sum(1 / e for e in ends)) < 1e-9
+    assert s["xcd"]["3"]["workgroups"] == 2
+    assert len(s["wg_duration_us"]) == n and s["wg_hw_id"][5] == 5
