@@ -238,10 +238,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials(MergeArgs a) {
 // of the merge rule (deterministic); each lane holds D/64 of the row's
 // outputs.
 constexpr int kRowsPerMergeBlock = 4;
+// Records of one row loaded together (batches of 4 or 16 measured slower).
 #ifndef ATTN_MERGE_ROW_BATCH
 #define ATTN_MERGE_ROW_BATCH 8
 #endif
-constexpr int kRowBatch = ATTN_MERGE_ROW_BATCH;  // records of one row loaded together (4, 16: slower)
+constexpr int kRowBatch = ATTN_MERGE_ROW_BATCH;
 
 template <int D, bool ENERGY, bool CAUSAL_ROWS>
 __global__ __launch_bounds__(kRowsPerMergeBlock * kWave) void merge_rows(MergeArgs a,

@@ -841,7 +841,8 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
         const int idx = q * kWave + lane;   // 256 float4 = 32 rows x 8
         const int rr = idx >> 3, c4 = (idx & 7) * 4;
         const float4 v = *reinterpret_cast<const float4 *>(stage + rr * OP + (c4 ^ ((rr & 7) * 4)));
-        __builtin_nontemporal_store(f32x4e{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4e *>(a.part.o + (rec0 + rr) * D + 32 * n + c4));
+        f32x4e *dst = reinterpret_cast<f32x4e *>(a.part.o + (rec0 + rr) * D + 32 * n + c4);
+        __builtin_nontemporal_store(f32x4e{v.x, v.y, v.z, v.w}, dst);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();

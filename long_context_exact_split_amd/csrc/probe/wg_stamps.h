@@ -50,7 +50,8 @@ struct WgStamp {
 // Copies the stamps of workgroups [0, n) of the last stamped launch of this
 // source's kernels to host memory: 4 values each (start clock, end clock,
 // XCC id register, HW id register).  0 on success.
-extern "C" __attribute__((visibility("default"))) int ATTN_WG_STAMPS_READBACK(uint64_t *host, int n) {
+extern "C" __attribute__((visibility("default")))
+int ATTN_WG_STAMPS_READBACK(uint64_t *host, int n) {
   if (n < 0 || n > attn::probe::kMaxStampedWgs) return (int)hipErrorInvalidValue;
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(attn::probe::g_wg_stamps),
                                   sizeof(uint64_t) * 4 * (size_t)n);

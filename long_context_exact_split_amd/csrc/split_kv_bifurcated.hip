@@ -12,16 +12,15 @@
 // or gives every workgroup a share of both.  A suffix segment is one sample's
 // own decoded KV of one KV head: a few hundred keys for the G query heads of
 // the group.  It runs on the 32-row matrix-core code with only G rows valid:
-// the matrix cores have the capacity to spare, and the dot products and the
-// P.V product leave the vector ALUs only the softmax, where the vector-ALU
-// decode code spends several hundred instructions per 16 keys on segments
-// that short (measured 13-14 us per 512-token segment per CU against
-// about 4 us here).  In the shared form half of the workgroups of every XCD
-// run their prefix piece first and the other half their suffix share first,
-// so that there too some CUs are busy on the matrix cores while others keep
-// HBM streaming.  Both parts write their (m, l, o) records as their own
-// kernels do (work_map.h, one map each, with the workgroup count of its
-// part), and the merge kernel combines them.
+// the matrix cores have the capacity to spare, a 512-token segment took the
+// same ~13 us per CU there as on the vector-ALU decode code (both bound by
+// the segment's stream), and the two parts' shared memory then overlays
+// within one 8-wave workgroup.  In the shared form half of the workgroups of
+// every XCD run their prefix piece first and the other half their suffix
+// share first, so that there too some CUs are busy on the matrix cores while
+// others keep HBM streaming.  Both parts write their (m, l, o) records as
+// their own kernels do (work_map.h, one map each, with the workgroup count
+// of its part), and the merge kernel combines them.
 #include "mfma_piece.h"
 
 namespace attn {
@@ -29,7 +28,6 @@ namespace {
 
 constexpr int kBifWaves = 8;  // the shared-tile code's 256-row blocks: 8 waves of 32 rows
 constexpr int kBifThreads = kBifWaves * kWave;
-
 
 // The suffix runs as kSufGroups groups of waves, each on a segment of its
 // own (a segment's pieces carry a latency chain of their own: query loads,
@@ -53,17 +51,18 @@ __global__ __launch_bounds__(kBifThreads) void split_kv_bifurcated(SplitArgs pre
   WorkMap pm = pre.map, sm = suf.map;
   pm.causal_rows = 0;  // neither part is causal (the launcher checks)
   sm.causal_rows = 0;
-  auto prefix = [&](int w) __attribute__((always_inline)) {
+  // wl: the workgroup's index in the part's own map.
+  auto prefix = [&](int wl) __attribute__((always_inline)) {
     const int64_t U = total_units(pm);
-    PieceCursor cur = first_piece(pm, U, w);
+    PieceCursor cur = first_piece(pm, U, wl);
     Piece p;
-    while (next_piece(pm, w, cur, &p))
+    while (next_piece(pm, wl, cur, &p))
       mfma::rows_piece<D, kBifWaves, false, false>(pre, p.b, p.kvh, p.rb, (int)p.t0, (int)p.t1,
                                                    p.slot, sh.pre);
   };
-  auto suffix = [&](int w) __attribute__((always_inline)) {
+  auto suffix = [&](int wl) __attribute__((always_inline)) {
     const int64_t U = total_units(sm);
-    PieceCursor cur = first_piece(sm, U, w);
+    PieceCursor cur = first_piece(sm, U, wl);
     const int grp = threadIdx.x / (kSufWaves * kWave);  // wave-uniform
     // Pieces kSufGroups at a time, one per group (every group walks the same
     // cursor and keeps the piece of its own index); a group left without one
@@ -73,11 +72,11 @@ __global__ __launch_bounds__(kBifThreads) void split_kv_bifurcated(SplitArgs pre
     for (;;) {
       Piece mine, q;
       bool have = false;
-      if (!next_piece(sm, w, cur, &mine)) break;
+      if (!next_piece(sm, wl, cur, &mine)) break;
       have = grp == 0;
 #pragma unroll
       for (int i = 1; i < kSufGroups; ++i) {
-        if (!next_piece(sm, w, cur, &q)) break;
+        if (!next_piece(sm, wl, cur, &q)) break;
         if (i == grp) {
           mine = q;
           have = true;
