@@ -354,11 +354,24 @@ attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans
              b->sp.balanced;
   b->workgroups = 0;
   if (b->fused) {
-    b->workgroups = cu;
-    int64_t wp = bifurcated_prefix_workgroups(d, cu), ws = cu - wp;
-    if (wp == 0) wp = ws = cu;  // shared form: every workgroup both parts
-    if ((st = set_workgroups(&b->pre, wp, &b->pp)) != ATTN_OK) return st;
-    if ((st = set_workgroups(&b->suf, ws, &b->sp)) != ATTN_OK) return st;
+    // Split form if the estimate asks for it, else (or if a part's shares
+    // would not fit the work map's 32-bit token ranges on its fewer
+    // workgroups) the shared form, else two launches with their own plans.
+    const attn_plan_t pp0 = b->pp, sp0 = b->sp;
+    auto recut = [&](int64_t wp, int64_t ws) {
+      b->pp = pp0;
+      b->sp = sp0;
+      return set_workgroups(&b->pre, wp, &b->pp) == ATTN_OK &&
+             set_workgroups(&b->suf, ws, &b->sp) == ATTN_OK;
+    };
+    const int64_t wp = bifurcated_prefix_workgroups(d, cu);
+    if (!((wp > 0 && recut(wp, cu - wp)) || recut(cu, cu))) {
+      b->pp = pp0;
+      b->sp = sp0;
+      b->fused = false;
+    } else {
+      b->workgroups = cu;
+    }
   }
   b->pre_bytes = (size_t)round_up((int64_t)b->pp.workspace_bytes, 256);
   b->total = b->pre_bytes + b->sp.workspace_bytes;

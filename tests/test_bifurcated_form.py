@@ -54,3 +54,13 @@ def test_small_batches_take_two_launches():
     assert form(8, 32, 8, 128, 1000, 100)[0] == 0      # 32 rows per KV head
     assert form(64, 32, 8, 128, 1000, 0)[0] == 0       # no suffix
     assert form(64, 32, 8, 128, 0, 100)[0] == 0        # no prefix
+
+
+def test_split_whose_shares_overflow_falls_back_to_the_shared_form():
+    # 2048 samples with 2^20-token suffixes (2^34 suffix tokens in all) and a
+    # 2^30-token prefix: the estimate gives the prefix all but 8 workgroups,
+    # whose 2^31-token suffix shares do not fit the work map's 32-bit ranges;
+    # on all 256 workgroups both parts' shares do.
+    assert form(2048, 32, 8, 128, 1 << 30, 1 << 20) == (1, 256, 256)
+    # half the samples (2^30-token suffix shares on 8 workgroups) split as estimated
+    assert form(1024, 32, 8, 128, 1 << 30, 1 << 20)[1:] == (248, 8)
