@@ -3,10 +3,10 @@
 plan.cpp (validation, partition and plans, including work_map.h's layout
 arithmetic) and the test hooks are compiled with g++ and
 -fsanitize=address,undefined into a host-only library (no HIP code).  A
-child pytest then drives it through the partition, anchor-path and host-check
-tests (hypothesis shapes, ragged and causal layouts, and the extreme shapes
-with 2^16 rows per KV head and 2^31 - 2^16 tokens), with the sanitizer
-runtime preloaded and every report fatal.
+child pytest then drives it through the partition, anchor-path, host-check and
+shared-prefix launch-form tests (hypothesis shapes, ragged and causal layouts,
+and the extreme shapes with 2^16 rows per KV head and 2^31 - 2^16 tokens),
+with the sanitizer runtime preloaded and every report fatal.
 """
 import os
 import shutil
@@ -43,7 +43,8 @@ def test_host_code_is_clean_under_asan_and_ubsan(tmp_path):
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1",
                HYPOTHESIS_STORAGE_DIRECTORY=str(tmp_path / "hyp"))
     tests = [os.path.join(ROOT, "tests", t) for t in
-             ("test_partition.py", "test_anchor_fusion.py", "test_host_checks.py")]
+             ("test_partition.py", "test_anchor_fusion.py", "test_host_checks.py",
+              "test_bifurcated_form.py")]
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-s", "-p", "no:cacheprovider",
                         *tests], cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     out = r.stdout + r.stderr
