@@ -4,7 +4,10 @@ Every HIP/C++ source under ``csrc/`` is compiled to an object in ``_build/``
 (in parallel), then linked into the shared library next to this file.  The
 test build ``libattn_decode_testing.so`` links the same objects plus the
 test-only hooks under ``csrc/testing/``; the product library holds none of
-them.  Symbols are hidden unless the public headers mark them ATTN_API.
+them.  ``libattn_decode_stamps.so`` is the product with its decode split
+kernels built to time every workgroup (bench.py --wg-stamps), and
+``libhbm_probe.so`` holds the HBM reference kernels.  Symbols are hidden
+unless the public headers mark them ATTN_API.
 """
 from __future__ import annotations
 

@@ -345,10 +345,11 @@ attn_status_t bifurcated_plans(const attn_bifurcated_desc_t *d, int cu, BifPlans
   if ((st = make_plan(&b->pre, cu, kMfmaPlans, &b->pp)) != ATTN_OK) return st;
   if ((st = make_plan(&b->suf, cu, kMfmaPlans, &b->sp)) != ATTN_OK) return st;
   // One launch for both parts when the prefix takes the shared-tile kernel's
-  // 256-row blocks and the suffix the vector-ALU code: one 8-wave workgroup
-  // per CU (the shared tiles need one workgroup per CU anyway), the CUs split
-  // between the parts by bifurcated_prefix_workgroups, or each workgroup
-  // with a share of both.
+  // 256-row blocks and the suffix is a decode of a few rows per KV head
+  // (planned for the vector-ALU kernel; in the one launch it runs on the
+  // 32-row matrix-core code): one 8-wave workgroup per CU (the shared tiles
+  // need one workgroup per CU anyway), the CUs split between the parts by
+  // bifurcated_prefix_workgroups, or each workgroup with a share of both.
   b->fused = b->pp.work_items > 0 && b->sp.work_items > 0 && b->pp.kernel == 2 &&
              b->pp.rows_per_block == 8 * kMfmaRows && b->sp.kernel == 0 && b->pp.balanced &&
              b->sp.balanced;
