@@ -10,9 +10,11 @@ Other workload shapes are selectable with --workload.
 Prints one JSON line: KV tokens/s (value), whole-path HBM GB/s against the
 8 TB/s peak, the roofline record of the dominant kernel (its per-launch time
 from HIP events recorded on the stream it runs on), and the fp64 CPU oracle
-timed on a bounded sample of the same workload.  Whole-call times are also
-given as median / 10th / 90th percentile, for the back-to-back timed calls
-(call_ms) and for calls that each follow a 1 GiB read evicting L2 and the
+timed on a bounded sample of the same workload.  Events bracket one timed
+step in four (event_every; every step when there are fewer than 40), so that
+the markers they put in the stream leave the other steps' time untouched.
+Whole-call times are also given as median / 10th / 90th percentile, for the
+event-timed calls (call_ms) and for calls that each follow a 1 GiB read evicting L2 and the
 Infinity Cache (call_ms_cold_cache; the bifurcated batch, ~203 MB, would
 otherwise stay cache-resident between calls), and for the call captured once
 into a HIP graph and replayed (call_ms_graph, with the wall time per replay).
@@ -592,15 +594,30 @@ def spread(ms):
     return {"median": statistics.median(xs), "p10": pct(10), "p90": pct(90), "calls": len(xs)}
 
 
-def timed_steps(torch, run, K, warmup, min_warmup_s):
+# Steps per event-timed step in the timed region: every event record is a
+# marker in the stream that the GPU processes between the launches, measured
+# at ~4 us on the shared-prefix call (~67 us per step with three per step,
+# ~55 us with none) and ~1 us on the 1M decode.
+EVENT_EVERY = 4
+
+
+def event_stride(K, every=EVENT_EVERY):
+    """Event-timed steps are one in `every`, but at least ~10 of the K."""
+    return max(1, min(every, K // 10))
+
+
+def timed_steps(torch, run, K, warmup, min_warmup_s, every=EVENT_EVERY):
     """Untimed warm-up (at least `warmup` steps and `min_warmup_s` seconds:
     from idle the GPU needs ~30-40 back-to-back steps to reach its steady
-    clocks), then K steps, each bracketed by HIP events on the launch stream
-    (first launch, second launch).  Returns the per-step event times and the
-    wall time of the K steps."""
+    clocks), then K steps.  Steps 0, n, 2n, ... (n = event_stride) are
+    bracketed by HIP events on the launch stream (before the first launch,
+    between the two launches, after the second); the others run without
+    markers.  Returns the per-launch event times of those steps and the wall
+    time of all K steps."""
+    n = event_stride(K, every)
     # Events are created before the warm-up: creating them afterwards would
     # leave the GPU idle long enough for its clocks to drop again.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(0, K, n)]
     stream = torch.cuda.current_stream()
     warm, t_w = 0, time.perf_counter()
     while warm < warmup or time.perf_counter() - t_w < min_warmup_s:
@@ -612,16 +629,22 @@ def timed_steps(torch, run, K, warmup, min_warmup_s):
     torch.cuda.synchronize()  # barrier (one rank)
     t0 = time.perf_counter()
     for i in range(K):
-        ev[i][0].record(stream)
+        if i % n:
+            run.first()
+            run.second()
+            continue
+        e = ev[i // n]
+        e[0].record(stream)
         run.first()
-        ev[i][1].record(stream)
+        e[1].record(stream)
         run.second()
-        ev[i][2].record(stream)
+        e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return {"first_ms": [e[0].elapsed_time(e[1]) for e in ev],
             "second_ms": [e[1].elapsed_time(e[2]) for e in ev],
-            "call_ms": [e[0].elapsed_time(e[2]) for e in ev], "wall_s": wall, "warmup": warm}
+            "call_ms": [e[0].elapsed_time(e[2]) for e in ev], "wall_s": wall, "warmup": warm,
+            "event_every": n}
 
 
 def cold_calls(torch, run, n):
@@ -716,7 +739,8 @@ def measure_config(torch, name, K, n_rows, warmup, min_warmup_s):
     call_avg = statistics.mean(t["call_ms"])
     rec = {"workload": WORKLOADS[name], "seed": getattr(w, "seed", None),
            "dtype": getattr(w, "dtype", "bf16"), "steps": K,
-           "ms_per_step": t["wall_s"] * 1e3 / K, "call_ms_mean": call_avg,
+           "ms_per_step": t["wall_s"] * 1e3 / K, "event_every": t["event_every"],
+           "call_ms_mean": call_avg,
            "call_ms": spread(t["call_ms"]), "dominant_kernel_ms": first_avg,
            "kv_tokens_per_call": run.kv_tokens,
            "kv_tokens_per_s": run.kv_tokens / (call_avg * 1e-3),
@@ -889,6 +913,7 @@ def main(argv=None):
         "warmup": args.warmup,
         "warmup_steps_run": t["warmup"],
         "ms_per_step": step_ms,
+        "event_every": t["event_every"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

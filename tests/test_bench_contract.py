@@ -91,3 +91,16 @@ def test_stamp_summary():
     assert abs(s["balanced_span_us"] - 8 / sum(1 / e for e in ends)) < 1e-9
     assert s["xcd"]["3"]["workgroups"] == 2
     assert len(s["wg_duration_us"]) == n and s["wg_hw_id"][5] == 5
+
+
+def test_event_stride():
+    """Event-timed steps: one in four, but at least ten of the timed steps."""
+    assert bench.event_stride(100) == 4
+    assert bench.event_stride(200) == 4
+    assert bench.event_stride(50) == 4
+    assert bench.event_stride(30) == 3
+    assert bench.event_stride(10) == 1
+    assert bench.event_stride(1) == 1
+    for K in range(1, 400):
+        n = bench.event_stride(K)
+        assert len(range(0, K, n)) >= min(K, 10)
