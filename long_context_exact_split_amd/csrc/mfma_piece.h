@@ -136,6 +136,14 @@ __device__ __forceinline__ u32x4 v_to_f16(u32x4 w) {
   return r;
 }
 
+// 16 bytes of a tile row in LDS.  Row pitches and column offsets are
+// multiples of 8 elements, so the address is 16-byte aligned; stated here so
+// that the store is one ds_write_b128 (the compiler otherwise splits it into
+// two 8-byte ds_write2_b32).
+__device__ __forceinline__ u32x4 *lds16(uint16_t *p) {
+  return reinterpret_cast<u32x4 *>(__builtin_assume_aligned(p, 16));
+}
+
 // The three parts of one 32-key tile in one wave.
 //
 // qk_tile: S^T = K.Q^T (raw logits), K read from LDS (row pitch KROW).
@@ -401,9 +409,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, int b, int kvh, i
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int key = i * KPI + lane / LPK;
-      *reinterpret_cast<u32x4 *>(ks + key * T::KROW + (lane % LPK) * 8) = kr[i];
-      if constexpr (!ENERGY)
-        *reinterpret_cast<u32x4 *>(vs + key * T::VROW + (lane % LPK) * 8) = v_to_f16(vr[i]);
+      *lds16(ks + key * T::KROW + (lane % LPK) * 8) = kr[i];
+      if constexpr (!ENERGY) *lds16(vs + key * T::VROW + (lane % LPK) * 8) = v_to_f16(vr[i]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -477,7 +484,7 @@ constexpr int kStoreAhead = 4;
 #define ATTN_ROWS_RING 2        // register ring stages with eight waves (3: 1% slower)
 #endif
 #ifndef ATTN_ROWS_VALU_PER_MFMA
-#define ATTN_ROWS_VALU_PER_MFMA 5  // softmax VALU instructions placed after each MFMA
+#define ATTN_ROWS_VALU_PER_MFMA 4  // softmax VALU instructions placed after each MFMA (5: ~1% slower)
 #endif
 
 template <int D, int RW, bool ENERGY>
@@ -679,9 +686,8 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
       const int p = threadIdx.x + i * NTH;
       if (PIECES % NTH != 0 && p >= PIECES) break;  // wave-uniform
       const int key = p / (D / 8), col = (p % (D / 8)) * 8;
-      *reinterpret_cast<u32x4 *>(sh.t.k[buf] + key * T::KROW + col) = kd[i];
-      if constexpr (!ENERGY)
-        *reinterpret_cast<u32x4 *>(sh.t.v[buf] + key * T::VROW + col) = v_to_f16(vd[i]);
+      *lds16(sh.t.k[buf] + key * T::KROW + col) = kd[i];
+      if constexpr (!ENERGY) *lds16(sh.t.v[buf] + key * T::VROW + col) = v_to_f16(vd[i]);
     }
   };
 
