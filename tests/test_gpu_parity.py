@@ -525,42 +525,49 @@ def test_prepared_bifurcated_call_matches_the_plain_call():
 
 
 def test_graph_replays_match_eager_calls():
-    """A decode (split + merge) and a bifurcated call captured into one HIP
-    graph (prepared calls bound to the capturing stream; the library launches
-    kernels only, no memset, no allocation) and replayed three times, with
-    eager work and synchronisation between the replays: every replay gives
-    the eager results bit for bit."""
+    """A decode (split + merge) and two bifurcated calls captured into one
+    HIP graph (prepared calls bound to the capturing stream; the library
+    launches kernels only, no memset, no allocation) and replayed three
+    times, with eager work and synchronisation between the replays: every
+    replay gives the eager results bit for bit.  The second bifurcated call
+    has 64 samples, so it runs the one-launch shared-prefix kernel."""
     w = inputs.make_decode("graph", 77, B=2, q_len=1, Hq=32, Hkv=8, D=128, L_max=3000,
                            kv_lens=[3000, 1500], nan_pad=True)
     q, k, v, lens = workload_tensors(w)
     O0, lse0 = binding.decode(q, k, v, lens, scale=w.scale)
-    wb = inputs.bifurcated_prefix(seed=45, S=8, Lp=700, Ls=90)
-    tb = [dev(x) for x in (wb.q, wb.kp, wb.vp, wb.ks, wb.vs)]
-    Ob0, lseb0 = binding.decode_bifurcated(*tb, scale=wb.scale)
+    calls = []
+    for wb in (inputs.bifurcated_prefix(seed=45, S=8, Lp=700, Ls=90),
+               inputs.bifurcated_prefix(seed=46, S=64, Lp=1024, Ls=64)):
+        tb = [dev(x) for x in (wb.q, wb.kp, wb.vp, wb.ks, wb.vs)]
+        calls.append((tb, wb.scale) + binding.decode_bifurcated(*tb, scale=wb.scale))
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         ph = binding.Phases(q, k, v, lens, scale=w.scale)
-        bc = binding.BifurcatedCall(*tb, scale=wb.scale)
+        bcs = [binding.BifurcatedCall(*tb, scale=sc) for tb, sc, _, _ in calls]
         ph.partials()
         ph.merge()
-        bc.run()
+        for bc in bcs:
+            bc.run()
     side.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
         ph.partials()
         ph.merge()
-        bc.run()
+        for bc in bcs:
+            bc.run()
     torch.cuda.synchronize()
     for rep in range(3):
-        for t in (ph.out, ph.lse, bc.out, bc.lse):
+        for t in [ph.out, ph.lse] + [x for bc in bcs for x in (bc.out, bc.lse)]:
             t.fill_(float("nan"))
         binding.decode(q, k, v, lens, scale=w.scale)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(ph.out, O0) and torch.equal(ph.lse, lse0), f"decode, replay {rep}"
-        assert torch.equal(bc.out, Ob0) and torch.equal(bc.lse, lseb0), f"bifurcated, replay {rep}"
+        for i, (bc, (_, _, Ob0, lseb0)) in enumerate(zip(bcs, calls)):
+            assert torch.equal(bc.out, Ob0) and torch.equal(bc.lse, lseb0), \
+                f"bifurcated call {i}, replay {rep}"
 
 
 # The one-launch shared-prefix kernel in each of its forms (64 samples x 4
