@@ -70,9 +70,12 @@ hipError_t launch_split_mfma(const attn_plan_t &plan, const SplitArgs &a, int he
                              bool energy_only, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t stream);
 // Both parts of a shared-prefix call in one launch of `workgroups` 8-wave
-// workgroups: the prefix split (shared-tile kernel, 256-row blocks) and the
-// suffix split (vector-ALU code, suffix_rows_per_block rows), each over its
-// own balanced map with n_wg == workgroups; full mode, dense caches.
+// workgroups: the prefix split (shared-tile code, 256-row blocks) and the
+// suffix split (32-row matrix-core code, suffix_rows_per_block rows), each
+// over its own balanced map: either both with n_wg == workgroups (every
+// workgroup takes a share of both) or with the two n_wg adding up to
+// workgroups (the first pre.map.n_wg take prefix pieces, the rest suffix
+// segments); full mode, dense caches.  The merge is launched after it.
 hipError_t launch_bifurcated(const SplitArgs &pre, const SplitArgs &suf, int head_dim,
                              int suffix_rows_per_block, int64_t workgroups, hipStream_t stream);
 
