@@ -759,6 +759,7 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
   auto body = [&](int tile, auto par, auto mask) {
     constexpr int PAR = decltype(par)::value;
     constexpr int MASK = decltype(mask)::value;
+    __builtin_amdgcn_s_setprio(0);  // see the tile store below
     bf16x8_t kf[KS];
     k_frags<D>(kbuf(tile + 2), kf);
     if constexpr (!ENERGY) pv_tile<D>(vbuf(tile), pf, oacc);
@@ -799,11 +800,17 @@ __device__ __forceinline__ void rows_piece(const SplitArgs &a, int b, int kvh, i
       }
       if constexpr (PAGED) lookup(tile + SA - 1 + 2 * NS, pr[(k + SA - 1) % NS]);
       const int st = (k + SA) % NS;  // stage of tile + SA (constant once unrolled)
+      // The tile store and the next loads run at a raised wave priority, so
+      // that the other wave of the SIMD, busy with its matrix and softmax
+      // work, does not hold them back (anchor prefill 1-2% faster; the same
+      // raise around the matrix and softmax work instead: no change).
+      __builtin_amdgcn_s_setprio(1);
       store((unsigned)(tile + SA) % kRowsBufs, kr[st], vr[st]);
       load(tile + SA + NS, pr[st], kr[st], vr[st]);
       if (k & 1) __syncthreads();  // after odd tiles only
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   if (n_tiles > 0) {  // the last tile's P.V
     if (__any(pend != 1.0f)) rescale_o<D, ENERGY>(oacc, pend);
     if constexpr (!ENERGY) pv_tile<D>(vbuf(n_tiles - 1), pf, oacc);
