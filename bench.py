@@ -56,6 +56,8 @@ WORKLOADS = {
     "paged_llama31_70b_ragged": "Llama-3.1-70B-shaped ragged decode in 16-token token-major pages",
     "anchor_prefill": "anchor-block context encoding: 2 blocks of 8192 tokens behind an 8192-token "
                       "anchor (Hq=32, Hkv=8, d=128)",
+    "long_context_5m_share8": "one device's share of the 5.12M-token GQA decode cut into 8 token "
+                              "shares (640,000 tokens) + the merge of the 8 shares' (O, lse)",
 }
 # Workloads that reuse another one's inputs: name -> (inputs of, call mode, paging)
 VARIANTS = {
@@ -65,6 +67,7 @@ VARIANTS = {
     "long_context_5m_zeta": ("long_context_5m", "zeta", None),
     "paged_long_context_1m": ("long_context_1m", "full", (16, "head_major")),
     "paged_llama31_70b_ragged": ("llama31_70b_ragged", "full", (16, "token_major")),
+    "long_context_5m_share8": ("long_context_5m", "share8", None),
 }
 # The configurations reported beside the headline: (workload, timed steps,
 # oracle rows sampled for parity).  Steps follow the per-config iteration
@@ -76,6 +79,7 @@ CONFIGS = [
     ("long_context_5m", 10, 8),
     ("long_context_5m_energy", 10, 8),
     ("long_context_5m_zeta", 10, 2),
+    ("long_context_5m_share8", 50, 8),
     ("bifurcated_prefix", 200, 16),
     ("llama31_70b_ragged", 30, 16),
 ]
@@ -388,6 +392,61 @@ class DecodeRunner:
         return list(groups.values())
 
 
+class ShardRunner(DecodeRunner):
+    """Sequence sharding as one device of N sees it: the cache's token axis
+    is cut into N equal shares (one per device); a step decodes this device's
+    share (share 0, at its real shape: split kernel, then its merge into
+    slot 0 of the parts buffer) and merges the N shares' (O, lse) with
+    attn_merge_results (the exchange step after an all-gather of the parts;
+    the other N - 1 parts are computed once beforehand, from the same cache).
+    The merged rows are the whole cache's: parity is against the oracle over
+    all of it."""
+
+    def __init__(self, torch, w, n=8):
+        from long_context_exact_split_amd import binding
+        self.w, self.mode, self.binding, self.pc = w, "full", binding, None
+        q, k, v = device_kv(torch, w)
+        S = w.L_max // n
+        assert S * n == w.L_max and (w.kv_lens == w.L_max).all()
+        B, q_len, Hq, D = w.q.shape
+        self.parts_o = torch.empty((n, B, q_len, Hq, D), dtype=torch.float32, device="cuda")
+        self.parts_lse = torch.empty((n, B, q_len, Hq), dtype=torch.float32, device="cuda")
+        for p in range(n - 1, -1, -1):
+            ks = k[:, :, p * S:(p + 1) * S].contiguous()
+            vs = v[:, :, p * S:(p + 1) * S].contiguous()
+            if p:
+                binding.decode(q, ks, vs, scale=w.scale, out=self.parts_o[p],
+                               lse=self.parts_lse[p])
+                del ks, vs
+        self.q, self.k, self.v, self.lens = q, ks, vs, None
+        self.ph_args = ((q, ks, vs, None), dict(scale=w.scale))
+        self.ph = binding.Phases(*self.ph_args[0], **self.ph_args[1])
+        self.ph.out, self.ph.lse = self.parts_o[0], self.parts_lse[0]
+        self.plan = self.ph.plan
+        self.out = torch.empty((B, q_len, Hq, D), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device="cuda")
+        self.kv_tokens = S * B
+        self.oracle_kv_tokens = w.L_max * B  # the oracle reads the whole cache of a row
+        self.kv_bytes = 2 * S * B * w.Hkv * w.D * 2
+        self.q_bytes = B * q_len * Hq * D * 2
+        self.out_bytes = B * q_len * Hq * (D + 1) * 4
+        self.flops = 4 * w.G * q_len * w.D * S * B * w.Hkv
+        self.kernel = (f"split_kv_valu<bf16,{w.D},rows={self.plan['rows_per_block']}> on a "
+                       f"{S}-token share")
+        self.bound = "hbm"
+        torch.cuda.synchronize()
+
+    def second(self):
+        self.ph.merge()
+        self.binding.merge_results(self.parts_o, self.parts_lse, out=self.out, lse=self.lse)
+
+    def make_graph_call(self):
+        return None
+
+    def outputs(self):
+        return self.out.cpu().numpy(), self.lse.cpu().numpy()
+
+
 class BifurcatedRunner:
     """The shared-prefix call, timed as one unit (three launches)."""
 
@@ -505,6 +564,8 @@ def make_runner(torch, name, page_size=0):
     if name == "anchor_prefill":
         return AnchorRunner(torch, w)
     _, mode, paging = VARIANTS.get(name, (None, "full", None))
+    if mode == "share8":
+        return ShardRunner(torch, w, 8)
     if paging is not None and page_size:
         paging = (page_size, paging[1])
     return DecodeRunner(torch, w, mode, paging)
@@ -569,7 +630,8 @@ def cpu_baseline(run, n_rows, O_gpu, lse_gpu):
     total_rows = lse_gpu.shape[0] * lse_gpu.shape[1] * lse_gpu.shape[2]
     frac = len(rows) / total_rows
     par = parity(rows, O_gpu, lse_gpu, Or, lr)
-    return {"value": run.kv_tokens * frac / dt, "unit": "KV tokens/s", "cores": used,
+    otok = getattr(run, "oracle_kv_tokens", run.kv_tokens)
+    return {"value": otok * frac / dt, "unit": "KV tokens/s", "cores": used,
             "kind": "oracle",
             "sample": f"{len(rows)} of {total_rows} query rows, each over its whole visible cache "
                       f"({dt:.2f} s on {used} threads, one (sequence, KV head) group each); "
@@ -754,8 +816,9 @@ def measure_config(torch, name, K, n_rows, warmup, min_warmup_s):
     Or, lr, dt, used = run_oracle(run, rows, host_cores())
     rec["parity"] = parity(rows, O, lse, Or, lr)
     total_rows = lse.size
+    otok = getattr(run, "oracle_kv_tokens", run.kv_tokens)  # tokens the oracle's rows read
     rec["oracle"] = {"seconds": dt, "threads": used,
-                     "kv_tokens_per_s": run.kv_tokens * len(rows) / total_rows / dt}
+                     "kv_tokens_per_s": otok * len(rows) / total_rows / dt}
     if name in ONE_CORE:
         _, _, dt1, _ = run_oracle(run, rows, 1)
         rec["oracle"]["one_core_seconds"] = dt1
@@ -957,7 +1020,7 @@ def main(argv=None):
             print(f"# config {name}: {configs[name]['call_ms_mean']:.4f} ms per call, parity "
                   f"{configs[name]['parity']} ({time.perf_counter() - t_c:.1f} s)",
                   file=sys.stderr, flush=True)
-            if name in ("long_context_5m_zeta", "llama31_70b_ragged", "bifurcated_prefix"):
+            if name in ("long_context_5m_share8", "llama31_70b_ragged", "bifurcated_prefix"):
                 forget(torch, make_workload(name))
         result["configs"] = configs
     result["parity_ok"] = parity_ok

@@ -314,6 +314,30 @@ ATTN_API attn_status_t attn_prefill_anchor(const attn_anchor_desc_t *desc, const
 ATTN_API attn_status_t attn_decode_static(const attn_desc_t *desc, const void *q, const void *k,
                                           const void *v, float *o, float *lse, void *stream);
 
+/* Merge of results computed over disjoint shares of the keys -- the
+ * exchange step of a sequence-sharded decode.  When each of N devices holds
+ * a share of every sequence's tokens, each runs attn_decode on its share,
+ * and the N (O, lse) pairs of every row (gathered on one device) give the
+ * row's result over all its keys: (O_p, lse_p) is the record (m = lse_p,
+ * l = 1, o = O_p), so with M = max_p lse_p and w_p = e^(lse_p - M)
+ *     O = sum_p w_p O_p / sum_p w_p,   lse = M + ln sum_p w_p
+ * (Star Attention article, phase 2: the query host combines the hosts'
+ * local outputs by their softmax statistics; Tree Attention article, "an
+ * energy view of attention": the local energies are reduced across
+ * devices).  Exact up to rounding for any cut of the keys into shares.
+ *     o_parts   float32 [n_parts][rows][D]   (part p, row r at (p*rows + r)*D)
+ *     lse_parts float32 [n_parts][rows]      natural log
+ *     o         float32 [rows][D];  lse float32 [rows]
+ * n_parts >= 1, 0 <= rows <= 2^25, D = head_dim in {64, 128}; 4-byte
+ * aligned pointers; the outputs must not overlap the inputs.  A part with
+ * lse_p = -inf (it saw no key) adds nothing and its O_p is not read; a row
+ * whose every part is -inf gets O = 0 and lse = -inf.  One launch on
+ * `stream`, nothing allocated; errors as above (ATTN_ERR_SHAPE for n_parts
+ * or rows out of range, ATTN_ERR_UNSUPPORTED for head_dim). */
+ATTN_API attn_status_t attn_merge_results(int32_t n_parts, int64_t rows, int32_t head_dim,
+                                          const float *o_parts, const float *lse_parts, float *o,
+                                          float *lse, void *stream);
+
 /* Static text for a status code. */
 ATTN_API const char *attn_status_string(attn_status_t status);
 

@@ -29,7 +29,7 @@ EXPORTS = ("attn_decode_plan", "attn_workspace_bytes", "attn_decode_energy", "at
            "attn_decode_paged", "attn_decode_energy_paged", "attn_decode_partials_paged",
            "attn_bifurcated_workspace_bytes", "attn_decode_bifurcated",
            "attn_anchor_workspace_bytes", "attn_prefill_anchor", "attn_decode_static",
-           "attn_status_string")
+           "attn_merge_results", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -132,6 +132,7 @@ def load_library():
         lib.attn_decode_bifurcated.argtypes = [P(AttnBifDesc)] + [c.c_void_p] * 8 + [
             c.c_size_t, c.c_void_p]
         lib.attn_decode_static.argtypes = [P(AttnDesc)] + [c.c_void_p] * 6
+        lib.attn_merge_results.argtypes = [c.c_int32, c.c_int64, c.c_int32] + [c.c_void_p] * 5
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = c.c_int
         lib.attn_status_string.argtypes = [c.c_int]
@@ -416,6 +417,29 @@ class Phases:
         _check(self.lib.attn_decode_merge(ctypes.byref(self.desc), _ptr(self.out), _ptr(self.lse),
                                           _ptr(self.ws), self.nbytes, self.stream),
                "attn_decode_merge")
+
+
+def merge_results(o_parts, lse_parts, *, out=None, lse=None):
+    """Merge results computed over disjoint shares of the keys (one share per
+    device in a sequence-sharded decode): o_parts float32 [n, ..., D] and
+    lse_parts float32 [n, ...] (the n results of the same rows) give O
+    [..., D] and lse [...] over all the keys (attn_merge_results)."""
+    torch = _torch()
+    lib = load_library()
+    if o_parts.dim() < 2 or lse_parts.shape != o_parts.shape[:-1]:
+        raise ValueError("o_parts must be [n, ..., D] and lse_parts [n, ...] with the same rows")
+    for t, name in ((o_parts, "o_parts"), (lse_parts, "lse_parts")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != o_parts.device:
+            raise ValueError(f"{name} must be a contiguous float32 tensor on {o_parts.device}")
+    n, D = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel() if n > 0 else 0
+    with torch.cuda.device(o_parts.device):
+        out = _output(out, tuple(o_parts.shape[1:]), o_parts.device, "out")
+        lse = _output(lse, tuple(lse_parts.shape[1:]), o_parts.device, "lse")
+        _check(lib.attn_merge_results(n, rows, D, _ptr(o_parts), _ptr(lse_parts), _ptr(out),
+                                      _ptr(lse), _stream_ptr(o_parts.device)),
+               "attn_merge_results")
+    return out, lse
 
 
 def decode_energy(q, k, kv_lens=None, *, scale: Optional[float] = None, causal: bool = False,

@@ -306,6 +306,25 @@ def test_anchor_validation(lib):
     assert lib.attn_prefill_anchor(ctypes.byref(d), *args) == 0
 
 
+def test_merge_results_validation(lib):
+    """attn_merge_results rejects bad sizes, null and misaligned pointers on
+    the host; an empty call is a valid no-op that needs no device."""
+    f = lib.attn_merge_results
+    ok = [16, 16, 16, 16, None]
+    assert binding.STATUS[f(0, 10, 128, *ok)] == "ATTN_ERR_SHAPE"
+    assert binding.STATUS[f(-1, 10, 128, *ok)] == "ATTN_ERR_SHAPE"
+    assert binding.STATUS[f(2, -1, 128, *ok)] == "ATTN_ERR_SHAPE"
+    assert binding.STATUS[f(2, (1 << 25) + 1, 128, *ok)] == "ATTN_ERR_SHAPE"
+    assert binding.STATUS[f(2, 10, 96, *ok)] == "ATTN_ERR_UNSUPPORTED"
+    for i in range(4):
+        args = list(ok)
+        args[i] = 0
+        assert binding.STATUS[f(2, 10, 64, *args)] == "ATTN_ERR_NULL"
+        args[i] = 18
+        assert binding.STATUS[f(2, 10, 64, *args)] == "ATTN_ERR_ALIGN"
+    assert f(3, 0, 128, 0, 0, 0, 0, None) == 0
+
+
 def test_status_strings(lib):
     for code, name in binding.STATUS.items():
         s = lib.attn_status_string(code).decode()
