@@ -331,9 +331,12 @@ ATTN_API attn_status_t attn_decode_static(const attn_desc_t *desc, const void *q
  * n_parts >= 1, 0 <= rows <= 2^25, D = head_dim in {64, 128}; 4-byte
  * aligned pointers; the outputs must not overlap the inputs.  A part with
  * lse_p = -inf (it saw no key) adds nothing and its O_p is not read; a row
- * whose every part is -inf gets O = 0 and lse = -inf.  One launch on
- * `stream`, nothing allocated; errors as above (ATTN_ERR_SHAPE for n_parts
- * or rows out of range, ATTN_ERR_UNSUPPORTED for head_dim). */
+ * whose every part is -inf gets O = 0 and lse = -inf.  With o_parts and o
+ * both NULL only lse is merged (lse = ln sum_p e^(lse_p): the energies of
+ * attn_decode_energy on each share reduced to the energy over all keys).
+ * One launch on `stream`, nothing allocated; errors as above
+ * (ATTN_ERR_SHAPE for n_parts or rows out of range, ATTN_ERR_UNSUPPORTED
+ * for head_dim, ATTN_ERR_NULL when only one of o_parts and o is NULL). */
 ATTN_API attn_status_t attn_merge_results(int32_t n_parts, int64_t rows, int32_t head_dim,
                                           const float *o_parts, const float *lse_parts, float *o,
                                           float *lse, void *stream);

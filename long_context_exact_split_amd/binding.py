@@ -442,6 +442,25 @@ def merge_results(o_parts, lse_parts, *, out=None, lse=None):
     return out, lse
 
 
+def merge_energies(lse_parts, *, lse=None):
+    """The lse-only form of merge_results: lse_parts float32 [n, ...] (the
+    energies of n disjoint shares of the keys) give lse [...] over all of
+    them, ln sum_p e^(lse_p)."""
+    torch = _torch()
+    lib = load_library()
+    if lse_parts.dim() < 1:
+        raise ValueError("lse_parts must be [n, ...]")
+    if lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be a contiguous float32 tensor")
+    n = lse_parts.shape[0]
+    rows = lse_parts[0].numel() if n > 0 else 0
+    with torch.cuda.device(lse_parts.device):
+        lse = _output(lse, tuple(lse_parts.shape[1:]), lse_parts.device, "lse")
+        _check(lib.attn_merge_results(n, rows, 64, None, _ptr(lse_parts), None, _ptr(lse),
+                                      _stream_ptr(lse_parts.device)), "attn_merge_results")
+    return lse
+
+
 def decode_energy(q, k, kv_lens=None, *, scale: Optional[float] = None, causal: bool = False,
                   chunk_len: int = 0, lse=None, workspace=None):
     """Energy only (reads K, not V): returns lse float32 [B, q_len, Hq]."""

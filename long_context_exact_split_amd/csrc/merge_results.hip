@@ -22,11 +22,12 @@ namespace {
 // A wave per row: the parts' maximum lse first (lane l reads parts l, l + 64,
 // ...), then every part weighted by e^(lse_p - M) in part order (fixed order:
 // deterministic); lane l holds D/64 of the outputs.  A part with lse = -inf
-// saw no key: it adds nothing and its O is not read.
+// saw no key: it adds nothing and its O is not read.  ENERGY: lse only (the
+// logsumexp of the parts' lse; no O is read or written).
 constexpr int kRowsPerBlock = 4;
 constexpr int kBatch = 8;  // parts loaded together
 
-template <int D>
+template <int D, bool ENERGY>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void merge_results(
     int n, int64_t rows, const float *__restrict__ o_parts, const float *__restrict__ lse_parts,
     float *__restrict__ o, float *__restrict__ lse) {
@@ -53,9 +54,11 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void merge_results(
           const float lp = lse_parts[(int64_t)p * rows + row];
           if (lp != -INFINITY) {
             wgt[k] = fast_exp2((lp - M) * kLog2e);
-            const float *src = o_parts + ((int64_t)p * rows + row) * D + lane * EPL;
+            if constexpr (!ENERGY) {
+              const float *src = o_parts + ((int64_t)p * rows + row) * D + lane * EPL;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) ov[k][e] = src[e];
+              for (int e = 0; e < EPL; ++e) ov[k][e] = src[e];
+            }
           }
         }
       }
@@ -69,6 +72,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void merge_results(
   }
   const bool empty = M == -INFINITY || !(wsum > 0.0f);
   if (lane == 0) lse[row] = empty ? -INFINITY : M + log2f(wsum) * kLn2;
+  if constexpr (ENERGY) return;
   const float inv = empty ? 0.0f : 1.0f / wsum;
   float *dst = o + row * D + lane * EPL;
 #pragma unroll
@@ -90,18 +94,22 @@ attn_status_t attn_merge_results(int32_t n_parts, int64_t rows, int32_t head_dim
     if (n_parts < 1 || rows < 0 || rows > kMaxResultRows) return ATTN_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     if (rows == 0) return ATTN_OK;
-    if (!o_parts || !lse_parts || !o || !lse) return ATTN_ERR_NULL;
+    const bool energy = o_parts == nullptr && o == nullptr;  // lse only
+    if (!lse_parts || !lse || (!energy && (!o_parts || !o))) return ATTN_ERR_NULL;
     if (!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(o, 4) || !aligned(lse, 4))
       return ATTN_ERR_ALIGN;
     (void)hipGetLastError();
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     const dim3 block(kRowsPerBlock * kWave);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (head_dim == 64)
-      hipLaunchKernelGGL(merge_results<64>, grid, block, 0, s, n_parts, rows, o_parts, lse_parts,
-                         o, lse);
+    if (energy)
+      hipLaunchKernelGGL((merge_results<64, true>), grid, block, 0, s, n_parts, rows, o_parts,
+                         lse_parts, o, lse);
+    else if (head_dim == 64)
+      hipLaunchKernelGGL((merge_results<64, false>), grid, block, 0, s, n_parts, rows, o_parts,
+                         lse_parts, o, lse);
     else
-      hipLaunchKernelGGL(merge_results<128>, grid, block, 0, s, n_parts, rows, o_parts,
+      hipLaunchKernelGGL((merge_results<128, false>), grid, block, 0, s, n_parts, rows, o_parts,
                          lse_parts, o, lse);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   } catch (...) {

@@ -323,6 +323,11 @@ def test_merge_results_validation(lib):
         args[i] = 18
         assert binding.STATUS[f(2, 10, 64, *args)] == "ATTN_ERR_ALIGN"
     assert f(3, 0, 128, 0, 0, 0, 0, None) == 0
+    # lse only takes both o_parts and o NULL; one of them NULL is an error
+    assert binding.STATUS[f(2, 10, 64, 0, 16, 16, 16, None)] == "ATTN_ERR_NULL"
+    assert binding.STATUS[f(2, 10, 64, 16, 16, 0, 16, None)] == "ATTN_ERR_NULL"
+    assert binding.STATUS[f(2, 10, 64, 0, 0, 0, 16, None)] == "ATTN_ERR_NULL"
+    assert binding.STATUS[f(2, 10, 64, 0, 18, 0, 16, None)] == "ATTN_ERR_ALIGN"
 
 
 def test_status_strings(lib):

@@ -62,6 +62,15 @@ def test_sharded_decode_matches_oracle(case):
     # the same rows as the one-call decode, up to the order of the merge
     assert torch.allclose(O, O1, atol=2e-5, rtol=0)
     assert torch.allclose(lse, lse1, atol=2e-5, rtol=1e-6)
+    # energies only: each share's lse from K alone, reduced to the whole cache's
+    e_parts = []
+    for c0, c1 in zip(cuts[:-1], cuts[1:]):
+        lens = torch.clamp(kv_lens - c0, 0, c1 - c0).to(torch.int32).contiguous()
+        e_parts.append(binding.decode_energy(q, k[:, :, c0:c1].contiguous(), lens, scale=w.scale))
+    lse_e = binding.merge_energies(torch.stack(e_parts))
+    torch.cuda.synchronize()
+    check_rows(None, lse_e.cpu().numpy(), None, lr, what=f"sharded energy {case[:5]}")
+    assert torch.allclose(lse_e, lse, atol=2e-5, rtol=1e-6)
 
 
 def test_merge_results_edge_rows():
