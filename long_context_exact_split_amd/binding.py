@@ -429,8 +429,9 @@ def merge_results(o_parts, lse_parts, *, out=None, lse=None):
     if o_parts.dim() < 2 or lse_parts.shape != o_parts.shape[:-1]:
         raise ValueError("o_parts must be [n, ..., D] and lse_parts [n, ...] with the same rows")
     for t, name in ((o_parts, "o_parts"), (lse_parts, "lse_parts")):
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != o_parts.device:
-            raise ValueError(f"{name} must be a contiguous float32 tensor on {o_parts.device}")
+        if (not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous()
+                or t.device != o_parts.device):
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor on {o_parts.device}")
     n, D = o_parts.shape[0], o_parts.shape[-1]
     rows = lse_parts[0].numel() if n > 0 else 0
     with torch.cuda.device(o_parts.device):
@@ -450,8 +451,8 @@ def merge_energies(lse_parts, *, lse=None):
     lib = load_library()
     if lse_parts.dim() < 1:
         raise ValueError("lse_parts must be [n, ...]")
-    if lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
-        raise ValueError("lse_parts must be a contiguous float32 tensor")
+    if not lse_parts.is_cuda or lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be a contiguous float32 GPU tensor")
     n = lse_parts.shape[0]
     rows = lse_parts[0].numel() if n > 0 else 0
     with torch.cuda.device(lse_parts.device):

@@ -330,6 +330,19 @@ def test_merge_results_validation(lib):
     assert binding.STATUS[f(2, 10, 64, 0, 18, 0, 16, None)] == "ATTN_ERR_ALIGN"
 
 
+def test_merge_binding_refuses_host_tensors(lib):
+    """The binding checks the tensors it hands over as pointers: host tensors
+    are refused before the library is called (a host pointer in a kernel
+    would fault the GPU)."""
+    import torch
+    with pytest.raises(ValueError):
+        binding.merge_results(torch.zeros(2, 3, 64), torch.zeros(2, 3))
+    with pytest.raises(ValueError):
+        binding.merge_energies(torch.zeros(2, 3))
+    with pytest.raises(ValueError):
+        binding.merge_results(torch.zeros(2, 3, 64), torch.zeros(2, 4))
+
+
 def test_status_strings(lib):
     for code, name in binding.STATUS.items():
         s = lib.attn_status_string(code).decode()
