@@ -96,6 +96,7 @@ COUNTERS = {
     "llama3_8b_gqa": "profiles/split_kv_valu_llama3_8b_gqa.counters.txt",
     "long_context_5m": "profiles/split_kv_valu_long_context_5m.counters.txt",
     "bifurcated_prefix": "profiles/bifurcated_call_bifurcated_prefix.counters.txt",
+    "long_context_5m_share8": "profiles/split_kv_valu_long_context_5m_share8.counters.txt",
 }
 
 
