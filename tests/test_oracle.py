@@ -70,3 +70,34 @@ def test_needle_row_is_near_its_closed_form():
     assert 0.0 <= lse[0, 0, 0] - s[n] <= upper * (1 + 1e-9) + 1e-15
     w_rest = 1.0 - math.exp(s[n] - lse[0, 0, 0])
     assert np.abs(O[0, 0, 0] - v[n]).max() <= 2 * w_rest * np.abs(v).max() + 1e-12
+
+
+def test_finalised_share_results_merge_as_records():
+    """The reading behind merging per-share results (a sequence-sharded
+    decode): a finalised result (O, lse) over some keys is the record
+    (m = lse, l = 1, o = O), so merging the shares' results with the merge
+    rule, in any order, gives attention over all the keys; a share with no
+    visible key (lse = -inf) is the identity."""
+    import random
+    rng = np.random.default_rng(37)
+    rnd = random.Random(37)
+    for case in range(12):
+        L = int(rng.integers(1, 90))
+        D = int(rng.integers(1, 9))
+        q = rng.standard_normal((1, 1, 1, D))
+        k = rng.standard_normal((1, 1, L, D)) * 2.0
+        v = rng.standard_normal((1, 1, L, D))
+        O, lse = oracle.attend(q, k, v, [L], 0.7)
+        cuts = sorted({0, L, *rng.integers(0, L + 1, size=int(rng.integers(0, 5))).tolist()})
+        recs = []
+        for c0, c1 in zip(cuts[:-1], cuts[1:]):
+            Os, ls = oracle.attend(q, k[:, :, c0:c1], v[:, :, c0:c1], [c1 - c0], 0.7)
+            recs.append((float(ls[0, 0, 0]), 1.0, Os[0, 0, 0]))
+        recs.append((-math.inf, 0.0, np.zeros(D)))  # an empty share
+        rnd.shuffle(recs)
+        acc = recs[0]
+        for r in recs[1:]:
+            acc = oracle.merge(acc, r)
+        Om, lm = oracle.finalize(acc)
+        assert np.allclose(Om, O[0, 0, 0], rtol=1e-12, atol=1e-13), case
+        assert abs(lm - lse[0, 0, 0]) <= 1e-12 * max(1.0, abs(lse[0, 0, 0])), case
