@@ -97,6 +97,8 @@ COUNTERS = {
     "long_context_5m": "profiles/split_kv_valu_long_context_5m.counters.txt",
     "bifurcated_prefix": "profiles/bifurcated_call_bifurcated_prefix.counters.txt",
     "long_context_5m_share8": "profiles/split_kv_valu_long_context_5m_share8.counters.txt",
+    "long_context_5m_energy": "profiles/split_kv_valu_energy_long_context_5m.counters.txt",
+    "long_context_5m_zeta": "profiles/split_kv_valu_zeta_long_context_5m.counters.txt",
 }
 
 
