@@ -188,17 +188,30 @@ ATTN_HD int64_t total_units(const WorkMap &m) {
   return u;
 }
 
-// First unit of workgroup w (balanced): floor(w * U / W); wg_start(W) = U.
-// Exact in 64-bit arithmetic while U * W < 2^63 (the planner enforces
-// U < 2^46 units, W < 2^16).
+// Workgroups that take a share of the U units: the planned n_wg, or U when
+// the cached tokens (read on the device) come to fewer units than that; the
+// others idle.  Every share is then non-empty, so the pieces of a segment sit
+// in consecutive workgroups and hence consecutive slots, which is what the
+// merge's closed form (segment_slots) counts.  (With more workgroups than
+// units some shares would be empty, and the merge would read slots no piece
+// wrote.)
+ATTN_HD int64_t active_wgs(const WorkMap &m, int64_t U) {
+  return U < (int64_t)m.n_wg ? U : (int64_t)m.n_wg;
+}
+
+// First unit of workgroup w (balanced): floor(w * U / W) over the W active
+// workgroups; wg_start(w) = U for w >= W (an idle workgroup).  Exact in
+// 64-bit arithmetic while U * W < 2^63 (the planner enforces U < 2^46 units,
+// W < 2^16).
 ATTN_HD int64_t wg_start(const WorkMap &m, int64_t U, int64_t w) {
-  return (w * U) / (int64_t)m.n_wg;
+  const int64_t W = active_wgs(m, U);
+  return w >= W ? U : (w * U) / W;
 }
 
 // The workgroup whose range holds unit x (0 <= x < U): the largest w with
 // floor(w*U/W) <= x, i.e. w*U < (x+1)*W, i.e. w = ((x+1)*W - 1) / U.
 ATTN_HD int64_t wg_of_unit(const WorkMap &m, int64_t U, int64_t x) {
-  return ((x + 1) * (int64_t)m.n_wg - 1) / U;
+  return ((x + 1) * active_wgs(m, U) - 1) / U;
 }
 
 // One piece of work: tokens [t0, t1) of segment sigma (numbered

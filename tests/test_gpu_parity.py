@@ -345,6 +345,33 @@ def test_isolated_huge_logits_at_every_lane_position(case):
 # ----------------------------------------------------------------------------
 # Properties of the path
 # ----------------------------------------------------------------------------
+FEW_TOKENS = [([5], 4, 1), ([1, 0, 2], 4, 1), ([3, 7], 32, 1), ([5], 16, 2), ([2, 9, 0, 4], 4, 1)]
+
+
+@pytest.mark.parametrize("case", FEW_TOKENS, ids=[f"lens{c[0]}_Hq{c[1]}_ql{c[2]}" for c in FEW_TOKENS])
+def test_ragged_lengths_below_the_planned_workgroups(case):
+    """Lengths far below max_kv_len: the cached tokens (read on the device)
+    come to fewer units than the workgroups the plan sized for max_kv_len, so
+    only as many workgroups as units take a share.  The workspace is filled
+    with NaN first: a record the merge read without a piece having written it
+    would poison its row.  Decode and energy-only, vector-ALU and matrix-core
+    kernels."""
+    lens, Hq, q_len = case
+    B = len(lens)
+    w = inputs.make_decode("few_tokens", 61 + B, B=B, q_len=q_len, Hq=Hq, Hkv=1, D=128,
+                           L_max=4096, kv_lens=lens, nan_pad=True)
+    q, k, v, _ = workload_tensors(w)
+    kv = torch.from_numpy(w.kv_lens.astype(np.int32)).cuda()
+    ws = torch.full((4 << 20,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
+    O, lse = binding.decode(q, k, v, kv, scale=w.scale, workspace=ws)
+    ws.view(torch.float32).fill_(float("nan"))
+    lse_e = binding.decode_energy(q, k, kv, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    Or, lr = oracle_decode(w)
+    check_rows(O.cpu().numpy(), lse.cpu().numpy(), Or, lr, what=f"few tokens {case}")
+    check_rows(None, lse_e.cpu().numpy(), None, lr, what=f"few tokens energy {case}")
+
+
 def test_energy_lse_matches_decode_lse():
     w = inputs.make_decode("energy", 9, B=2, q_len=2, Hq=16, Hkv=4, D=128, L_max=5000,
                            kv_lens=[5000, 2222], causal=True, nan_pad=True)
