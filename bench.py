@@ -868,6 +868,8 @@ def wg_stamps(torch, args):
     from long_context_exact_split_amd import binding
     lib = binding.load_library()
     run = make_runner(torch, args.workload, args.page_size)
+    if isinstance(run, BifurcatedRunner):
+        return wg_stamps_bifurcated(torch, args, run, lib)
     if run.plan.get("kernel") not in (0, 1) or getattr(run, "mode", "full") == "zeta":
         raise RuntimeError("--wg-stamps covers the decode split kernels (vector-ALU, 32-row MFMA)")
     readback = getattr(lib, ("attn_probe_wg_stamps", "attn_probe_wg_stamps_mfma")[run.plan["kernel"]],
@@ -936,6 +938,63 @@ def wg_stamps(torch, args):
               f"{out['read_share']['isolated'][-1]['event_us']:.1f} us, sustained "
               f"{out['read_share']['sustained'][-1]['event_us']:.1f} us", file=sys.stderr,
               flush=True)
+    print(json.dumps(out))
+
+
+def wg_stamps_bifurcated(torch, args, run, lib):
+    """Per-workgroup timing of the one-launch shared-prefix kernel: REPS
+    launches after a run of back-to-back calls, each workgroup's start and end
+    summarised separately for the prefix workgroups and the suffix ones (the
+    split the planner chose, read from the test build's hook)."""
+    import ctypes
+    import numpy as np
+    from long_context_exact_split_amd import binding
+    readback = getattr(lib, "attn_probe_wg_stamps_bif", None)
+    if readback is None:
+        raise RuntimeError(f"{binding.library_path()} is not the stamping build")
+    readback.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    tl = binding.load_testing_library()
+    fused, npre, nsuf = ctypes.c_int32(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    desc = binding.bifurcated_desc(run.t[0], run.t[1], run.t[3], run.w.scale)
+    if tl.attn_testing_bifurcated_form(ctypes.byref(desc), cu, ctypes.byref(fused),
+                                       ctypes.byref(npre), ctypes.byref(nsuf)) != 0:
+        raise RuntimeError("attn_testing_bifurcated_form failed")
+    split = bool(fused.value) and npre.value + nsuf.value == cu
+    n = cu if fused.value else 0
+    if n == 0:
+        raise RuntimeError("this batch does not run the one-launch kernel")
+    timed_steps(torch, run, 20, args.warmup, args.min_warmup_s)
+    out = {"workload": WORKLOADS[args.workload], "kernel": "split_kv_bifurcated<128> (stamped)",
+           "workgroups": n, "form": "split" if split else "shared",
+           "prefix_workgroups": int(npre.value) if split else n,
+           "library": os.path.basename(binding.library_path()), "launches": []}
+    stream = torch.cuda.current_stream()
+    for rep in range(args.wg_stamps):
+        for _ in range(100):
+            run.first()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run.first()
+        b.record(stream)
+        torch.cuda.synchronize()
+        st = np.zeros((n, 4), dtype=np.uint64)
+        if readback(st.ctypes.data, n) != 0:
+            raise RuntimeError("stamp read-back failed")
+        t0, t1 = st[:, 0].astype(np.int64), st[:, 1].astype(np.int64)
+        base = t0.min()
+        start, end = (t0 - base) * 0.01, (t1 - base) * 0.01
+        rec = {"call_us": a.elapsed_time(b) * 1e3, "span_us": float(end.max())}
+        parts = ({"prefix": slice(0, int(npre.value)), "suffix": slice(int(npre.value), n)}
+                 if split else {"all": slice(0, n)})
+        for name, sl in parts.items():
+            rec[name] = {"start_max_us": float(start[sl].max()),
+                         "end_min_med_max_us": [float(end[sl].min()), float(np.median(end[sl])),
+                                                float(end[sl].max())]}
+        out["launches"].append(rec)
+        print(f"# rep {rep}: " + ", ".join(
+            f"{k} ends {v['end_min_med_max_us'][1]:.1f}/{v['end_min_med_max_us'][2]:.1f} us"
+            for k, v in rec.items() if isinstance(v, dict)), file=sys.stderr, flush=True)
     print(json.dumps(out))
 
 

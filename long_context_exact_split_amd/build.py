@@ -26,11 +26,12 @@ LIB_NAME = "libattn_decode.so"
 TESTING_LIB_NAME = "libattn_decode_testing.so"
 PROBE_NAME = "libhbm_probe.so"  # HBM read-stream / copy reference kernels
 # The product library with the decode split kernels (vector-ALU and 32-row
-# matrix-core) built to record each workgroup's start and end clocks and XCD
+# matrix-core) and the one-launch shared-prefix kernel built to record each
+# workgroup's start and end clocks and XCD
 # (csrc/probe/wg_stamps.h); loaded only by the bench's --wg-stamps
 # measurement.  Each stamped source has its own stamp array and read-back.
 STAMPS_LIB_NAME = "libattn_decode_stamps.so"
-STAMPED_SOURCES = ("split_kv_valu.hip", "split_kv_mfma.hip")
+STAMPED_SOURCES = ("split_kv_valu.hip", "split_kv_mfma.hip", "split_kv_bifurcated.hip")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",

@@ -23,6 +23,13 @@
 // of its part), and the merge kernel combines them.
 #include "mfma_piece.h"
 
+#ifdef ATTN_WG_STAMPS
+#define ATTN_WG_STAMPS_READBACK attn_probe_wg_stamps_bif
+#include "probe/wg_stamps.h"  // per-workgroup clocks: measurement builds only
+#else
+#define ATTN_WG_STAMP()
+#endif
+
 namespace attn {
 namespace {
 
@@ -46,6 +53,7 @@ union BifSmem {
 
 template <int D>
 __global__ __launch_bounds__(kBifThreads) void split_kv_bifurcated(SplitArgs pre, SplitArgs suf) {
+  ATTN_WG_STAMP();
   __shared__ BifSmem<D> sh;
   const int w = blockIdx.x;
   WorkMap pm = pre.map, sm = suf.map;

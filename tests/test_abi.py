@@ -79,7 +79,7 @@ def test_stamping_build_exports_the_boundary_and_its_probe(lib):
     if not os.path.exists(path):
         pytest.skip("stamping build not built")
     exported = exported_functions(path)
-    probes = {"attn_probe_wg_stamps", "attn_probe_wg_stamps_mfma"}
+    probes = {"attn_probe_wg_stamps", "attn_probe_wg_stamps_mfma", "attn_probe_wg_stamps_bif"}
     assert exported == set(declared_functions()) | probes
     assert not probes & exported_functions(binding.library_path())
 
